@@ -1,0 +1,244 @@
+"""Benchmark of one per-GPU K-FAC step on an MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+A factors and G factors of every layer with their running average, pack and
+unpack of all factors through the fused buffer, the damped inverse of every
+factor, and the preconditioned gradient of every layer.  Inputs are seeded
+synthetic tensors of the workload's shapes, resident in GPU memory before the
+timed region.  Prints one JSON line.
+
+Workloads (--config): 1 single FC layer, 2 four-layer MLP (default),
+3 ResNet-50 shapes, 4 twelve-layer encoder with bf16 inputs, 5 large-factor
+stress (gamma = 1e-2).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X published peaks
+PEAK_FP32_MFMA = 157.3e12
+PEAK_FP64_MFMA = 78.6e12
+PEAK_BF16_MFMA = 2.5e15
+PEAK_HBM = 8.0e12
+
+
+def algorithmic_work(cfg):
+    """Algorithmic flops and bytes of one step (upper-triangle factor work,
+    d^3 per inverse, 2 dg da (dg + da) per preconditioned layer)."""
+    dims = [l.d_a for l in cfg.layers] + [l.d_g for l in cfg.layers]
+    rows = [l.rows for l in cfg.layers] * 2
+    f_factor = sum(r * d * (d + 1) for r, d in zip(rows, dims))
+    f_inverse = sum(d ** 3 for d in dims)
+    f_precond = sum(2 * l.d_g * l.d_a * (l.d_g + l.d_a) for l in cfg.layers)
+    packed = sum(d * (d + 1) // 2 for d in dims)
+    b_pack = 8 * packed
+    b_unpack = 4 * (packed + sum(d * d for d in dims))
+    return dict(factor=f_factor, inverse=f_inverse, precondition=f_precond,
+                pack_bytes=b_pack, unpack_bytes=b_unpack, packed=packed)
+
+
+def cpu_baseline(cfg, data, budget_s=30.0):
+    """The fp64 oracle on the host cores, over a bounded sample of the step:
+    whole layers are added (A and G factors, both inverses, the
+    preconditioned gradient) until the budget is spent; the rate is the
+    sample's algorithmic flops over its time."""
+    import numpy as np
+    import oracle
+
+    eps, gamma = np.float32(cfg.eps), np.float32(cfg.gammas[0])
+    flops, spent, done = 0, 0.0, 0
+    for li, layer in enumerate(cfg.layers):
+        a, g, grad = data[li]
+        t0 = time.perf_counter()
+        fa = oracle.factor(oracle.upcast(a, cfg.in_dtype))
+        fg = oracle.factor(oracle.upcast(g, cfg.in_dtype))
+        ma = oracle.running_average(None, fa, eps, True)
+        mg = oracle.running_average(None, fg, eps, True)
+        dims = [layer.d_a, layer.d_g]
+        p = oracle.pack([ma.astype(np.float32), mg.astype(np.float32)], dims)
+        oracle.unpack(p, dims)
+        za, _ = oracle.damped_inverse(ma, gamma)
+        zg, _ = oracle.damped_inverse(mg, gamma)
+        oracle.precondition(zg, grad, za)
+        spent += time.perf_counter() - t0
+        done += 1
+        for d in dims:
+            flops += layer.rows * d * (d + 1) + d ** 3
+        flops += 2 * layer.d_g * layer.d_a * (layer.d_g + layer.d_a)
+        if spent >= budget_s:
+            break
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    return {
+        "value": flops / spent / 1e12,
+        "unit": "TFLOP/s",
+        "cores": min(cores, threads),
+        "kind": "oracle",
+        "sample": f"{done} of {cfg.n_layers} layers of one step (factors, running average, pack/unpack, "
+                  f"both damped inverses, preconditioned gradient), fp64, {spent:.1f} s",
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=25.0)
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for {args.gpus}); "
+              "the multi-GPU exchange of the fused factor buffer is not part of it.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import linear_algebra_amd as la
+    from workloads import CONFIGS, gen_layer_step
+
+    la.load_library()
+    dev = torch.device("cuda:0")
+    cfg = CONFIGS[args.config]
+    L = cfg.layers
+    n = len(L)
+    eps, gamma = float(np.float32(cfg.eps)), float(np.float32(cfg.gammas[0]))
+
+    print(f"bench: generating config {cfg.cid} ({cfg.name}) inputs", file=sys.stderr, flush=True)
+    data = gen_layer_step(cfg, 0, threads=16)
+
+    def dev_tensor(x):
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(x).to(dev)
+
+    a_d = [dev_tensor(t[0]) for t in data]
+    g_d = [dev_tensor(t[1]) for t in data]
+    w_d = [dev_tensor(t[2]) for t in data]
+    ma = [torch.zeros(l.d_a, l.d_a, device=dev) for l in L]
+    mg = [torch.zeros(l.d_g, l.d_g, device=dev) for l in L]
+    za = [torch.zeros(l.d_a, l.d_a, device=dev) for l in L]
+    zg = [torch.zeros(l.d_g, l.d_g, device=dev) for l in L]
+    out = [torch.zeros(l.d_g, l.d_a, device=dev) for l in L]
+    facs = ma + mg[::-1]                      # A's forward, G's backward
+    zs = za + zg[::-1]
+    dims = [l.d_a for l in L] + [l.d_g for l in reversed(L)]
+    packed = torch.zeros(la.kfac_packed_size(dims), device=dev)
+    info = torch.zeros(len(facs), dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+
+    stages = ["factors_A", "factors_G", "pack", "unpack", "inverse", "precondition"]
+
+    def step(first, ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        la.kfac_factors(a_d, ma, eps, first)
+        mark(1)
+        la.kfac_factors(g_d, mg, eps, first)
+        mark(2)
+        la.kfac_pack_sym(facs, packed, la.KFAC_PACK)
+        mark(3)
+        la.kfac_pack_sym(facs, packed, la.KFAC_UNPACK)
+        mark(4)
+        la.kfac_damped_inverse(facs, gamma, zs, info)
+        mark(5)
+        la.kfac_precondition(zg, w_d, za, out)
+        mark(6)
+
+    print(f"bench: warmup {args.warmup}", file=sys.stderr, flush=True)
+    for w in range(args.warmup):
+        step(w == 0)
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(args.warmup == 0 and s == 0, events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    print(f"bench: {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
+
+    stage_ms = {name: 0.0 for name in stages}
+    for ev in events:
+        for i, name in enumerate(stages):
+            stage_ms[name] += ev[i].elapsed_time(ev[i + 1])
+    stage_ms = {k: v / args.steps for k, v in stage_ms.items()}
+    ms = wall * 1e3 / args.steps
+
+    bad = [i for i, v in enumerate(info.cpu().tolist()) if v != 0]
+    finite = all(bool(torch.isfinite(o).all()) for o in out)
+    if bad or not finite:
+        print(f"bench: numerical failure (info nonzero at {bad}, finite outputs {finite})", file=sys.stderr)
+        return 1
+
+    work = algorithmic_work(cfg)
+    flops = work["factor"] + work["inverse"] + work["precondition"]
+    value = flops / (ms * 1e-3) / 1e12
+    factor_peak = PEAK_BF16_MFMA if cfg.in_dtype == "bf16" else PEAK_FP32_MFMA
+    fa_flops = sum(l.rows * l.d_a * (l.d_a + 1) for l in L)
+    fg_flops = sum(l.rows * l.d_g * (l.d_g + 1) for l in L)
+    stage_rate = {
+        "factors_A": ("mfma", fa_flops / (stage_ms["factors_A"] * 1e-3), factor_peak, "TFLOP/s"),
+        "factors_G": ("mfma", fg_flops / (stage_ms["factors_G"] * 1e-3), factor_peak, "TFLOP/s"),
+        "pack": ("hbm", work["pack_bytes"] / (stage_ms["pack"] * 1e-3), PEAK_HBM, "GB/s"),
+        "unpack": ("hbm", work["unpack_bytes"] / (stage_ms["unpack"] * 1e-3), PEAK_HBM, "GB/s"),
+        "inverse": ("mfma", work["inverse"] / (stage_ms["inverse"] * 1e-3), PEAK_FP64_MFMA, "TFLOP/s"),
+        "precondition": ("mfma", work["precondition"] / (stage_ms["precondition"] * 1e-3), PEAK_FP32_MFMA, "TFLOP/s"),
+    }
+    scale = {"TFLOP/s": 1e12, "GB/s": 1e9}
+    stages_out = {}
+    for k in stages:
+        bound, rate, peak, unit = stage_rate[k]
+        stages_out[k] = {"ms": round(stage_ms[k], 4), "achieved": round(rate / scale[unit], 3), "unit": unit,
+                         "peak": peak / scale[unit], "frac": round(rate / peak, 4)}
+    dom = max(stages, key=lambda k: stage_ms[k])
+    bound, rate, peak, unit = stage_rate[dom]
+    roofline = {"bound": bound, "stage": dom, "achieved": round(rate / scale[unit], 3), "peak": peak / scale[unit],
+                "unit": unit, "frac": round(rate / peak, 4), "traffic": None}
+
+    result = {
+        "metric": "K-FAC step ms (factors+inverse+precondition) & TFLOP/s vs MFMA peak, 1 GPU",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16-in/f32" if cfg.in_dtype == "bf16" else "f32 (inverse in f64)",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {cfg.note}", "layers": n, "factors": len(dims),
+                   "gamma": gamma, "eps": eps, "flops_per_step": flops, "parallelism": "single GPU"},
+        "roofline": roofline,
+        "stages": stages_out,
+    }
+    if not args.no_cpu_baseline:
+        print("bench: timing the oracle on the host", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(cfg, data, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,157 @@
+/*
+ * kfac.h -- C ABI of the per-GPU K-FAC hot path for AMD Instinct MI355X
+ * (gfx950).  One K-FAC step on one GPU is
+ *
+ *     kfac_factors      A and G Kronecker factors with their running average
+ *     kfac_pack_sym     upper triangles of the factors <-> one fused buffer
+ *     kfac_damped_inverse  (X + gamma I)^-1 of every factor, batched
+ *     kfac_precondition (G + gamma I)^-1 . gradW . (A + gamma I)^-1 per layer
+ *
+ * following "Accelerating Distributed K-FAC with Smart Parallelism of
+ * Computing and Communication Tasks" (cited per entry point below).
+ *
+ * Common rules
+ *   - Matrices are row-major.  "Upper" means the entries (i, j) with j >= i.
+ *   - Arrays of per-layer pointers (x, m, xinv, grad, ...) and the size
+ *     arrays (rows, d, ...) are HOST arrays, read during the call only.  The
+ *     pointers they hold are DEVICE pointers, at least 4-byte aligned.
+ *   - `workspace` is a device buffer of at least the size returned by the
+ *     matching *_workspace_size() call, 256-byte aligned, owned by the
+ *     caller, and must stay untouched until the enqueued work has finished.
+ *     The library allocates no device memory and keeps no state between
+ *     calls; calls on different streams with different workspaces may run
+ *     concurrently.
+ *   - Every call validates its arguments on the host first.  On an error it
+ *     returns a non-zero status and enqueues nothing.  On success the work is
+ *     enqueued on `stream` (0 = the null stream) and the call returns
+ *     without waiting for it.
+ *   - Inputs containing NaN or Inf are not screened; they propagate
+ *     (the inverse reports them through `info`).
+ */
+#ifndef KFAC_H
+#define KFAC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KFAC_OK = 0,
+    KFAC_ERR_INVALID_VALUE = 1, /* bad count, size, pointer, alignment, gamma or eps */
+    KFAC_ERR_WORKSPACE = 2,     /* workspace missing, misaligned or too small */
+    KFAC_ERR_UNSUPPORTED = 3,   /* valid request this build cannot serve */
+    KFAC_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed */
+} kfac_status_t;
+
+typedef enum { KFAC_F32 = 0, KFAC_BF16 = 1 } kfac_dtype_t;
+typedef enum { KFAC_PACK = 0, KFAC_UNPACK = 1 } kfac_pack_dir_t;
+
+/* Largest factor dimension and largest number of layers / matrices per call. */
+#define KFAC_MAX_DIM 16384
+#define KFAC_MAX_COUNT 4096
+
+/* ABI version of this header (bumped on any incompatible change). */
+int kfac_abi_version(void);
+
+/* Static, human-readable name of a status code. */
+const char* kfac_status_string(kfac_status_t status);
+
+/* ---------------------------------------------------------------- factors --
+ * Kronecker factors with running average.  The page builds, per layer l, the
+ * factor A from the layer's input a and the factor G from the gradient with
+ * respect to the layer's output g, both symmetric (paragraph introducing the
+ * Kronecker factors; the pipelining paragraph computes them in the forward
+ * pre-hook and the backward hook, "Eq. (7)" and "Eq. (8)").  For each of the
+ * n matrices:
+ *
+ *     F_i = (1 / rows_i) * X_i^T X_i
+ *     M_i <- F_i                                 if first_step != 0
+ *     M_i <- eps * M_i + (1 - eps) * F_i         otherwise
+ *
+ * x[i]   : [rows[i], d[i]] row-major, float32 (in_dtype KFAC_F32) or bfloat16
+ *          (KFAC_BF16, accumulated in float32).  A layer with a bias carries
+ *          a trailing column of ones.
+ * m[i]   : [d[i], d[i]] float32.  Only the upper triangle is read (when
+ *          first_step == 0) and written; the strict lower triangle is left
+ *          as it was.
+ * eps    : in [0, 1].  rows[i] >= 1, 1 <= d[i] <= KFAC_MAX_DIM.
+ * The x[i] must not overlap any m[j].  Results are deterministic: the same
+ * inputs give the same bits on every run.
+ */
+size_t kfac_factors_workspace_size(int n, const int64_t* rows, const int64_t* d, kfac_dtype_t in_dtype);
+kfac_status_t kfac_factors(int n, const void* const* x, const int64_t* rows, const int64_t* d,
+                           kfac_dtype_t in_dtype, float* const* m, float eps, int first_step,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------- pack --
+ * Tensor fusion of the symmetric factors: only the upper triangle including
+ * the diagonal is kept, d(d+1)/2 elements per factor (tensor-fusion
+ * paragraph on communicated elements; paragraph on sending only the upper
+ * triangles), and consecutive factors are merged into one contiguous buffer
+ * (paragraph on dynamic tensor fusion).
+ *
+ *     packed[off_l + i*d_l - i*(i-1)/2 + (j - i)] = M_l[i][j],  0 <= i <= j < d_l
+ *     off_l = sum_{k<l} d_k (d_k + 1) / 2
+ *
+ * KFAC_PACK reads the upper triangles of m[l] and writes `packed`
+ * (kfac_packed_size() float32 elements).  KFAC_UNPACK reads `packed` and
+ * writes every element of m[l]: entry (i, j) and its mirror (j, i).  Values
+ * are copied bit for bit.  The m[l] must not overlap each other or `packed`.
+ */
+int64_t kfac_packed_size(int n, const int64_t* d);
+size_t kfac_pack_workspace_size(int n, const int64_t* d);
+kfac_status_t kfac_pack_sym(int n, float* const* m, const int64_t* d, float* packed, kfac_pack_dir_t dir,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------- inverse --
+ * Tikhonov-damped inverse of each factor (paragraph on damping before
+ * inverting; the inverses of different layers are independent, paragraph on
+ * MPD-KFAC; the inverse goes through a Cholesky decomposition, paragraph on
+ * the inverse performance model).  For each of the n matrices:
+ *
+ *     Y_i = X_i + gamma I   (X_i read from the upper triangle of x[i])
+ *     Y_i = U^T U  (Cholesky),  V = U^-1,  xinv[i] = V V^T = Y_i^-1
+ *
+ * computed in float64 on the GPU and written as float32, both triangles,
+ * exactly symmetric.  info[i] (device int32 array of n entries) receives 0 on
+ * success, or k > 0 when the leading minor of order k of Y_i is not positive
+ * definite or not finite (LAPACK xPOTRF convention); xinv[i] is then
+ * unspecified.  gamma must be finite and >= 0.  x[i] and xinv[j] must not
+ * overlap.
+ */
+size_t kfac_inverse_workspace_size(int n, const int64_t* d);
+kfac_status_t kfac_damped_inverse(int n, const float* const* x, const int64_t* d, float gamma,
+                                  float* const* xinv, int32_t* info,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ----------------------------------------------------------- precondition --
+ * Preconditioned gradient of each layer (the damped update rule that follows
+ * the Kronecker inverse property (A (x) G)^-1 = A^-1 (x) G^-1):
+ *
+ *     out[l] = ginv[l] . grad[l] . ainv[l]
+ *
+ * ginv[l] : [d_g[l], d_g[l]] float32, (G + gamma I)^-1, symmetric;
+ * grad[l] : [d_g[l], d_a[l]] float32 weight gradient (bias gradient in the
+ *           last column for layers with a bias);
+ * ainv[l] : [d_a[l], d_a[l]] float32, (A + gamma I)^-1, symmetric;
+ * out[l]  : [d_g[l], d_a[l]] float32.
+ * ginv and ainv must be exactly symmetric (as kfac_damped_inverse writes
+ * them): the kernels read them in whichever orientation coalesces.  out[l]
+ * must not overlap any input.
+ */
+size_t kfac_precondition_workspace_size(int n, const int64_t* d_g, const int64_t* d_a);
+kfac_status_t kfac_precondition(int n, const float* const* ginv, const float* const* grad,
+                                const float* const* ainv, const int64_t* d_g, const int64_t* d_a,
+                                float* const* out, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KFAC_H */

@@ -1,0 +1,40 @@
+// Device-side helpers shared by the kernels of the K-FAC library (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kfac {
+
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef double doublex4 __attribute__((ext_vector_type(4)));
+
+// Work items are numbered so that neighbours share input data.  The hardware
+// hands consecutive workgroups to the 8 XCDs in turn, and each XCD has its
+// own L2; this remap gives every XCD one contiguous range of items instead,
+// so neighbouring items run under the same L2.  It is a bijection on
+// [0, count).
+__device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t count) {
+    const int64_t x = b & 7, local = b >> 3;
+    const int64_t q = count >> 3, r = count & 7;
+    if (count < 8) return b;
+    return x * q + (x < r ? x : r) + local;
+}
+
+// Row-major enumeration of the upper triangle (i <= j) of a T x T grid:
+// row i holds T - i entries.  t in [0, T(T+1)/2).
+__device__ __forceinline__ void upper_decode(int64_t t, int64_t T, int& i, int& j) {
+    // closed form from the quadratic, then fix-ups for rounding
+    const double a = 2.0 * (double)T + 1.0;
+    int64_t r = (int64_t)((a - sqrt(a * a - 8.0 * (double)t)) * 0.5);
+    if (r < 0) r = 0;
+    if (r > T - 1) r = T - 1;
+    while (r > 0 && r * T - r * (r - 1) / 2 > t) --r;
+    while (r + 1 < T && (r + 1) * T - (r + 1) * r / 2 <= t) ++r;
+    i = (int)r;
+    j = (int)(r + (t - (r * T - r * (r - 1) / 2)));
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+}  // namespace kfac

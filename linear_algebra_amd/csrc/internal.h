@@ -1,0 +1,148 @@
+// Internal declarations shared by the host launchers and the kernels of the
+// K-FAC library.  Nothing here is part of the public ABI (include/kfac.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kfac {
+
+// ----------------------------------------------------------------- tables --
+// Per-call descriptor tables live in the caller's workspace.  They are
+// written by a tiny kernel whose by-value argument carries the bytes, so the
+// upload is ordered on the stream like every other launch, needs no pinned
+// host memory, and survives stream capture.
+constexpr int kTableChunk = 2048;
+struct TableChunk {
+    uint8_t bytes[kTableChunk];
+};
+hipError_t upload_table(void* dst_device, const void* src_host, size_t nbytes, hipStream_t stream);
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// --------------------------------------------------------- fp32 MFMA GEMM --
+// C = alpha * Aop^T Bop with Aop [K][lda] and Bop [K][ldb] row-major (the
+// reduction index is the slow index of both operands).  Used for
+//   factors:        Aop = Bop = X [rows][d], upper tiles only, running average;
+//   precondition:   S^T = grad^T Z_G  (Aop = grad, Bop = Z_G)  and
+//                   P   = (S^T)^T Z_A (Aop = S^T,  Bop = Z_A).
+constexpr int kGemmTile = 128;     // output tile edge (BM = BN)
+constexpr int kGemmBK = 16;        // rows of each operand staged per LDS buffer
+constexpr int kGemmThreads = 256;  // 4 waves, 2 x 2 over the tile, 64 x 64 each
+constexpr int kGemmSubK = 512;     // rows accumulated before folding into the running sum
+
+enum GemmMode : int32_t { kModePlain = 0, kModeFactor = 1 };
+
+struct GemmProb {
+    const void* a;        // Aop
+    const void* b;        // Bop (== a for factors)
+    float* c;             // output (factor: running-average matrix M)
+    float* part;          // split-K partial tiles (nullptr when ksplit == 1)
+    int64_t lda, ldb, ldc;
+    int64_t item_begin;   // first work item of this problem in the GEMM launch
+    int64_t red_begin;    // first tile of this problem in the split-K reduce launch
+    int32_t M, N, K;
+    int32_t tiles_m, tiles_n;
+    int32_t ntiles;       // output tiles (upper tiles only for factors)
+    int32_t ksplit;       // K chunks
+    int32_t kchunk;       // rows per chunk, multiple of kGemmBK
+    int32_t mode;         // GemmMode
+    int32_t bf16;         // operands are bfloat16 bit patterns
+    float alpha;
+    float pad_;
+};
+
+struct GemmLaunch {
+    const GemmProb* probs;
+    int32_t nprob;
+    int32_t first_step;
+    float eps;
+    int32_t pad_;
+};
+
+hipError_t launch_gemm(const GemmLaunch& L, int64_t items, hipStream_t stream, bool bf16);
+hipError_t launch_gemm_reduce(const GemmLaunch& L, int64_t tiles, hipStream_t stream);
+
+// ------------------------------------------------------------------- pack --
+struct PackLayer {
+    float* m;             // [d][d] matrix
+    int64_t d;
+    int64_t off;          // first packed element of this layer
+    int64_t tile_begin;   // first unpack tile of this layer
+    int64_t tiles_1d;     // unpack tiles per edge
+};
+hipError_t launch_pack(const PackLayer* layers_dev, int n, float* packed, int64_t total, hipStream_t stream);
+hipError_t launch_unpack(const PackLayer* layers_dev, int n, const float* packed, int64_t tiles,
+                         hipStream_t stream);
+constexpr int kUnpackTile = 64;
+
+// ---------------------------------------------------------------- inverse --
+// Every matrix is padded with the identity to D = NB * kInvNB and factored in
+// float64 in the workspace.  Matrices are grouped in buckets of equal NB,
+// largest first; each blocked step launches over all matrices that still
+// have work at that step.
+constexpr int kInvNB = 64;
+constexpr int kInvThreads = 256;
+
+struct InvMat {
+    const float* x;       // input (upper read), [d][d]
+    float* z;             // output, [d][d]
+    double* w;            // workspace [D][D] float64: U, then V = U^-1 above the diagonal
+    double* dinv;         // workspace [NB][64][64]: inverses of the diagonal blocks of U
+    int32_t* info;        // &info[original index]
+    int32_t d;
+    int32_t nb;           // blocks per edge
+};
+
+struct InvBucket {
+    int32_t nb;           // blocks per edge of every matrix in the bucket
+    int32_t first;        // first matrix (index into the sorted InvMat table)
+    int32_t count;        // matrices in the bucket
+    int32_t pad_;
+};
+
+struct InvLaunch {
+    const InvMat* mats;
+    const InvBucket* buckets;
+    int32_t nbuckets;
+    int32_t step;         // k for potrf steps, level for trtri
+    double gamma;
+};
+
+// Tiles each inverse kernel needs per matrix with nb blocks per edge at a
+// given potrf step (trsm, syrk) or trtri level.  Shared by the host, which
+// sizes the grids, and the kernels, which decode their tile index.
+enum InvKind : int32_t { kInvPrepare = 0, kInvTrsm = 1, kInvSyrk = 2, kInvTrtri = 3, kInvLauum = 4 };
+
+__host__ __device__ inline int64_t inv_tiles(int kind, int64_t nb, int64_t step) {
+    switch (kind) {
+        case kInvPrepare:
+        case kInvLauum:
+            return nb * (nb + 1) / 2;
+        case kInvTrsm:
+            return nb - step - 1 > 0 ? nb - step - 1 : 0;
+        case kInvSyrk: {
+            const int64_t t = nb - step - 1;
+            return t > 0 ? t * (t + 1) / 2 : 0;
+        }
+        case kInvTrtri: {
+            // level >= 1 joins pairs of groups of h = 2^(level-1) blocks
+            const int64_t h = int64_t(1) << (step - 1), g = 2 * h;
+            const int64_t full = nb / g, rem = nb % g;
+            return full * h * h + (rem > h ? h * (rem - h) : 0);
+        }
+        default:
+            return 0;
+    }
+}
+
+hipError_t launch_inv_prepare(const InvLaunch& L, int64_t tiles, hipStream_t s);
+hipError_t launch_inv_trsm(const InvLaunch& L, int64_t tiles, hipStream_t s);
+hipError_t launch_inv_syrk(const InvLaunch& L, int64_t tiles, hipStream_t s);
+hipError_t launch_inv_trtri_a(const InvLaunch& L, int64_t tiles, hipStream_t s);
+hipError_t launch_inv_trtri_b(const InvLaunch& L, int64_t tiles, hipStream_t s);
+hipError_t launch_inv_lauum(const InvLaunch& L, int64_t tiles, hipStream_t s);
+
+}  // namespace kfac

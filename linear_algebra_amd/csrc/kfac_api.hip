@@ -1,0 +1,418 @@
+// Host side of the C ABI declared in include/kfac.h: argument validation,
+// work planning, descriptor tables and launch sequences.  No device memory
+// is allocated here; all scratch lives in the caller's workspace.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <numeric>
+#include <vector>
+
+#include "../../include/kfac.h"
+#include "internal.h"
+
+namespace kfac {
+namespace {
+
+__global__ void table_write_kernel(uint8_t* dst, TableChunk c, int nbytes) {
+    for (int i = threadIdx.x; i < nbytes; i += blockDim.x) dst[i] = c.bytes[i];
+}
+
+constexpr size_t kAlign = 256;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Bump allocator over the caller's workspace (or a size-only dry run).
+struct Carver {
+    uint8_t* base;
+    size_t used = 0;
+    explicit Carver(void* b) : base(static_cast<uint8_t*>(b)) {}
+    void* take(size_t bytes) {
+        void* p = base ? base + used : nullptr;
+        used = align_up(used + bytes, kAlign);
+        return p;
+    }
+};
+
+kfac_status_t hip_status(hipError_t e) { return e == hipSuccess ? KFAC_OK : KFAC_ERR_HIP; }
+
+bool valid_dims(int n, const int64_t* d) {
+    if (n < 1 || n > KFAC_MAX_COUNT || d == nullptr) return false;
+    for (int i = 0; i < n; ++i)
+        if (d[i] < 1 || d[i] > KFAC_MAX_DIM) return false;
+    return true;
+}
+
+// ------------------------------------------------------------- factors --
+
+struct FactorPlan {
+    std::vector<GemmProb> probs;
+    int64_t items = 0;
+    int64_t red_tiles = 0;
+    size_t part_bytes = 0;
+};
+
+// Rows per K chunk: enough chunks overall to keep every CU busy, never so
+// many that the partial tiles outweigh the work.
+FactorPlan plan_factors(int n, const int64_t* rows, const int64_t* d) {
+    FactorPlan p;
+    p.probs.resize(n);
+    double work = 0.0;
+    for (int i = 0; i < n; ++i) {
+        const int64_t t = ceil_div(d[i], kGemmTile);
+        work += (double)(t * (t + 1) / 2) * (double)rows[i];
+    }
+    const double target_items = 4096.0;
+    int64_t kc = (int64_t)std::ceil(work / target_items);
+    kc = std::max<int64_t>(kc, 1024);
+    kc = align_up(kc, kGemmSubK);
+    int64_t part_elems = 0;
+    for (int i = 0; i < n; ++i) {
+        GemmProb& g = p.probs[i];
+        std::memset(&g, 0, sizeof(g));
+        const int64_t t = ceil_div(d[i], kGemmTile);
+        g.lda = g.ldb = g.ldc = d[i];
+        g.M = g.N = (int32_t)d[i];
+        g.K = (int32_t)rows[i];
+        g.tiles_m = g.tiles_n = (int32_t)t;
+        g.ntiles = (int32_t)(t * (t + 1) / 2);
+        const int64_t ksplit = std::max<int64_t>(1, ceil_div(rows[i], kc));
+        g.ksplit = (int32_t)ksplit;
+        g.kchunk = (int32_t)align_up(ceil_div(rows[i], ksplit), kGemmBK);
+        g.mode = kModeFactor;
+        g.alpha = (float)(1.0 / (double)rows[i]);
+        g.item_begin = p.items;
+        g.red_begin = p.red_tiles;
+        p.items += (int64_t)g.ntiles * ksplit;
+        if (ksplit > 1) {
+            p.red_tiles += g.ntiles;
+            part_elems += (int64_t)g.ntiles * ksplit * kGemmTile * kGemmTile;
+        }
+    }
+    p.part_bytes = (size_t)part_elems * sizeof(float);
+    return p;
+}
+
+size_t factors_ws(const FactorPlan& p, int n) {
+    Carver c(nullptr);
+    c.take(sizeof(GemmProb) * n);
+    c.take(p.part_bytes);
+    return c.used;
+}
+
+// --------------------------------------------------------- precondition --
+
+size_t precondition_ws(int n, const int64_t* d_g, const int64_t* d_a) {
+    Carver c(nullptr);
+    c.take(sizeof(GemmProb) * n);
+    c.take(sizeof(GemmProb) * n);
+    for (int i = 0; i < n; ++i) c.take(sizeof(float) * (size_t)(d_g[i] * d_a[i]));
+    return c.used;
+}
+
+// -------------------------------------------------------------- inverse --
+
+struct InvPlan {
+    std::vector<int> order;  // matrices sorted by block count, largest first
+    std::vector<InvBucket> buckets;
+    int nbmax = 0;
+};
+
+InvPlan plan_inverse(int n, const int64_t* d) {
+    InvPlan p;
+    p.order.resize(n);
+    std::iota(p.order.begin(), p.order.end(), 0);
+    auto nb = [&](int i) { return (int)ceil_div(d[i], kInvNB); };
+    std::stable_sort(p.order.begin(), p.order.end(), [&](int a, int b) { return nb(a) > nb(b); });
+    for (int s = 0; s < n; ++s) {
+        const int b = nb(p.order[s]);
+        if (p.buckets.empty() || p.buckets.back().nb != b) p.buckets.push_back(InvBucket{b, s, 0, 0});
+        p.buckets.back().count++;
+    }
+    p.nbmax = nb(p.order[0]);
+    return p;
+}
+
+size_t inverse_ws(int n, const int64_t* d) {
+    Carver c(nullptr);
+    c.take(sizeof(InvMat) * n);
+    c.take(sizeof(InvBucket) * n);
+    for (int i = 0; i < n; ++i) {
+        const int64_t D = ceil_div(d[i], kInvNB) * kInvNB;
+        c.take(sizeof(double) * (size_t)(D * D));
+        c.take(sizeof(double) * (size_t)(D * kInvNB));
+    }
+    return c.used;
+}
+
+int64_t bucket_tiles(const InvPlan& p, int kind, int step) {
+    int64_t t = 0;
+    for (const InvBucket& b : p.buckets) t += inv_tiles(kind, b.nb, step) * b.count;
+    return t;
+}
+
+// -------------------------------------------------------------- packing --
+
+size_t pack_ws(int n) {
+    Carver c(nullptr);
+    c.take(sizeof(PackLayer) * n);
+    return c.used;
+}
+
+}  // namespace
+
+hipError_t upload_table(void* dst_device, const void* src_host, size_t nbytes, hipStream_t stream) {
+    const uint8_t* src = static_cast<const uint8_t*>(src_host);
+    uint8_t* dst = static_cast<uint8_t*>(dst_device);
+    for (size_t off = 0; off < nbytes; off += kTableChunk) {
+        TableChunk c;
+        const size_t nb = std::min<size_t>(kTableChunk, nbytes - off);
+        std::memcpy(c.bytes, src + off, nb);
+        hipLaunchKernelGGL(table_write_kernel, dim3(1), dim3(256), 0, stream, dst + off, c, (int)nb);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace kfac
+
+using namespace kfac;
+
+extern "C" {
+
+int kfac_abi_version(void) { return 1; }
+
+const char* kfac_status_string(kfac_status_t s) {
+    switch (s) {
+        case KFAC_OK: return "KFAC_OK";
+        case KFAC_ERR_INVALID_VALUE: return "KFAC_ERR_INVALID_VALUE";
+        case KFAC_ERR_WORKSPACE: return "KFAC_ERR_WORKSPACE";
+        case KFAC_ERR_UNSUPPORTED: return "KFAC_ERR_UNSUPPORTED";
+        case KFAC_ERR_HIP: return "KFAC_ERR_HIP";
+    }
+    return "KFAC_ERR_UNKNOWN";
+}
+
+// ---------------------------------------------------------------- factors --
+
+size_t kfac_factors_workspace_size(int n, const int64_t* rows, const int64_t* d, kfac_dtype_t in_dtype) {
+    if (!valid_dims(n, d) || rows == nullptr || (in_dtype != KFAC_F32 && in_dtype != KFAC_BF16)) return 0;
+    for (int i = 0; i < n; ++i)
+        if (rows[i] < 1 || rows[i] > INT32_MAX) return 0;
+    return factors_ws(plan_factors(n, rows, d), n);
+}
+
+kfac_status_t kfac_factors(int n, const void* const* x, const int64_t* rows, const int64_t* d,
+                           kfac_dtype_t in_dtype, float* const* m, float eps, int first_step,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!valid_dims(n, d) || x == nullptr || rows == nullptr || m == nullptr) return KFAC_ERR_INVALID_VALUE;
+    if (in_dtype != KFAC_F32 && in_dtype != KFAC_BF16) return KFAC_ERR_INVALID_VALUE;
+    if (!std::isfinite(eps) || eps < 0.0f || eps > 1.0f) return KFAC_ERR_INVALID_VALUE;
+    const size_t esz = in_dtype == KFAC_BF16 ? 2 : 4;
+    for (int i = 0; i < n; ++i) {
+        if (rows[i] < 1 || rows[i] > INT32_MAX) return KFAC_ERR_INVALID_VALUE;
+        if (x[i] == nullptr || m[i] == nullptr || !aligned(x[i], esz) || !aligned(m[i], 4)) return KFAC_ERR_INVALID_VALUE;
+    }
+    FactorPlan p = plan_factors(n, rows, d);
+    const size_t need = factors_ws(p, n);
+    if (workspace == nullptr || !aligned(workspace, kAlign) || workspace_bytes < need) return KFAC_ERR_WORKSPACE;
+
+    Carver c(workspace);
+    GemmProb* probs_dev = static_cast<GemmProb*>(c.take(sizeof(GemmProb) * n));
+    float* part = static_cast<float*>(c.take(p.part_bytes));
+    int64_t part_off = 0;
+    for (int i = 0; i < n; ++i) {
+        GemmProb& g = p.probs[i];
+        g.a = g.b = x[i];
+        g.c = m[i];
+        g.bf16 = in_dtype == KFAC_BF16;
+        if (g.ksplit > 1) {
+            g.part = part + part_off;
+            part_off += (int64_t)g.ntiles * g.ksplit * kGemmTile * kGemmTile;
+        }
+    }
+    hipError_t e = upload_table(probs_dev, p.probs.data(), sizeof(GemmProb) * n, stream);
+    if (e != hipSuccess) return KFAC_ERR_HIP;
+    GemmLaunch L{probs_dev, n, first_step ? 1 : 0, eps, 0};
+    e = launch_gemm(L, p.items, stream, in_dtype == KFAC_BF16);
+    if (e != hipSuccess) return KFAC_ERR_HIP;
+    return hip_status(launch_gemm_reduce(L, p.red_tiles, stream));
+}
+
+// ------------------------------------------------------------------- pack --
+
+int64_t kfac_packed_size(int n, const int64_t* d) {
+    if (!valid_dims(n, d)) return -1;
+    int64_t s = 0;
+    for (int i = 0; i < n; ++i) s += d[i] * (d[i] + 1) / 2;
+    return s;
+}
+
+size_t kfac_pack_workspace_size(int n, const int64_t* d) {
+    if (!valid_dims(n, d)) return 0;
+    return pack_ws(n);
+}
+
+kfac_status_t kfac_pack_sym(int n, float* const* m, const int64_t* d, float* packed, kfac_pack_dir_t dir,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!valid_dims(n, d) || m == nullptr || packed == nullptr || !aligned(packed, 4)) return KFAC_ERR_INVALID_VALUE;
+    if (dir != KFAC_PACK && dir != KFAC_UNPACK) return KFAC_ERR_INVALID_VALUE;
+    for (int i = 0; i < n; ++i)
+        if (m[i] == nullptr || !aligned(m[i], 4)) return KFAC_ERR_INVALID_VALUE;
+    const size_t need = pack_ws(n);
+    if (workspace == nullptr || !aligned(workspace, kAlign) || workspace_bytes < need) return KFAC_ERR_WORKSPACE;
+
+    std::vector<PackLayer> layers(n);
+    int64_t off = 0, tiles = 0;
+    for (int i = 0; i < n; ++i) {
+        const int64_t t1 = ceil_div(d[i], kUnpackTile);
+        layers[i] = PackLayer{m[i], d[i], off, tiles, t1};
+        off += d[i] * (d[i] + 1) / 2;
+        tiles += t1 * (t1 + 1) / 2;
+    }
+    Carver c(workspace);
+    PackLayer* dev = static_cast<PackLayer*>(c.take(sizeof(PackLayer) * n));
+    hipError_t e = upload_table(dev, layers.data(), sizeof(PackLayer) * n, stream);
+    if (e != hipSuccess) return KFAC_ERR_HIP;
+    if (dir == KFAC_PACK) return hip_status(launch_pack(dev, n, packed, off, stream));
+    return hip_status(launch_unpack(dev, n, packed, tiles, stream));
+}
+
+// ---------------------------------------------------------------- inverse --
+
+size_t kfac_inverse_workspace_size(int n, const int64_t* d) {
+    if (!valid_dims(n, d)) return 0;
+    return inverse_ws(n, d);
+}
+
+kfac_status_t kfac_damped_inverse(int n, const float* const* x, const int64_t* d, float gamma,
+                                  float* const* xinv, int32_t* info,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!valid_dims(n, d) || x == nullptr || xinv == nullptr || info == nullptr || !aligned(info, 4))
+        return KFAC_ERR_INVALID_VALUE;
+    if (!std::isfinite(gamma) || gamma < 0.0f) return KFAC_ERR_INVALID_VALUE;
+    for (int i = 0; i < n; ++i)
+        if (x[i] == nullptr || xinv[i] == nullptr || !aligned(x[i], 4) || !aligned(xinv[i], 4))
+            return KFAC_ERR_INVALID_VALUE;
+    const size_t need = inverse_ws(n, d);
+    if (workspace == nullptr || !aligned(workspace, kAlign) || workspace_bytes < need) return KFAC_ERR_WORKSPACE;
+
+    InvPlan p = plan_inverse(n, d);
+    Carver c(workspace);
+    InvMat* mats_dev = static_cast<InvMat*>(c.take(sizeof(InvMat) * n));
+    InvBucket* buckets_dev = static_cast<InvBucket*>(c.take(sizeof(InvBucket) * n));
+    // per-matrix scratch in original order
+    std::vector<double*> w(n), dinv(n);
+    for (int i = 0; i < n; ++i) {
+        const int64_t D = ceil_div(d[i], kInvNB) * kInvNB;
+        w[i] = static_cast<double*>(c.take(sizeof(double) * (size_t)(D * D)));
+        dinv[i] = static_cast<double*>(c.take(sizeof(double) * (size_t)(D * kInvNB)));
+    }
+    std::vector<InvMat> mats(n);
+    for (int s = 0; s < n; ++s) {
+        const int i = p.order[s];
+        mats[s] = InvMat{x[i], xinv[i], w[i], dinv[i], info + i, (int32_t)d[i], (int32_t)ceil_div(d[i], kInvNB)};
+    }
+    hipError_t e = upload_table(mats_dev, mats.data(), sizeof(InvMat) * n, stream);
+    if (e == hipSuccess) e = upload_table(buckets_dev, p.buckets.data(), sizeof(InvBucket) * p.buckets.size(), stream);
+    if (e != hipSuccess) return KFAC_ERR_HIP;
+
+    InvLaunch L{mats_dev, buckets_dev, (int32_t)p.buckets.size(), 0, (double)gamma};
+    e = launch_inv_prepare(L, bucket_tiles(p, kInvPrepare, 0), stream);
+    for (int k = 0; e == hipSuccess && k + 1 < p.nbmax; ++k) {
+        L.step = k;
+        e = launch_inv_trsm(L, bucket_tiles(p, kInvTrsm, k), stream);
+        if (e == hipSuccess) e = launch_inv_syrk(L, bucket_tiles(p, kInvSyrk, k), stream);
+    }
+    for (int lvl = 1; e == hipSuccess && (1 << (lvl - 1)) < p.nbmax; ++lvl) {
+        L.step = lvl;
+        const int64_t t = bucket_tiles(p, kInvTrtri, lvl);
+        e = launch_inv_trtri_a(L, t, stream);
+        if (e == hipSuccess) e = launch_inv_trtri_b(L, t, stream);
+    }
+    if (e == hipSuccess) {
+        L.step = 0;
+        e = launch_inv_lauum(L, bucket_tiles(p, kInvLauum, 0), stream);
+    }
+    return hip_status(e);
+}
+
+// ----------------------------------------------------------- precondition --
+
+size_t kfac_precondition_workspace_size(int n, const int64_t* d_g, const int64_t* d_a) {
+    if (!valid_dims(n, d_g) || !valid_dims(n, d_a)) return 0;
+    return precondition_ws(n, d_g, d_a);
+}
+
+kfac_status_t kfac_precondition(int n, const float* const* ginv, const float* const* grad,
+                                const float* const* ainv, const int64_t* d_g, const int64_t* d_a,
+                                float* const* out, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+    if (!valid_dims(n, d_g) || !valid_dims(n, d_a) || ginv == nullptr || grad == nullptr || ainv == nullptr ||
+        out == nullptr)
+        return KFAC_ERR_INVALID_VALUE;
+    for (int i = 0; i < n; ++i) {
+        if (ginv[i] == nullptr || grad[i] == nullptr || ainv[i] == nullptr || out[i] == nullptr)
+            return KFAC_ERR_INVALID_VALUE;
+        if (!aligned(ginv[i], 4) || !aligned(grad[i], 4) || !aligned(ainv[i], 4) || !aligned(out[i], 4))
+            return KFAC_ERR_INVALID_VALUE;
+    }
+    const size_t need = precondition_ws(n, d_g, d_a);
+    if (workspace == nullptr || !aligned(workspace, kAlign) || workspace_bytes < need) return KFAC_ERR_WORKSPACE;
+
+    Carver c(workspace);
+    GemmProb* p1_dev = static_cast<GemmProb*>(c.take(sizeof(GemmProb) * n));
+    GemmProb* p2_dev = static_cast<GemmProb*>(c.take(sizeof(GemmProb) * n));
+    std::vector<GemmProb> p1(n), p2(n);
+    int64_t items1 = 0, items2 = 0;
+    for (int i = 0; i < n; ++i) {
+        float* st = static_cast<float*>(c.take(sizeof(float) * (size_t)(d_g[i] * d_a[i])));
+        // S^T [d_a][d_g] = grad^T . ginv   (ginv symmetric)
+        GemmProb& a = p1[i];
+        std::memset(&a, 0, sizeof(a));
+        a.a = grad[i];
+        a.b = ginv[i];
+        a.c = st;
+        a.lda = d_a[i];
+        a.ldb = d_g[i];
+        a.ldc = d_g[i];
+        a.M = (int32_t)d_a[i];
+        a.N = (int32_t)d_g[i];
+        a.K = (int32_t)d_g[i];
+        // P [d_g][d_a] = (S^T)^T . ainv
+        GemmProb& b = p2[i];
+        std::memset(&b, 0, sizeof(b));
+        b.a = st;
+        b.b = ainv[i];
+        b.c = out[i];
+        b.lda = d_g[i];
+        b.ldb = d_a[i];
+        b.ldc = d_a[i];
+        b.M = (int32_t)d_g[i];
+        b.N = (int32_t)d_a[i];
+        b.K = (int32_t)d_a[i];
+        for (GemmProb* g : {&a, &b}) {
+            g->tiles_m = (int32_t)ceil_div(g->M, kGemmTile);
+            g->tiles_n = (int32_t)ceil_div(g->N, kGemmTile);
+            g->ntiles = g->tiles_m * g->tiles_n;
+            g->ksplit = 1;
+            g->kchunk = (int32_t)align_up(g->K, kGemmBK);
+            g->mode = kModePlain;
+            g->alpha = 1.0f;
+        }
+        a.item_begin = items1;
+        b.item_begin = items2;
+        items1 += a.ntiles;
+        items2 += b.ntiles;
+    }
+    hipError_t e = upload_table(p1_dev, p1.data(), sizeof(GemmProb) * n, stream);
+    if (e == hipSuccess) e = upload_table(p2_dev, p2.data(), sizeof(GemmProb) * n, stream);
+    if (e != hipSuccess) return KFAC_ERR_HIP;
+    GemmLaunch L1{p1_dev, n, 0, 0.0f, 0};
+    e = launch_gemm(L1, items1, stream, false);
+    if (e != hipSuccess) return KFAC_ERR_HIP;
+    GemmLaunch L2{p2_dev, n, 0, 0.0f, 0};
+    return hip_status(launch_gemm(L2, items2, stream, false));
+}
+
+}  // extern "C"

@@ -101,6 +101,12 @@ def factor_entries(x, ii, jj) -> np.ndarray:
     return out / x.shape[0]
 
 
+def factor_diagonal(x) -> np.ndarray:
+    """Diagonal of the factor: F[i][i] = (1/rows) sum_r x[r, i]^2."""
+    x = _f64(x)
+    return np.einsum("ri,ri->i", x, x) / x.shape[0]
+
+
 def running_average(m_prev, f, eps: float, first: bool) -> np.ndarray:
     """M = F on the first step, else eps * M_prev + (1 - eps) * F."""
     f = _f64(f)
@@ -205,7 +211,7 @@ def rel_fro_upper(x, ref) -> float:
 
 
 __all__ = [
-    "upcast", "factor", "factor_entries", "running_average", "packed_size", "pack", "unpack",
+    "upcast", "factor", "factor_entries", "factor_diagonal", "running_average", "packed_size", "pack", "unpack",
     "cholesky_upper", "damped_inverse", "damped_inverse_columns", "precondition",
     "precondition_entries", "rel_fro", "rel_fro_upper",
 ]

@@ -1,0 +1,139 @@
+"""Host-side checks of the C ABI: the library loads without a GPU, exports
+every entry point include/kfac.h declares, and rejects bad arguments before
+enqueuing anything (these calls never reach the HIP runtime)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_algebra_amd as la
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from linear_algebra_amd import build
+    build.build()
+    return la.load_library()
+
+
+def declared_functions():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(kfac_[a-z0-9_]+)\s*\(", text))
+    return names
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared_functions()
+    for n in ("kfac_factors", "kfac_pack_sym", "kfac_damped_inverse", "kfac_precondition"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert names == set(la.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.kfac_abi_version() == 1
+    assert la.status_string(0) == "KFAC_OK"
+    assert la.status_string(2) == "KFAC_ERR_WORKSPACE"
+    assert la.status_string(99) == "KFAC_ERR_UNKNOWN"
+
+
+def i64(v):
+    return (ctypes.c_int64 * len(v))(*v)
+
+
+def vps(v):
+    return (ctypes.c_void_p * len(v))(*v)
+
+
+def test_packed_size(lib):
+    d = [1, 2, 65, 4608]
+    assert lib.kfac_packed_size(len(d), i64(d)) == sum(x * (x + 1) // 2 for x in d)
+    assert lib.kfac_packed_size(0, i64([1])) == -1
+    assert lib.kfac_packed_size(1, i64([0])) == -1
+    assert lib.kfac_packed_size(1, i64([16385])) == -1
+
+
+def test_workspace_sizes(lib):
+    d, rows = [65, 2049], [32, 128]
+    assert lib.kfac_factors_workspace_size(2, i64(rows), i64(d), 0) > 0
+    assert lib.kfac_factors_workspace_size(2, i64(rows), i64(d), 7) == 0
+    assert lib.kfac_factors_workspace_size(1, i64([0]), i64([4]), 0) == 0
+    # the inverse keeps one float64 copy of every padded matrix
+    ws = lib.kfac_inverse_workspace_size(2, i64(d))
+    assert ws >= 8 * (128 * 128 + 2112 * 2112)
+    assert lib.kfac_inverse_workspace_size(0, i64(d)) == 0
+    assert lib.kfac_precondition_workspace_size(1, i64([32]), i64([65])) >= 4 * 32 * 65
+    assert lib.kfac_pack_workspace_size(2, i64(d)) > 0
+
+
+def test_split_k_partials_for_tall_inputs(lib):
+    # a 401408 x 147 input needs split-K partial tiles beyond the descriptor table
+    small = lib.kfac_factors_workspace_size(1, i64([128]), i64([147]), 0)
+    tall = lib.kfac_factors_workspace_size(1, i64([401408]), i64([147]), 0)
+    assert tall > small + 3 * 128 * 128 * 4
+
+
+FAKE = 0x10000   # never dereferenced: every call below fails validation first
+
+
+def test_factors_rejects_bad_arguments(lib):
+    x, m = vps([FAKE]), vps([FAKE])
+    ws = ctypes.c_void_p(FAKE)
+    call = lambda n=1, x=x, rows=i64([8]), d=i64([4]), dt=0, m=m, eps=0.5, wsb=1 << 30, w=ws: \
+        lib.kfac_factors(n, x, rows, d, dt, m, ctypes.c_float(eps), 0, w, wsb, None)
+    assert call(n=0) == la.KFAC_ERR_INVALID_VALUE
+    assert call(d=i64([0])) == la.KFAC_ERR_INVALID_VALUE
+    assert call(rows=i64([0])) == la.KFAC_ERR_INVALID_VALUE
+    assert call(eps=1.5) == la.KFAC_ERR_INVALID_VALUE
+    assert call(eps=float("nan")) == la.KFAC_ERR_INVALID_VALUE
+    assert call(dt=3) == la.KFAC_ERR_INVALID_VALUE
+    assert call(x=vps([0])) == la.KFAC_ERR_INVALID_VALUE
+    assert call(x=vps([FAKE + 2])) == la.KFAC_ERR_INVALID_VALUE       # misaligned float32
+    assert call(wsb=16) == la.KFAC_ERR_WORKSPACE
+    assert call(w=ctypes.c_void_p(FAKE + 8)) == la.KFAC_ERR_WORKSPACE  # misaligned workspace
+    assert call(w=ctypes.c_void_p(0)) == la.KFAC_ERR_WORKSPACE
+
+
+def test_inverse_rejects_bad_arguments(lib):
+    x, z = vps([FAKE]), vps([FAKE])
+    info = ctypes.c_void_p(FAKE)
+    ws = ctypes.c_void_p(FAKE)
+    call = lambda n=1, d=i64([4]), g=1e-3, info=info, wsb=1 << 30: \
+        lib.kfac_damped_inverse(n, x, d, ctypes.c_float(g), z, info, ws, wsb, None)
+    assert call(g=-1.0) == la.KFAC_ERR_INVALID_VALUE
+    assert call(g=float("inf")) == la.KFAC_ERR_INVALID_VALUE
+    assert call(info=ctypes.c_void_p(0)) == la.KFAC_ERR_INVALID_VALUE
+    assert call(n=4097, d=i64([4] * 4097)) == la.KFAC_ERR_INVALID_VALUE
+    assert call(wsb=100) == la.KFAC_ERR_WORKSPACE
+
+
+def test_pack_and_precondition_reject_bad_arguments(lib):
+    m = vps([FAKE])
+    ws = ctypes.c_void_p(FAKE)
+    assert lib.kfac_pack_sym(1, m, i64([4]), ctypes.c_void_p(FAKE), 2, ws, 1 << 20, None) == la.KFAC_ERR_INVALID_VALUE
+    assert lib.kfac_pack_sym(1, m, i64([4]), ctypes.c_void_p(0), 0, ws, 1 << 20, None) == la.KFAC_ERR_INVALID_VALUE
+    assert lib.kfac_pack_sym(1, m, i64([4]), ctypes.c_void_p(FAKE), 0, ws, 0, None) == la.KFAC_ERR_WORKSPACE
+    p = vps([FAKE])
+    assert lib.kfac_precondition(1, p, p, p, i64([0]), i64([4]), p, ws, 1 << 20, None) == la.KFAC_ERR_INVALID_VALUE
+    assert lib.kfac_precondition(1, p, vps([0]), p, i64([4]), i64([4]), p, ws, 1 << 20, None) == la.KFAC_ERR_INVALID_VALUE
+    assert lib.kfac_precondition(1, p, p, p, i64([4]), i64([4]), p, ws, 8, None) == la.KFAC_ERR_WORKSPACE
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 3)
+    m = torch.zeros(3, 3)
+    with pytest.raises((ValueError, la.KfacLibraryError)):
+        la.kfac_factors([x], [m], 0.95, True)

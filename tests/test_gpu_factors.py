@@ -1,0 +1,160 @@
+"""GPU parity: Kronecker factors with running average against the fp64 oracle.
+
+Gate (relative Frobenius error on the upper triangle incl. the diagonal):
+1e-5 for float32 inputs, 2e-3 for bfloat16 inputs.  The oracle consumes the
+exact values given to the GPU (bf16 upcast exactly)."""
+import numpy as np
+import pytest
+
+import linear_algebra_amd as la
+import oracle
+from tests.gpu_helpers import nan_f32, say, to_dev, to_host, upper_rel_fro
+from workloads import CONFIGS, gen_a, gen_g, gen_layer_step
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32, TOL_BF16 = 1e-5, 2e-3
+EPS = 0.95
+
+
+def gpu_factors(xs, ms, eps, first):
+    la.kfac_factors([to_dev(x) if isinstance(x, np.ndarray) else x for x in xs], ms, eps, first)
+
+
+@pytest.mark.parametrize("shapes", [
+    [(1, 1)],
+    [(32, 65), (32, 32)],
+    [(100, 129), (7, 300), (1000, 64), (3, 2)],
+    [(5000, 257), (2000, 130), (600, 1)],
+])
+def test_factors_small_running_average(shapes):
+    """First step, then two running-average steps, several layers per call
+    (ragged tails in rows and in both tile directions)."""
+    say("factors small", shapes)
+    rng = np.random.default_rng(len(shapes) * 7 + shapes[0][1])
+    ms = [nan_f32(d, d) for _, d in shapes]
+    ref = [None] * len(shapes)
+    for step in range(3):
+        xs = [np.maximum(rng.standard_normal((r, d)), 0).astype(np.float32) for r, d in shapes]
+        gpu_factors(xs, ms, EPS, step == 0)
+        for k, x in enumerate(xs):
+            ref[k] = oracle.running_average(ref[k], oracle.factor(oracle.upcast(x)), np.float32(EPS), step == 0)
+        for k, m in enumerate(ms):
+            got = to_host(m)
+            err = upper_rel_fro(got, ref[k])
+            assert err <= TOL_F32, (shapes[k], step, err)
+            # strict lower triangle is left as it was (NaN sentinel)
+            assert np.all(np.isnan(got[np.tril_indices(shapes[k][1], -1)]))
+
+
+def test_factors_tall_split_k():
+    """Very tall inputs use split-K partial tiles and the fixed-order reduce."""
+    say("factors tall split-K")
+    rng = np.random.default_rng(3)
+    xs = [np.maximum(rng.standard_normal((200000, 147)), 0).astype(np.float32),
+          rng.standard_normal((150000, 64)).astype(np.float32)]
+    ms = [nan_f32(147, 147), nan_f32(64, 64)]
+    gpu_factors(xs, ms, EPS, True)
+    for x, m in zip(xs, ms):
+        err = upper_rel_fro(to_host(m), oracle.factor(oracle.upcast(x)))
+        say("  tall err", x.shape, err)
+        assert err <= TOL_F32
+
+
+def test_factors_deterministic():
+    rng = np.random.default_rng(4)
+    x = to_dev(rng.standard_normal((70000, 300)).astype(np.float32))
+    m1, m2 = nan_f32(300, 300), nan_f32(300, 300)
+    la.kfac_factors([x], [m1], EPS, True)
+    la.kfac_factors([x], [m2], EPS, True)
+    np.testing.assert_array_equal(to_host(m1).view(np.uint32)[np.triu_indices(300)],
+                                  to_host(m2).view(np.uint32)[np.triu_indices(300)])
+
+
+def test_factors_bf16_small():
+    from workloads import f32_to_bf16_bits
+    rng = np.random.default_rng(5)
+    shapes = [(4096, 1025), (300, 70)]
+    xs = [f32_to_bf16_bits(0.02 * rng.standard_normal((r, d)).astype(np.float32)) for r, d in shapes]
+    ms = [nan_f32(d, d) for _, d in shapes]
+    gpu_factors(xs, ms, EPS, True)
+    for x, m in zip(xs, ms):
+        err = upper_rel_fro(to_host(m), oracle.factor(oracle.upcast(x, "bf16")))
+        say("  bf16 err", x.shape, err)
+        assert err <= TOL_BF16
+
+
+def run_config_factors(cid, steps=None):
+    """A factors then G factors of every layer, as one call each, for the
+    given steps of the workload's schedule; full comparison with the oracle."""
+    cfg = CONFIGS[cid]
+    steps = cfg.steps if steps is None else steps
+    L = cfg.layers
+    ma = [nan_f32(l.d_a, l.d_a) for l in L]
+    mg = [nan_f32(l.d_g, l.d_g) for l in L]
+    ref_a, ref_g = [None] * len(L), [None] * len(L)
+    worst = 0.0
+    for step in range(steps):
+        data = gen_layer_step(cfg, step, threads=16)
+        a = [t[0] for t in data]
+        g = [t[1] for t in data]
+        gpu_factors(a, ma, EPS, step == 0)
+        gpu_factors(g, mg, EPS, step == 0)
+        tol = TOL_BF16 if cfg.in_dtype == "bf16" else TOL_F32
+        for k in range(len(L)):
+            fa = oracle.factor(oracle.upcast(a[k], cfg.in_dtype))
+            fg = oracle.factor(oracle.upcast(g[k], cfg.in_dtype))
+            ref_a[k] = oracle.running_average(ref_a[k], fa, np.float32(EPS), step == 0)
+            ref_g[k] = oracle.running_average(ref_g[k], fg, np.float32(EPS), step == 0)
+            ea = upper_rel_fro(to_host(ma[k]), ref_a[k])
+            eg = upper_rel_fro(to_host(mg[k]), ref_g[k])
+            worst = max(worst, ea, eg)
+            assert ea <= tol and eg <= tol, (cid, step, L[k].name, ea, eg)
+        del data, a, g
+    say(f"config {cid}: worst factor rel err {worst:.3e} over {steps} step(s)")
+
+
+def test_factors_config1():
+    run_config_factors(1)
+
+
+def test_factors_config2_two_steps():
+    run_config_factors(2, steps=2)
+
+
+def test_factors_config3_full():
+    say("config 3 factors (ResNet-50 shapes, 108 factors)")
+    run_config_factors(3)
+
+
+def test_factors_config4_bf16_full():
+    say("config 4 factors (encoder, bf16 inputs)")
+    run_config_factors(4)
+
+
+def test_factors_config5_sampled():
+    """Large-factor workload: every layer in one call, checked on sampled
+    entries (and every diagonal) against the oracle's entry-wise sums."""
+    cfg = CONFIGS[5]
+    say("config 5 factors (16 large layers), sampled")
+    data = gen_layer_step(cfg, 0, threads=16)
+    L = cfg.layers
+    ma = [nan_f32(l.d_a, l.d_a) for l in L]
+    la.kfac_factors([to_dev(t[0]) for t in data], ma, EPS, True)
+    rng = np.random.default_rng(55)
+    worst = 0.0
+    for k in range(0, len(L), 3):
+        x = data[k][0]
+        d = x.shape[1]
+        got = to_host(ma[k])
+        ii = rng.integers(0, d, 24)
+        jj = rng.integers(0, d, 24)
+        ii, jj = np.minimum(ii, jj), np.maximum(ii, jj)
+        diag = oracle.factor_diagonal(x)
+        ref = oracle.factor_entries(x, ii, jj)
+        scale = np.sqrt(diag[ii] * diag[jj])
+        err = np.abs(got[ii, jj] - ref) / scale
+        derr = np.abs(np.diag(got) - diag) / diag
+        worst = max(worst, err.max(), derr.max())
+        assert err.max() <= TOL_F32 and derr.max() <= TOL_F32, (L[k].name, err.max(), derr.max())
+    say(f"config 5: worst sampled relative error {worst:.3e}")

@@ -1,0 +1,198 @@
+"""GPU parity: damped SPD inverse against the fp64 oracle.
+
+Gate: relative Frobenius error <= 1e-3 (for gamma >= 1e-3; the large-factor
+workload's gamma = 1e-4 is held to the same bound).  Both sides invert the
+same float32 matrix; the inputs are float32 roundings of oracle factors of
+the workloads' seeded activations and gradients (rank-deficient whenever a
+layer has fewer rows than its dimension), so the condition numbers are the
+workloads' own.  Outputs must also be exactly symmetric."""
+import numpy as np
+import pytest
+
+import linear_algebra_amd as la
+import oracle
+from tests.gpu_helpers import nan_f32, rel_fro, say, to_dev, to_host
+from workloads import CONFIGS, gen_a, gen_g
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-3
+
+
+def gpu_inverse(xs, gamma):
+    import torch
+    dx = [to_dev(x) for x in xs]
+    zs = [nan_f32(*x.shape) for x in xs]
+    info = torch.full((len(xs),), -7, dtype=torch.int32, device="cuda:0")
+    la.kfac_damped_inverse(dx, gamma, zs, info)
+    return [to_host(z) for z in zs], to_host(info)
+
+
+def factor_input(x, in_dtype="f32"):
+    return oracle.factor(oracle.upcast(x, in_dtype)).astype(np.float32)
+
+
+def spd_f32(rng, d, rows):
+    x = np.maximum(rng.standard_normal((rows, d)), 0).astype(np.float32)
+    return factor_input(x)
+
+
+@pytest.mark.parametrize("dims", [[1], [2, 3], [63, 64, 65], [100, 128, 129, 1], [200, 257, 64, 64, 31]])
+def test_inverse_small_batch(dims):
+    say("inverse small", dims)
+    rng = np.random.default_rng(sum(dims))
+    gamma = np.float32(1e-3)
+    xs = [spd_f32(rng, d, max(1, d // 2)) for d in dims]   # rank-deficient
+    zs, info = gpu_inverse(xs, gamma)
+    assert np.all(info == 0), info
+    for x, z in zip(xs, zs):
+        ref, rinfo = oracle.damped_inverse(x, gamma)
+        assert rinfo == 0
+        err = rel_fro(z, ref)
+        say("  d", x.shape[0], "err", err)
+        assert err <= TOL
+        np.testing.assert_array_equal(z, z.T)
+
+
+def test_inverse_reads_upper_only():
+    rng = np.random.default_rng(8)
+    x = spd_f32(rng, 150, 300)
+    xg = x.copy()
+    xg[np.tril_indices(150, -1)] = 1e30
+    z1, _ = gpu_inverse([x], 1e-2)
+    z2, _ = gpu_inverse([xg], 1e-2)
+    np.testing.assert_array_equal(z1[0], z2[0])
+
+
+def test_inverse_closed_forms():
+    gamma = np.float32(0.25)
+    d = 130
+    diag = np.linspace(0.0, 5.0, d).astype(np.float32)
+    zs, info = gpu_inverse([np.diag(diag), np.zeros((70, 70), np.float32)], gamma)
+    assert np.all(info == 0)
+    np.testing.assert_allclose(zs[0], np.diag(1.0 / (diag.astype(np.float64) + float(gamma))), rtol=1e-6, atol=1e-30)
+    np.testing.assert_allclose(zs[1], np.eye(70) / float(gamma), rtol=1e-6, atol=0)
+
+
+@pytest.mark.parametrize("k", [1, 5, 64, 65, 100])
+def test_inverse_info_reports_first_failing_pivot(k):
+    """A matrix whose leading minor of order k is negative reports info = k,
+    like the oracle; its neighbours in the batch are unaffected."""
+    d = 130
+    gamma = np.float32(1e-3)
+    bad = np.eye(d, dtype=np.float32)
+    bad[k - 1, k - 1] = np.float32(-1.0) - gamma
+    good = spd_f32(np.random.default_rng(k), 90, 200)
+    zs, info = gpu_inverse([good, bad, good], gamma)
+    _, rinfo = oracle.damped_inverse(bad, gamma)
+    assert rinfo == k
+    assert list(info) == [0, k, 0]
+    ref, _ = oracle.damped_inverse(good, gamma)
+    assert rel_fro(zs[0], ref) <= TOL and rel_fro(zs[2], ref) <= TOL
+
+
+def test_inverse_nan_reports_info():
+    d = 70
+    x = np.eye(d, dtype=np.float32)
+    x[10, 10] = np.nan
+    _, info = gpu_inverse([x], 1e-3)
+    _, rinfo = oracle.damped_inverse(x, np.float32(1e-3))
+    assert info[0] == rinfo == 11
+
+
+def config_factor_inputs(cid, rows_cap=None):
+    """float32 factors (A's then G's) of a workload's first step, from the
+    oracle; rows_cap limits the rows drawn per layer (same recipe)."""
+    cfg = CONFIGS[cid]
+    xs = []
+    for li, l in enumerate(cfg.layers):
+        r = l.rows if rows_cap is None else min(l.rows, rows_cap)
+        xs.append(factor_input(gen_a(cfg, 0, li, rows=r), cfg.in_dtype))
+    for li in reversed(range(cfg.n_layers)):
+        l = cfg.layers[li]
+        r = l.rows if rows_cap is None else min(l.rows, rows_cap)
+        xs.append(factor_input(gen_g(cfg, 0, li, rows=r), cfg.in_dtype))
+    return xs
+
+
+def check_sampled(xs, zs, gamma, pick, ncols=6, seed=0):
+    """Oracle columns of the picked matrices (one Cholesky each)."""
+    rng = np.random.default_rng(seed)
+    worst = 0.0
+    for k in pick:
+        d = xs[k].shape[0]
+        cols = np.unique(np.concatenate([[0, d - 1], rng.integers(0, d, ncols)]))
+        ref, info = oracle.damped_inverse_columns(xs[k], gamma, cols)
+        assert info == 0
+        err = rel_fro(zs[k][:, cols].T, ref)
+        worst = max(worst, err)
+        assert err <= TOL, (k, d, err)
+    return worst
+
+
+def test_inverse_config1_full():
+    xs = config_factor_inputs(1)
+    gamma = np.float32(0.01)
+    zs, info = gpu_inverse(xs, gamma)
+    assert np.all(info == 0)
+    for x, z in zip(xs, zs):
+        ref, _ = oracle.damped_inverse(x, gamma)
+        assert rel_fro(z, ref) <= TOL
+
+
+def test_inverse_config2_full():
+    xs = config_factor_inputs(2)
+    gamma = np.float32(1e-3)
+    say("config 2 inverse", [x.shape[0] for x in xs])
+    zs, info = gpu_inverse(xs, gamma)
+    assert np.all(info == 0)
+    for z in zs:
+        np.testing.assert_array_equal(z, z.T)
+    worst = check_sampled(xs, zs, gamma, range(len(xs)), ncols=8)
+    # the two 1025-wide and the 10-wide factors in full
+    for k, x in enumerate(xs):
+        if x.shape[0] <= 1025:
+            ref, _ = oracle.damped_inverse(x, gamma)
+            err = rel_fro(zs[k], ref)
+            worst = max(worst, err)
+            assert err <= TOL
+    say(f"config 2 inverse: worst rel err {worst:.3e}")
+
+
+def bucket_representatives(xs):
+    seen, pick = set(), []
+    for k, x in enumerate(xs):
+        b = (x.shape[0] + 63) // 64
+        if b not in seen:
+            seen.add(b)
+            pick.append(k)
+    return pick
+
+
+def test_inverse_config3_full_batch():
+    """All 108 ResNet-50 factors in one call; one matrix of every size bucket
+    checked against oracle columns, every output checked for symmetry."""
+    xs = config_factor_inputs(3, rows_cap=8192)
+    gamma = np.float32(1e-3)
+    say("config 3 inverse: 108 matrices")
+    zs, info = gpu_inverse(xs, gamma)
+    assert np.all(info == 0), info
+    for z in zs:
+        np.testing.assert_array_equal(z, z.T)
+    worst = check_sampled(xs, zs, gamma, bucket_representatives(xs))
+    say(f"config 3 inverse: worst sampled rel err {worst:.3e}")
+
+
+@pytest.mark.parametrize("gamma", [1e-2, 1e-4])
+def test_inverse_config5_ill_conditioned(gamma):
+    """Large factors with 10% of the input columns scaled x100: the largest
+    condition numbers of the five workloads."""
+    cfg = CONFIGS[5]
+    xs = [factor_input(gen_a(cfg, 0, li, rows=6000)) for li in (0, 1)] + \
+         [factor_input(gen_g(cfg, 0, li, rows=6000)) for li in (0, 1, 2)]
+    gamma = np.float32(gamma)
+    say("config 5 inverse, gamma", float(gamma), [x.shape[0] for x in xs])
+    zs, info = gpu_inverse(xs, gamma)
+    assert np.all(info == 0), info
+    worst = check_sampled(xs, zs, gamma, range(len(xs)), ncols=4)
+    say(f"config 5 inverse gamma={float(gamma)}: worst sampled rel err {worst:.3e}")

@@ -78,6 +78,13 @@ def test_factor_symmetric_psd():
     assert w.min() >= -1e-12 * np.linalg.norm(f)
 
 
+def test_factor_diagonal_is_trace_split():
+    rng = np.random.default_rng(16)
+    x = rng.standard_normal((29, 11))
+    np.testing.assert_allclose(oracle.factor_diagonal(x), (x * x).sum(axis=0) / 29, rtol=1e-14)
+    np.testing.assert_allclose(oracle.factor_diagonal(x), np.diag(oracle.factor(x)), rtol=1e-13)
+
+
 def test_factor_entries_agree_with_full():
     rng = np.random.default_rng(4)
     x = rng.standard_normal((300, 40)).astype(np.float32)
