@@ -193,16 +193,24 @@ __global__ __launch_bounds__(NT) void gemm_reduce_kernel(GemmLaunch L, int64_t t
         ti = t / P.tiles_n;
         tj = t % P.tiles_n;
     }
+    // thread t sums elements t + s*NT of the tile over the K chunks in
+    // chunk order; the PERR loads of one chunk are in flight together
+    constexpr int PERR = BM * BM / NT;
     const int64_t stride = (int64_t)P.ntiles * (BM * BM);
     const float* base = P.part + (int64_t)t * (BM * BM);
-    for (int e = threadIdx.x; e < BM * BM; e += NT) {
+    float s[PERR];
+#pragma unroll
+    for (int q = 0; q < PERR; ++q) s[q] = 0.0f;
+    for (int k = 0; k < P.ksplit; ++k) {
+        const float* pk = base + k * stride;
+#pragma unroll
+        for (int q = 0; q < PERR; ++q) s[q] += pk[threadIdx.x + q * NT];
+    }
+#pragma unroll
+    for (int q = 0; q < PERR; ++q) {
+        const int e = threadIdx.x + q * NT;
         const int row = e / BM, col = e % BM;
-        const int i = ti * BM + row, j = tj * BM + col;
-        if (i >= P.M || j >= P.N) continue;
-        if (P.mode == kModeFactor && j < i) continue;
-        float s = 0.0f;
-        for (int k = 0; k < P.ksplit; ++k) s += base[k * stride + e];
-        store_elem(P, i, j, s, L.eps, L.first_step);
+        store_elem(P, ti * BM + row, tj * BM + col, s[q], L.eps, L.first_step);
     }
 }
 

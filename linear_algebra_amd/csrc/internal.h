@@ -114,15 +114,15 @@ struct InvLaunch {
 // Tiles each inverse kernel needs per matrix with nb blocks per edge at a
 // given potrf step (trsm, syrk) or trtri level.  Shared by the host, which
 // sizes the grids, and the kernels, which decode their tile index.
-enum InvKind : int32_t { kInvPrepare = 0, kInvTrsm = 1, kInvSyrk = 2, kInvTrtri = 3, kInvLauum = 4 };
+enum InvKind : int32_t { kInvPrepare = 0, kInvPanel = 1, kInvSyrk = 2, kInvTrtri = 3, kInvLauum = 4 };
 
 __host__ __device__ inline int64_t inv_tiles(int kind, int64_t nb, int64_t step) {
     switch (kind) {
         case kInvPrepare:
         case kInvLauum:
             return nb * (nb + 1) / 2;
-        case kInvTrsm:
-            return nb - step - 1 > 0 ? nb - step - 1 : 0;
+        case kInvPanel:  // one workgroup per block right of the diagonal, at least one
+            return nb > step ? (nb - step - 1 > 1 ? nb - step - 1 : 1) : 0;
         case kInvSyrk: {
             const int64_t t = nb - step - 1;
             return t > 0 ? t * (t + 1) / 2 : 0;
@@ -139,7 +139,7 @@ __host__ __device__ inline int64_t inv_tiles(int kind, int64_t nb, int64_t step)
 }
 
 hipError_t launch_inv_prepare(const InvLaunch& L, int64_t tiles, hipStream_t s);
-hipError_t launch_inv_trsm(const InvLaunch& L, int64_t tiles, hipStream_t s);
+hipError_t launch_inv_panel_trsm(const InvLaunch& L, int64_t tiles, hipStream_t s);
 hipError_t launch_inv_syrk(const InvLaunch& L, int64_t tiles, hipStream_t s);
 hipError_t launch_inv_trtri_a(const InvLaunch& L, int64_t tiles, hipStream_t s);
 hipError_t launch_inv_trtri_b(const InvLaunch& L, int64_t tiles, hipStream_t s);

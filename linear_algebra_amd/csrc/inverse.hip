@@ -10,7 +10,7 @@
 //               trsm  U_kj = U_kk^-T W_kj           (j > k)
 //               syrk  W_ij -= U_ki^T U_kj           (k < i <= j); the
 //                     workgroup that updates block (k+1, k+1) then factors it
-//                     (Cholesky in LDS) and inverts its triangle;
+//                     and inverts its triangle (one wave, registers);
 //   trtri     V = U^-1 by recursive doubling over groups of blocks: for
 //             sibling groups G1, G2 (G1 before G2)
 //               V_12 = -V_11 . (U_12 . V_22)
@@ -22,6 +22,12 @@
 // a separate array (dinv).  Matrices are grouped in buckets of equal nb,
 // largest first; every launch covers every matrix that has work at that
 // step, so independent inverses of different layers run side by side.
+//
+// Block products stage 64 x 64 operand blocks in LDS; the next pair of
+// blocks is fetched into registers while the matrix cores work on the
+// current pair.
+#include <float.h>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -32,6 +38,7 @@ constexpr int B = kInvNB;      // block edge
 constexpr int LD = B + 1;      // LDS row stride in doubles (conflict-free columns)
 constexpr int NT = kInvThreads;
 constexpr int BB = B * B;
+constexpr int PER = BB / NT;   // block elements per thread (16)
 
 // Which matrix and which of its tiles a workgroup owns.
 __device__ __forceinline__ bool locate(const InvLaunch& L, int kind, int64_t tile, int& mat, int64_t& local) {
@@ -49,13 +56,28 @@ __device__ __forceinline__ bool locate(const InvLaunch& L, int kind, int64_t til
     return false;
 }
 
-// S[m][k] <- G block (64 x 64, leading dimension ld); `trans` stores G^T.
-// Global reads run along G's rows (coalesced) in both cases.
-__device__ __forceinline__ void load_block(double* S, const double* G, int64_t ld, bool trans) {
-    for (int e = threadIdx.x; e < BB; e += NT) {
-        const int r = e >> 6, c = e & 63;
-        const double v = G[(int64_t)r * ld + c];
-        if (trans) S[c * LD + r] = v; else S[r * LD + c] = v;
+// A 64 x 64 block in global memory; `trans` stages it transposed in LDS.
+struct Blk {
+    const double* p;
+    int64_t ld;
+    bool trans;
+};
+
+// Thread t handles elements e = t + s*NT: row e/64, column e%64, so each
+// wave reads whole 512-byte rows.
+__device__ __forceinline__ void fetch(double (&v)[PER], const Blk& b) {
+    const int r0 = threadIdx.x >> 6, c = threadIdx.x & 63;
+#pragma unroll
+    for (int s = 0; s < PER; ++s) v[s] = b.p[(int64_t)(r0 + 4 * s) * b.ld + c];
+}
+__device__ __forceinline__ void put(double* S, const double (&v)[PER], bool trans) {
+    const int r0 = threadIdx.x >> 6, c = threadIdx.x & 63;
+    if (trans) {
+#pragma unroll
+        for (int s = 0; s < PER; ++s) S[c * LD + r0 + 4 * s] = v[s];
+    } else {
+#pragma unroll
+        for (int s = 0; s < PER; ++s) S[(r0 + 4 * s) * LD + c] = v[s];
     }
 }
 
@@ -69,7 +91,7 @@ __device__ __forceinline__ void mma_block(doublex4 (&acc)[2][2], const double* A
     const double* a1p = a0p + 16 * LD;
     const double* b0p = Bs + (wc * 32 + li) * LD + lk;
     const double* b1p = b0p + 16 * LD;
-#pragma unroll 4
+#pragma unroll
     for (int k0 = 0; k0 < B; k0 += 4) {
         double a0 = a0p[k0], a1 = a1p[k0];
         const double b0 = b0p[k0], b1 = b1p[k0];
@@ -78,6 +100,31 @@ __device__ __forceinline__ void mma_block(doublex4 (&acc)[2][2], const double* A
         acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, acc[0][1], 0, 0, 0);
         acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, acc[1][0], 0, 0, 0);
         acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, acc[1][1], 0, 0, 0);
+    }
+}
+
+// acc += sum_{t in [t0, t1)} A_t B_t^T (in the LDS convention of mma_block),
+// with the blocks of step t given by srcA(t), srcB(t).  `same` reuses the A
+// block for B.  Loads of step t+1 are in flight during the products of step t.
+template <typename FA, typename FB>
+__device__ __forceinline__ void block_gemm(doublex4 (&acc)[2][2], double* As, double* Bs, int t0, int t1,
+                                           FA srcA, FB srcB, bool neg, bool same) {
+    if (t0 >= t1) return;
+    double ra[PER], rb[PER];
+    fetch(ra, srcA(t0));
+    if (!same) fetch(rb, srcB(t0));
+    for (int t = t0; t < t1; ++t) {
+        const bool ta = srcA(t).trans;
+        const bool tb = same ? ta : srcB(t).trans;
+        __syncthreads();
+        put(As, ra, ta);
+        if (!same) put(Bs, rb, tb);
+        __syncthreads();
+        if (t + 1 < t1) {
+            fetch(ra, srcA(t + 1));
+            if (!same) fetch(rb, srcB(t + 1));
+        }
+        mma_block(acc, As, same ? As : Bs, neg);
     }
 }
 
@@ -110,65 +157,114 @@ __device__ __forceinline__ void acc_to_lds(const doublex4 (&acc)[2][2], double* 
     for_acc([&](int a, int b, int r, int row, int col) { S[row * LD + col] = acc[a][b][r]; });
 }
 
-// In-place Cholesky P = U^T U of a 64 x 64 block in LDS (upper triangle
-// read and written).  Returns 0, or the 1-based column of the first pivot
-// that is not positive or not finite.  Caller synchronises before the call.
-__device__ int panel_cholesky(double* P) {
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+    const long long b = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_readlane((int)(b & 0xffffffffll), lane);
+    const int hi = __builtin_amdgcn_readlane((int)(b >> 32), lane);
+    return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+// LDS scratch of factor_diagonal: two published rows, the reciprocals of the
+// diagonal, and one failure slot per wave.
+struct PanelScratch {
+    double row[2][B];
+    double rdiag[B];
+    int fail[NT / 64];
+};
+
+constexpr int RS = B / 4;   // rows of the diagonal block per wave
+
+// Cholesky P = U^T U and V = U^-1 of the 64 x 64 diagonal block in LDS
+// (upper triangle of P read; U written back with zeros below the diagonal,
+// V into Q).  Wave w keeps rows 16w..16w+15 of every column in registers
+// (lane j owns column j).  Right-looking: at step c the wave that owns row c
+// takes the pivot from lane c, scales the row and publishes it through LDS
+// (two alternating rows); after one barrier every wave subtracts the
+// rank-one update from its rows below c.  The steps run as 4 rolled rounds
+// of 16 unrolled steps, so register slots are compile-time constants while
+// the code stays small.  V solves U V = I from the bottom row up with the
+// same layout: row k is divided by U_kk, published, and eliminated from the
+// rows above.  Returns the 1-based column of the first pivot that is not
+// positive or not finite, or 0 (in every thread).
+__device__ int factor_diagonal(double* P, double* Q, PanelScratch& S) {
+    const int w = threadIdx.x >> 6, j = threadIdx.x & 63;
+    double a[RS];
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < RS; ++s) a[s] = P[(RS * w + s) * LD + j];
     int failed = 0;
-    for (int c = 0; c < B; ++c) {
-        const double piv = P[c * LD + c];
-        if (failed == 0 && (!(piv > 0.0) || !isfinite(piv))) failed = c + 1;
-        const double r = sqrt(piv);
-        __syncthreads();  // every thread has read the pivot
-        for (int j = c + (int)threadIdx.x; j < B; j += NT) P[c * LD + j] = (j == c) ? r : P[c * LD + j] / r;
-        __syncthreads();
-        const int m = B - 1 - c;
-        for (int e = threadIdx.x; e < m * m; e += NT) {
-            const int i = c + 1 + e / m, j = c + 1 + e % m;
-            if (j >= i) P[i * LD + j] -= P[c * LD + i] * P[c * LD + j];
+#pragma unroll 1
+    for (int wb = 0; wb < 4; ++wb) {
+#pragma unroll
+        for (int s = 0; s < RS; ++s) {
+            const int c = RS * wb + s;
+            double* Rc = S.row[s & 1];
+            if (w == wb) {
+                const double piv = readlane_f64(a[s], c);
+                failed = (failed == 0 && !(piv > 0.0 && piv <= DBL_MAX)) ? c + 1 : failed;
+                const double sq = sqrt(piv);
+                a[s] = (j == c) ? sq : a[s] / sq;
+                Rc[j] = a[s];
+            }
+            __syncthreads();
+            const double uj = Rc[j];
+            if (w == wb) {
+#pragma unroll
+                for (int t = s + 1; t < RS; ++t) a[t] = fma(-Rc[RS * w + t], uj, a[t]);
+            } else if (w > wb) {
+#pragma unroll
+                for (int t = 0; t < RS; ++t) a[t] = fma(-Rc[RS * w + t], uj, a[t]);
+            }
         }
-        __syncthreads();
     }
-    return failed;
-}
-
-// V = U^-1 for the upper-triangular 64 x 64 block U in LDS (V upper, zero
-// below the diagonal).  Column j is solved backwards by the four threads
-// 4j .. 4j+3, which split each inner product and combine it with shuffles;
-// all four write the same value, so each reads back only its own writes.
-__device__ void triangle_inverse(const double* U, double* V) {
-    const int j = threadIdx.x >> 2, p = threadIdx.x & 3;
-    for (int i = j + 1 + p; i < B; i += 4) V[i * LD + j] = 0.0;
-    V[j * LD + j] = 1.0 / U[j * LD + j];
-    for (int i = j - 1; i >= 0; --i) {
-        double s = 0.0;
-        for (int t = i + 1 + p; t <= j; t += 4) s += U[i * LD + t] * V[t * LD + j];
-        s += __shfl_xor(s, 1);
-        s += __shfl_xor(s, 2);
-        V[i * LD + j] = -s / U[i * LD + i];
+    if (j == 0) S.fail[w] = failed;
+#pragma unroll
+    for (int s = 0; s < RS; ++s) {
+        const int i = RS * w + s;
+        P[i * LD + j] = (j >= i) ? a[s] : 0.0;
+        a[s] = (i == j) ? 1.0 : 0.0;
     }
     __syncthreads();
-}
-
-// Factor the diagonal block held in P (LDS), invert its triangle into Q,
-// store U (zero below the diagonal) into W's block and U^-1 into dinv.
-// Returns the 1-based failing column inside the block, or 0.
-__device__ int factor_diagonal_block(double* P, double* Q, double* Wkk, int64_t D, double* dinv_k) {
+    if (threadIdx.x < B) S.rdiag[threadIdx.x] = 1.0 / P[threadIdx.x * LD + threadIdx.x];
     __syncthreads();
-    const int f = panel_cholesky(P);
-    triangle_inverse(P, Q);
-    for (int e = threadIdx.x; e < BB; e += NT) {
-        const int r = e >> 6, c = e & 63;
-        Wkk[(int64_t)r * D + c] = (c >= r) ? P[r * LD + c] : 0.0;
-        dinv_k[e] = Q[r * LD + c];
+#pragma unroll 1
+    for (int wb = 3; wb >= 0; --wb) {
+#pragma unroll
+        for (int s = RS - 1; s >= 0; --s) {
+            const int k = RS * wb + s;
+            double* Rk = S.row[s & 1];
+            if (w == wb) {
+                a[s] *= S.rdiag[k];
+                Rk[j] = a[s];
+            }
+            __syncthreads();
+            const double vj = Rk[j];
+            if (w == wb) {
+#pragma unroll
+                for (int t = 0; t < s; ++t) a[t] = fma(-P[(RS * w + t) * LD + k], vj, a[t]);
+            } else if (w < wb) {
+#pragma unroll
+                for (int t = 0; t < RS; ++t) a[t] = fma(-P[(RS * w + t) * LD + k], vj, a[t]);
+            }
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < RS; ++s) Q[(RS * w + s) * LD + j] = a[s];
+    __syncthreads();
+    // pivots are visited in order, so the first failure is the smallest code
+    int f = 0;
+#pragma unroll
+    for (int q = 0; q < NT / 64; ++q) {
+        const int v = S.fail[q];
+        f = (v != 0 && (f == 0 || v < f)) ? v : f;
     }
     return f;
 }
 
-__device__ __forceinline__ void record_info(const InvMat& M, int k, int f, bool first_panel) {
+__device__ __forceinline__ void record_info(const InvMat& M, int k, int f) {
     if (threadIdx.x != 0) return;
-    if (first_panel) {
-        *M.info = f ? f : 0;
+    if (k == 0) {
+        *M.info = f;
     } else if (f && *M.info == 0) {
         *M.info = k * B + f;
     }
@@ -176,9 +272,8 @@ __device__ __forceinline__ void record_info(const InvMat& M, int k, int f, bool 
 
 // -------------------------------------------------------------- kernels --
 
+// W = sym(X) + gamma I on the upper blocks, identity in the padding.
 __global__ __launch_bounds__(NT) void inv_prepare_kernel(InvLaunch L, int64_t tiles) {
-    __shared__ double P[B * LD];
-    __shared__ double Q[B * LD];
     int mi;
     int64_t local;
     if (!locate(L, kInvPrepare, blockIdx.x, mi, local)) return;
@@ -186,45 +281,84 @@ __global__ __launch_bounds__(NT) void inv_prepare_kernel(InvLaunch L, int64_t ti
     int bi, bj;
     upper_decode(local, M.nb, bi, bj);
     const int64_t D = (int64_t)M.nb * B, d = M.d;
-    const bool first = (bi == 0 && bj == 0);
-    for (int e = threadIdx.x; e < BB; e += NT) {
-        const int r = e >> 6, c = e & 63;
-        const int64_t i = (int64_t)bi * B + r, j = (int64_t)bj * B + c;
+    const int r0 = threadIdx.x >> 6, c = threadIdx.x & 63;
+    float xv[PER];
+#pragma unroll
+    for (int s = 0; s < PER; ++s) {
+        const int64_t i = (int64_t)bi * B + r0 + 4 * s, j = (int64_t)bj * B + c;
+        xv[s] = (i < d && j < d && j >= i) ? M.x[i * d + j] : 0.0f;
+    }
+#pragma unroll
+    for (int s = 0; s < PER; ++s) {
+        const int64_t i = (int64_t)bi * B + r0 + 4 * s, j = (int64_t)bj * B + c;
         double v;
         if (i < d && j < d) {
-            v = (j >= i) ? (double)M.x[i * d + j] : 0.0;
+            v = (double)xv[s];
             if (i == j) v += L.gamma;
         } else {
             v = (i == j) ? 1.0 : 0.0;  // identity padding
         }
-        if (first) P[r * LD + c] = v; else M.w[i * D + j] = v;
-    }
-    if (first) {
-        const int f = factor_diagonal_block(P, Q, M.w, D, M.dinv);
-        record_info(M, 0, f, true);
+        M.w[i * D + j] = v;
     }
 }
 
-__global__ __launch_bounds__(NT) void inv_trsm_kernel(InvLaunch L, int64_t tiles) {
+// Step k of potrf, first half: every workgroup factors the diagonal block
+// (k, k) (already updated by the previous steps) and, when the matrix has
+// blocks to the right, solves one of them: U_kj = U_kk^-T W_kj.  The
+// workgroup of the first such block (or the only one) stores U_kk^-1 and the
+// failure code.
+__global__ __launch_bounds__(NT) void inv_panel_trsm_kernel(InvLaunch L, int64_t tiles) {
     __shared__ double As[B * LD];
     __shared__ double Bs[B * LD];
+    __shared__ PanelScratch R;
     int mi;
     int64_t local;
-    if (!locate(L, kInvTrsm, blockIdx.x, mi, local)) return;
+    if (!locate(L, kInvPanel, blockIdx.x, mi, local)) return;
     const InvMat M = L.mats[mi];
     const int k = L.step;
-    const int J = k + 1 + (int)local;
     const int64_t D = (int64_t)M.nb * B;
-    double* Wkj = M.w + (int64_t)k * B * D + (int64_t)J * B;
-    load_block(As, M.dinv + (int64_t)k * BB, B, true);   // A[r][t] = Uinv_kk[t][r]
-    load_block(Bs, Wkj, D, true);                        // B[c][t] = W_kj[t][c]
+    double* Wkk = M.w + (int64_t)k * B * D + (int64_t)k * B;
+    const bool has_right = k + 1 < M.nb;
+    const int J = k + 1 + (int)local;
+    double rb[PER];
+    if (has_right) fetch(rb, Blk{M.w + (int64_t)k * B * D + (int64_t)J * B, D, false});
+    {
+        double ra[PER];
+        fetch(ra, Blk{Wkk, D, false});
+        put(As, ra, false);
+    }
+    const int f = factor_diagonal(As, Bs, R);   // As: U_kk, Bs: U_kk^-1
+    // W_kk itself is left as it is: other workgroups of this launch read it,
+    // and no later step reads a diagonal block of W (they use dinv).
+    if (local == 0) {
+        const int r0 = threadIdx.x >> 6, c = threadIdx.x & 63;
+#pragma unroll
+        for (int s = 0; s < PER; ++s) {
+            const int r = r0 + 4 * s;
+            M.dinv[(int64_t)k * BB + r * B + c] = Bs[r * LD + c];
+        }
+        record_info(M, k, f);
+    }
+    if (!has_right) return;
+    // A[r][t] = Uinv_kk[t][r]: stage U_kk^-1 transposed over As, W_kj transposed in Bs
+    __syncthreads();
+    {
+        const int r0 = threadIdx.x >> 6, c = threadIdx.x & 63;
+        double q[PER];
+#pragma unroll
+        for (int s = 0; s < PER; ++s) q[s] = Bs[(r0 + 4 * s) * LD + c];
+        __syncthreads();
+        put(As, q, true);
+        put(Bs, rb, true);
+    }
     __syncthreads();
     doublex4 acc[2][2];
     acc_zero(acc);
     mma_block(acc, As, Bs, false);
-    acc_store(acc, Wkj, D);
+    acc_store(acc, M.w + (int64_t)k * B * D + (int64_t)J * B, D);
 }
 
+// Step k of potrf, second half: trailing update W_ij -= U_ki^T U_kj.
 __global__ __launch_bounds__(NT) void inv_syrk_kernel(InvLaunch L, int64_t tiles) {
     __shared__ double As[B * LD];
     __shared__ double Bs[B * LD];
@@ -242,18 +376,11 @@ __global__ __launch_bounds__(NT) void inv_syrk_kernel(InvLaunch L, int64_t tiles
     const double* rowk = M.w + (int64_t)k * B * D;
     doublex4 acc[2][2];
     acc_load(acc, Wij, D);
-    load_block(As, rowk + (int64_t)I * B, D, true);      // A[r][t] = U_ki[t][r]
-    if (I != J) load_block(Bs, rowk + (int64_t)J * B, D, true);
-    __syncthreads();
-    mma_block(acc, As, (I == J) ? As : Bs, true);
-    if (I == k + 1 && J == k + 1) {
-        __syncthreads();
-        acc_to_lds(acc, As);
-        const int f = factor_diagonal_block(As, Bs, Wij, D, M.dinv + (int64_t)I * BB);
-        record_info(M, I, f, false);
-    } else {
-        acc_store(acc, Wij, D);
-    }
+    // A[r][t] = U_ki[t][r], B[c][t] = U_kj[t][c]
+    block_gemm(acc, As, Bs, 0, 1,
+               [&](int) { return Blk{rowk + (int64_t)I * B, D, true}; },
+               [&](int) { return Blk{rowk + (int64_t)J * B, D, true}; }, true, I == J);
+    acc_store(acc, Wij, D);
 }
 
 // Tile of level `lvl` of the doubling: group m joins G1 = [m*2h, m*2h + h)
@@ -294,14 +421,13 @@ __global__ __launch_bounds__(NT) void inv_trtri_a_kernel(InvLaunch L, int64_t ti
     const int64_t D = (int64_t)M.nb * B;
     doublex4 acc[2][2];
     acc_zero(acc);
-    for (int t = g1_end; t <= J; ++t) {
-        __syncthreads();
-        load_block(As, M.w + (int64_t)I * B * D + (int64_t)t * B, D, false);          // U_It
-        if (t == J) load_block(Bs, M.dinv + (int64_t)J * BB, B, true);                // V_JJ
-        else load_block(Bs, M.w + (int64_t)t * B * D + (int64_t)J * B, D, true);     // V_tJ
-        __syncthreads();
-        mma_block(acc, As, Bs, false);
-    }
+    block_gemm(acc, As, Bs, g1_end, J + 1,
+               [&](int t) { return Blk{M.w + (int64_t)I * B * D + (int64_t)t * B, D, false}; },   // U_It
+               [&](int t) {                                                                     // V_tJ
+                   return t == J ? Blk{M.dinv + (int64_t)J * BB, B, true}
+                                 : Blk{M.w + (int64_t)t * B * D + (int64_t)J * B, D, true};
+               },
+               false, false);
     acc_store(acc, M.w + (int64_t)J * B * D + (int64_t)I * B, D);
 }
 
@@ -318,14 +444,13 @@ __global__ __launch_bounds__(NT) void inv_trtri_b_kernel(InvLaunch L, int64_t ti
     const int64_t D = (int64_t)M.nb * B;
     doublex4 acc[2][2];
     acc_zero(acc);
-    for (int t = I; t < g1_end; ++t) {
-        __syncthreads();
-        if (t == I) load_block(As, M.dinv + (int64_t)I * BB, B, false);               // V_II
-        else load_block(As, M.w + (int64_t)I * B * D + (int64_t)t * B, D, false);     // V_It
-        load_block(Bs, M.w + (int64_t)J * B * D + (int64_t)t * B, D, true);           // T_tJ (parked at (J, t))
-        __syncthreads();
-        mma_block(acc, As, Bs, true);
-    }
+    block_gemm(acc, As, Bs, I, g1_end,
+               [&](int t) {                                                                     // V_It
+                   return t == I ? Blk{M.dinv + (int64_t)I * BB, B, false}
+                                 : Blk{M.w + (int64_t)I * B * D + (int64_t)t * B, D, false};
+               },
+               [&](int t) { return Blk{M.w + (int64_t)J * B * D + (int64_t)t * B, D, true}; },   // T_tJ at (J, t)
+               true, false);
     acc_store(acc, M.w + (int64_t)I * B * D + (int64_t)J * B, D);
 }
 
@@ -342,23 +467,20 @@ __global__ __launch_bounds__(NT) void inv_lauum_kernel(InvLaunch L, int64_t tile
     const int64_t D = (int64_t)M.nb * B, d = M.d;
     doublex4 acc[2][2];
     acc_zero(acc);
-    for (int t = J; t < M.nb; ++t) {
-        __syncthreads();
-        if (t == I) load_block(As, M.dinv + (int64_t)I * BB, B, false);
-        else load_block(As, M.w + (int64_t)I * B * D + (int64_t)t * B, D, false);
-        if (I != J) {
-            if (t == J) load_block(Bs, M.dinv + (int64_t)J * BB, B, false);
-            else load_block(Bs, M.w + (int64_t)J * B * D + (int64_t)t * B, D, false);
-        }
-        __syncthreads();
-        mma_block(acc, As, (I == J) ? As : Bs, false);
-    }
+    auto V = [&](int row, int t) {
+        return t == row ? Blk{M.dinv + (int64_t)row * BB, B, false}
+                        : Blk{M.w + (int64_t)row * B * D + (int64_t)t * B, D, false};
+    };
+    block_gemm(acc, As, Bs, J, M.nb, [&](int t) { return V(I, t); }, [&](int t) { return V(J, t); }, false,
+               I == J);
     __syncthreads();
     acc_to_lds(acc, As);
     __syncthreads();
     const int64_t r0 = (int64_t)I * B, c0 = (int64_t)J * B;
-    for (int e = threadIdx.x; e < BB; e += NT) {
-        const int r = e >> 6, c = e & 63;
+    const int q0 = threadIdx.x >> 6, l = threadIdx.x & 63;
+#pragma unroll
+    for (int s = 0; s < PER; ++s) {
+        const int r = q0 + 4 * s, c = l;
         const int64_t i = r0 + r, j = c0 + c;
         if (i < d && j < d) {
             const double v = (I != J || c >= r) ? As[r * LD + c] : As[c * LD + r];
@@ -366,8 +488,9 @@ __global__ __launch_bounds__(NT) void inv_lauum_kernel(InvLaunch L, int64_t tile
         }
     }
     if (I != J) {
-        for (int e = threadIdx.x; e < BB; e += NT) {
-            const int c = e >> 6, r = e & 63;     // destination row c0+c, column r0+r
+#pragma unroll
+        for (int s = 0; s < PER; ++s) {
+            const int c = q0 + 4 * s, r = l;      // destination row c0+c, column r0+r
             const int64_t i = c0 + c, j = r0 + r;
             if (i < d && j < d) M.z[i * d + j] = (float)As[r * LD + c];
         }
@@ -384,7 +507,7 @@ hipError_t launch(K kernel, const InvLaunch& L, int64_t tiles, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_inv_prepare(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_prepare_kernel, L, t, s); }
-hipError_t launch_inv_trsm(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_trsm_kernel, L, t, s); }
+hipError_t launch_inv_panel_trsm(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_panel_trsm_kernel, L, t, s); }
 hipError_t launch_inv_syrk(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_syrk_kernel, L, t, s); }
 hipError_t launch_inv_trtri_a(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_trtri_a_kernel, L, t, s); }
 hipError_t launch_inv_trtri_b(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_trtri_b_kernel, L, t, s); }

@@ -319,10 +319,10 @@ kfac_status_t kfac_damped_inverse(int n, const float* const* x, const int64_t* d
 
     InvLaunch L{mats_dev, buckets_dev, (int32_t)p.buckets.size(), 0, (double)gamma};
     e = launch_inv_prepare(L, bucket_tiles(p, kInvPrepare, 0), stream);
-    for (int k = 0; e == hipSuccess && k + 1 < p.nbmax; ++k) {
+    for (int k = 0; e == hipSuccess && k < p.nbmax; ++k) {
         L.step = k;
-        e = launch_inv_trsm(L, bucket_tiles(p, kInvTrsm, k), stream);
-        if (e == hipSuccess) e = launch_inv_syrk(L, bucket_tiles(p, kInvSyrk, k), stream);
+        e = launch_inv_panel_trsm(L, bucket_tiles(p, kInvPanel, k), stream);
+        if (e == hipSuccess && k + 1 < p.nbmax) e = launch_inv_syrk(L, bucket_tiles(p, kInvSyrk, k), stream);
     }
     for (int lvl = 1; e == hipSuccess && (1 << (lvl - 1)) < p.nbmax; ++lvl) {
         L.step = lvl;

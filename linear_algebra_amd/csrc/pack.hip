@@ -96,24 +96,32 @@ __global__ __launch_bounds__(PT) void unpack_kernel(const PackLayer* __restrict_
     const int64_t r0 = (int64_t)ti * UT, c0 = (int64_t)tj * UT;
     const float* src = packed + L.off;
 
-    // stage the tile's upper entries (i <= j) from the fused buffer
-    for (int e = threadIdx.x; e < UT * UT; e += PT) {
-        const int r = e / UT, c = e % UT;
-        const int64_t i = r0 + r, j = c0 + c;
-        if (i < d && j < d && j >= i) S[r][c] = src[row_start(i, d) + (j - i)];
+    // stage the tile's upper entries (i <= j) from the fused buffer: thread
+    // t handles rows t/64 + 4s, column t%64, all loads in flight together
+    constexpr int PERT = UT * UT / PT;
+    const int q0 = threadIdx.x / UT, l = threadIdx.x % UT;
+    float v[PERT];
+#pragma unroll
+    for (int s = 0; s < PERT; ++s) {
+        const int64_t i = r0 + q0 + 4 * s, j = c0 + l;
+        v[s] = (i < d && j < d && j >= i) ? src[row_start(i, d) + (j - i)] : 0.0f;
     }
+#pragma unroll
+    for (int s = 0; s < PERT; ++s) S[q0 + 4 * s][l] = v[s];
     __syncthreads();
 
     // the tile itself: on diagonal tiles the lower half is the mirror
-    for (int e = threadIdx.x; e < UT * UT; e += PT) {
-        const int r = e / UT, c = e % UT;
+#pragma unroll
+    for (int s = 0; s < PERT; ++s) {
+        const int r = q0 + 4 * s, c = l;
         const int64_t i = r0 + r, j = c0 + c;
         if (i < d && j < d) L.m[i * d + j] = (j >= i) ? S[r][c] : S[c][r];
     }
     // the mirrored tile below the diagonal, written row by row
     if (ti != tj) {
-        for (int e = threadIdx.x; e < UT * UT; e += PT) {
-            const int c = e / UT, r = e % UT;   // destination row c0+c, column r0+r
+#pragma unroll
+        for (int s = 0; s < PERT; ++s) {
+            const int c = q0 + 4 * s, r = l;   // destination row c0+c, column r0+r
             const int64_t i = c0 + c, j = r0 + r;
             if (i < d && j < d) L.m[i * d + j] = S[r][c];
         }
