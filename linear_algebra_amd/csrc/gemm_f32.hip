@@ -12,6 +12,12 @@
 // float32 over sub-chunks of kGemmSubK rows and then folded into a second
 // float32 sum, which keeps the rounding error of long reductions (hundreds of
 // thousands of rows) near that of a 512-term sum.
+//
+// Operands are read with buffer loads whose descriptor covers one K-slab:
+// rows past the end of the input read as zero without a branch, and the
+// per-thread offsets inside a slab are computed once.  LDS holds each slab
+// as [m][k] with k contiguous, so a lane fetches its eight k-values of a
+// block with two 128-bit reads and the slab's 32 MFMAs issue back to back.
 #include "device_common.h"
 #include "internal.h"
 
@@ -56,10 +62,35 @@ __device__ __forceinline__ void store_elem(const GemmProb& P, int i, int j, floa
     }
 }
 
+constexpr int LDK = BK + 4;        // LDS row stride (floats): [m][k], k contiguous
+constexpr uint32_t kOOB = 0x80000000u;  // buffer offset past any slab: loads return 0
+constexpr int RED_SLICES = 16;     // workgroups per partial tile in the reduce
+
+// Buffer resource over rows [k0, min(k0 + BK, k_end)) of a row-major
+// operand; rows past the end of the slab read as zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const void* base, int64_t ld, int k0, int k_end, int esz) {
+    const char* p = static_cast<const char*>(base) + (int64_t)k0 * ld * esz;
+    const int rows = max(0, min(BK, k_end - k0));
+    // every operand is uniform; readfirstlane keeps the descriptor in
+    // scalar registers (a per-lane descriptor would need a waterfall loop)
+    const int bytes = __builtin_amdgcn_readfirstlane(rows * (int)ld * esz);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p), (short)0, bytes, 0x00020000);
+}
+
+template <bool BF16>
+__device__ __forceinline__ float slab_load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    if constexpr (BF16) {
+        return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
+    } else {
+        // the builtin returns the 32 bits as an integer: reinterpret, do not convert
+        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+    }
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(NT, 2) void gemm_tn_kernel(GemmLaunch L, int64_t items) {
-    __shared__ float As[2][BK][BM];
-    __shared__ float Bs[2][BK][BM];
+    __shared__ __attribute__((aligned(16))) float As[2][BM * LDK];
+    __shared__ __attribute__((aligned(16))) float Bs[2][BM * LDK];
 
     const int64_t item = xcd_remap(blockIdx.x, gridDim.x);
     if (item >= items) return;
@@ -80,6 +111,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_tn_kernel(GemmLaunch L, int64_t it
     const int k_end = min(P.K, k_begin + P.kchunk);
     // Factor tiles on the diagonal read the same columns for both operands.
     const bool same = (P.a == P.b) && (m0 == n0);
+    constexpr int esz = BF16 ? 2 : 4;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -88,24 +120,37 @@ __global__ __launch_bounds__(NT, 2) void gemm_tn_kernel(GemmLaunch L, int64_t it
     // the wave below the diagonal of a diagonal factor tile has nothing to compute
     const bool active = !(P.mode == kModeFactor && ti == tj && wm > wn);
 
-    const int lc = tid & (BM - 1);  // column loaded by this thread
-    const int lr = tid >> 7;        // first slab row loaded by this thread (0 or 1)
+    // Thread t loads column lc of the tile, slab rows lr8 .. lr8+7; the byte
+    // offsets inside a slab are the same for every slab.
+    const int lc = tid & (BM - 1);
+    const int lr8 = (tid >> 7) * LOADS;
+    uint32_t offa[LOADS], offb[LOADS];
+#pragma unroll
+    for (int s = 0; s < LOADS; ++s) {
+        const int row = lr8 + s;
+        offa[s] = (m0 + lc < P.M) ? (uint32_t)((row * P.lda + m0 + lc) * esz) : kOOB;
+        offb[s] = (n0 + lc < P.N) ? (uint32_t)((row * P.ldb + n0 + lc) * esz) : kOOB;
+    }
 
     float ra[LOADS], rb[LOADS];
     auto gload = [&](int k0) {
+        const __amdgpu_buffer_rsrc_t rA = slab_rsrc(P.a, P.lda, k0, k_end, esz);
 #pragma unroll
-        for (int s = 0; s < LOADS; ++s) {
-            const int row = k0 + lr + 2 * s;
-            const bool rok = row < k_end;
-            ra[s] = (rok && m0 + lc < P.M) ? load_op<BF16>(P.a, (int64_t)row * P.lda + m0 + lc) : 0.0f;
-            if (!same) rb[s] = (rok && n0 + lc < P.N) ? load_op<BF16>(P.b, (int64_t)row * P.ldb + n0 + lc) : 0.0f;
+        for (int s = 0; s < LOADS; ++s) ra[s] = slab_load<BF16>(rA, offa[s]);
+        if (!same) {
+            const __amdgpu_buffer_rsrc_t rB = slab_rsrc(P.b, P.ldb, k0, k_end, esz);
+#pragma unroll
+            for (int s = 0; s < LOADS; ++s) rb[s] = slab_load<BF16>(rB, offb[s]);
         }
     };
     auto sstore = [&](int buf) {
-#pragma unroll
-        for (int s = 0; s < LOADS; ++s) {
-            As[buf][lr + 2 * s][lc] = ra[s];
-            if (!same) Bs[buf][lr + 2 * s][lc] = rb[s];
+        float4* da = reinterpret_cast<float4*>(&As[buf][lc * LDK + lr8]);
+        da[0] = make_float4(ra[0], ra[1], ra[2], ra[3]);
+        da[1] = make_float4(ra[4], ra[5], ra[6], ra[7]);
+        if (!same) {
+            float4* db = reinterpret_cast<float4*>(&Bs[buf][lc * LDK + lr8]);
+            db[0] = make_float4(rb[0], rb[1], rb[2], rb[3]);
+            db[1] = make_float4(rb[4], rb[5], rb[6], rb[7]);
         }
     };
 
@@ -124,22 +169,32 @@ __global__ __launch_bounds__(NT, 2) void gemm_tn_kernel(GemmLaunch L, int64_t it
     }
     __syncthreads();
 
-    const int col_a = wm * 64 + (lane & 31);
-    const int col_b = wn * 64 + (lane & 31);
-    const int khalf = lane >> 5;
+    // MFMA fragments: lane l supplies rows/columns (l % 32) of its 32-wide
+    // blocks and, over the 8 steps s of a slab, the slab rows 8*(l/32) + s
+    // (the sum over the slab does not depend on how its rows are paired).
+    const int fr = lane & 31;
+    const int fk = (lane >> 5) * 8;
 
     for (int st = 0; st < nstages; ++st) {
         const int buf = st & 1;
         if (st + 1 < nstages) gload(k_begin + (st + 1) * BK);
         if (active) {
-            const float(*Bsrc)[BM] = same ? As[buf] : Bs[buf];
+            const float* Ab = As[buf];
+            const float* Bb = same ? As[buf] : Bs[buf];
+            float4 fa[2][2], fb[2][2];
 #pragma unroll
-            for (int ks = 0; ks < BK; ks += 2) {
-                const int kk = ks + khalf;
-                const float a0 = As[buf][kk][col_a];
-                const float a1 = As[buf][kk][col_a + 32];
-                const float b0 = Bsrc[kk][col_b];
-                const float b1 = Bsrc[kk][col_b + 32];
+            for (int a = 0; a < 2; ++a) {
+                const float4* pa = reinterpret_cast<const float4*>(&Ab[(wm * 64 + a * 32 + fr) * LDK + fk]);
+                fa[a][0] = pa[0];
+                fa[a][1] = pa[1];
+                const float4* pb = reinterpret_cast<const float4*>(&Bb[(wn * 64 + a * 32 + fr) * LDK + fk]);
+                fb[a][0] = pb[0];
+                fb[a][1] = pb[1];
+            }
+#pragma unroll
+            for (int s = 0; s < BK / 2; ++s) {
+                const float a0 = fa[0][s >> 2][s & 3], a1 = fa[1][s >> 2][s & 3];
+                const float b0 = fb[0][s >> 2][s & 3], b1 = fb[1][s >> 2][s & 3];
                 acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
                 acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
                 acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
@@ -162,6 +217,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_tn_kernel(GemmLaunch L, int64_t it
 
     // Output layout of a 32 x 32 MFMA block: lane l holds column (l % 32);
     // register r holds row 8*(r/4) + 4*(l/32) + (r%4).
+    const int khalf = lane >> 5;
     const int ksplit = P.ksplit;
     float* part = (ksplit > 1) ? P.part + ((int64_t)kc * P.ntiles + t) * (BM * BM) : nullptr;
 #pragma unroll
@@ -181,9 +237,13 @@ __global__ __launch_bounds__(NT, 2) void gemm_tn_kernel(GemmLaunch L, int64_t it
 }
 
 // Sums the split-K partial tiles in chunk order and applies the epilogue.
-__global__ __launch_bounds__(NT) void gemm_reduce_kernel(GemmLaunch L, int64_t tiles) {
-    const int64_t tile = blockIdx.x;
-    if (tile >= tiles) return;
+// Each partial tile is spread over RED_SLICES workgroups; thread t sums
+// four consecutive elements, with the loads of four chunks in flight.
+__global__ __launch_bounds__(NT) void gemm_reduce_kernel(GemmLaunch L, int64_t slices) {
+    const int64_t g = blockIdx.x;
+    if (g >= slices) return;
+    const int64_t tile = g / RED_SLICES;
+    const int slice = (int)(g % RED_SLICES);
     const GemmProb P = L.probs[find_prob(L.probs, L.nprob, tile, true)];
     const int t = (int)(tile - P.red_begin);
     int ti, tj;
@@ -193,24 +253,28 @@ __global__ __launch_bounds__(NT) void gemm_reduce_kernel(GemmLaunch L, int64_t t
         ti = t / P.tiles_n;
         tj = t % P.tiles_n;
     }
-    // thread t sums elements t + s*NT of the tile over the K chunks in
-    // chunk order; the PERR loads of one chunk are in flight together
-    constexpr int PERR = BM * BM / NT;
-    const int64_t stride = (int64_t)P.ntiles * (BM * BM);
-    const float* base = P.part + (int64_t)t * (BM * BM);
-    float s[PERR];
-#pragma unroll
-    for (int q = 0; q < PERR; ++q) s[q] = 0.0f;
-    for (int k = 0; k < P.ksplit; ++k) {
-        const float* pk = base + k * stride;
-#pragma unroll
-        for (int q = 0; q < PERR; ++q) s[q] += pk[threadIdx.x + q * NT];
+    const int e0 = slice * (BM * BM / RED_SLICES) + threadIdx.x * 4;
+    const int64_t stride4 = (int64_t)P.ntiles * (BM * BM) / 4;
+    const float4* base = reinterpret_cast<const float4*>(P.part + (int64_t)t * (BM * BM) + e0);
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    int k = 0;
+    for (; k + 4 <= P.ksplit; k += 4) {
+        const float4 v0 = base[(k + 0) * stride4], v1 = base[(k + 1) * stride4];
+        const float4 v2 = base[(k + 2) * stride4], v3 = base[(k + 3) * stride4];
+        s.x += v0.x; s.y += v0.y; s.z += v0.z; s.w += v0.w;
+        s.x += v1.x; s.y += v1.y; s.z += v1.z; s.w += v1.w;
+        s.x += v2.x; s.y += v2.y; s.z += v2.z; s.w += v2.w;
+        s.x += v3.x; s.y += v3.y; s.z += v3.z; s.w += v3.w;
     }
+    for (; k < P.ksplit; ++k) {
+        const float4 v = base[k * stride4];
+        s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+    const float sv[4] = {s.x, s.y, s.z, s.w};
 #pragma unroll
-    for (int q = 0; q < PERR; ++q) {
-        const int e = threadIdx.x + q * NT;
-        const int row = e / BM, col = e % BM;
-        store_elem(P, ti * BM + row, tj * BM + col, s[q], L.eps, L.first_step);
+    for (int q = 0; q < 4; ++q) {
+        const int e = e0 + q;
+        store_elem(P, ti * BM + e / BM, tj * BM + e % BM, sv[q], L.eps, L.first_step);
     }
 }
 
@@ -228,7 +292,8 @@ hipError_t launch_gemm(const GemmLaunch& L, int64_t items, hipStream_t stream, b
 
 hipError_t launch_gemm_reduce(const GemmLaunch& L, int64_t tiles, hipStream_t stream) {
     if (tiles <= 0) return hipSuccess;
-    hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)tiles), dim3(NT), 0, stream, L, tiles);
+    const int64_t slices = tiles * RED_SLICES;
+    hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)slices), dim3(NT), 0, stream, L, slices);
     return hipGetLastError();
 }
 
