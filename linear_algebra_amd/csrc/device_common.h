@@ -35,6 +35,17 @@ __device__ __forceinline__ void upper_decode(int64_t t, int64_t T, int& i, int& 
     j = (int)(r + (t - (r * T - r * (r - 1) / 2)));
 }
 
+// Column-by-column enumeration of an upper triangle: t = j(j+1)/2 + i with
+// 0 <= i <= j, so column j holds j + 1 entries.
+__device__ __forceinline__ void column_decode(int64_t t, int& i, int& j) {
+    int64_t r = (int64_t)((sqrt(8.0 * (double)t + 1.0) - 1.0) * 0.5);
+    if (r < 0) r = 0;
+    while (r > 0 && r * (r + 1) / 2 > t) --r;
+    while ((r + 1) * (r + 2) / 2 <= t) ++r;
+    j = (int)r;
+    i = (int)(t - r * (r + 1) / 2);
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
 
 }  // namespace kfac

@@ -70,10 +70,11 @@ struct PackLayer {
     float* m;             // [d][d] matrix
     int64_t d;
     int64_t off;          // first packed element of this layer
-    int64_t tile_begin;   // first unpack tile of this layer
+    int64_t tile_begin;   // first work unit of this layer (pack chunk or unpack tile)
     int64_t tiles_1d;     // unpack tiles per edge
 };
-hipError_t launch_pack(const PackLayer* layers_dev, int n, float* packed, int64_t total, hipStream_t stream);
+constexpr int kPackChunk = 4096;  // packed elements per pack workgroup
+hipError_t launch_pack(const PackLayer* layers_dev, int n, float* packed, int64_t blocks, hipStream_t stream);
 hipError_t launch_unpack(const PackLayer* layers_dev, int n, const float* packed, int64_t tiles,
                          hipStream_t stream);
 constexpr int kUnpackTile = 64;

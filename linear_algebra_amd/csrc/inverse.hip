@@ -164,6 +164,17 @@ __device__ __forceinline__ double readlane_f64(double v, int lane) {
     return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
 }
 
+// 1/sqrt(x) to double precision: the hardware estimate refined by two Newton
+// steps y <- y (3 - x y^2) / 2 (quadratic convergence).  Shorter on the
+// pivot chain than a square root followed by a division.
+__device__ __forceinline__ double rsqrt_refined(double x) {
+    double y = __builtin_amdgcn_rsq(x);
+    const double h = 0.5 * x;
+    y = y * fma(-h * y, y, 1.5);
+    y = y * fma(-h * y, y, 1.5);
+    return y;
+}
+
 // LDS scratch of factor_diagonal: two published rows, the reciprocals of the
 // diagonal, and one failure slot per wave.
 struct PanelScratch {
@@ -202,8 +213,8 @@ __device__ int factor_diagonal(double* P, double* Q, PanelScratch& S) {
             if (w == wb) {
                 const double piv = readlane_f64(a[s], c);
                 failed = (failed == 0 && !(piv > 0.0 && piv <= DBL_MAX)) ? c + 1 : failed;
-                const double sq = sqrt(piv);
-                a[s] = (j == c) ? sq : a[s] / sq;
+                const double y = rsqrt_refined(piv);
+                a[s] = (j == c) ? piv * y : a[s] * y;
                 Rc[j] = a[s];
             }
             __syncthreads();
@@ -276,7 +287,7 @@ __device__ __forceinline__ void record_info(const InvMat& M, int k, int f) {
 __global__ __launch_bounds__(NT) void inv_prepare_kernel(InvLaunch L, int64_t tiles) {
     int mi;
     int64_t local;
-    if (!locate(L, kInvPrepare, blockIdx.x, mi, local)) return;
+    if (!locate(L, kInvPrepare, xcd_remap(blockIdx.x, gridDim.x), mi, local)) return;
     const InvMat M = L.mats[mi];
     int bi, bj;
     upper_decode(local, M.nb, bi, bj);
@@ -313,7 +324,7 @@ __global__ __launch_bounds__(NT) void inv_panel_trsm_kernel(InvLaunch L, int64_t
     __shared__ PanelScratch R;
     int mi;
     int64_t local;
-    if (!locate(L, kInvPanel, blockIdx.x, mi, local)) return;
+    if (!locate(L, kInvPanel, xcd_remap(blockIdx.x, gridDim.x), mi, local)) return;
     const InvMat M = L.mats[mi];
     const int k = L.step;
     const int64_t D = (int64_t)M.nb * B;
@@ -364,7 +375,7 @@ __global__ __launch_bounds__(NT) void inv_syrk_kernel(InvLaunch L, int64_t tiles
     __shared__ double Bs[B * LD];
     int mi;
     int64_t local;
-    if (!locate(L, kInvSyrk, blockIdx.x, mi, local)) return;
+    if (!locate(L, kInvSyrk, xcd_remap(blockIdx.x, gridDim.x), mi, local)) return;
     const InvMat M = L.mats[mi];
     const int k = L.step;
     const int T = M.nb - k - 1;
@@ -414,7 +425,7 @@ __global__ __launch_bounds__(NT) void inv_trtri_a_kernel(InvLaunch L, int64_t ti
     __shared__ double Bs[B * LD];
     int mi;
     int64_t local;
-    if (!locate(L, kInvTrtri, blockIdx.x, mi, local)) return;
+    if (!locate(L, kInvTrtri, xcd_remap(blockIdx.x, gridDim.x), mi, local)) return;
     const InvMat M = L.mats[mi];
     int I, J, g1_end;
     trtri_decode(local, M.nb, L.step, I, J, g1_end);
@@ -437,7 +448,7 @@ __global__ __launch_bounds__(NT) void inv_trtri_b_kernel(InvLaunch L, int64_t ti
     __shared__ double Bs[B * LD];
     int mi;
     int64_t local;
-    if (!locate(L, kInvTrtri, blockIdx.x, mi, local)) return;
+    if (!locate(L, kInvTrtri, xcd_remap(blockIdx.x, gridDim.x), mi, local)) return;
     const InvMat M = L.mats[mi];
     int I, J, g1_end;
     trtri_decode(local, M.nb, L.step, I, J, g1_end);
@@ -460,10 +471,13 @@ __global__ __launch_bounds__(NT) void inv_lauum_kernel(InvLaunch L, int64_t tile
     __shared__ double Bs[B * LD];
     int mi;
     int64_t local;
-    if (!locate(L, kInvLauum, blockIdx.x, mi, local)) return;
+    if (!locate(L, kInvLauum, xcd_remap(blockIdx.x, gridDim.x), mi, local)) return;
     const InvMat M = L.mats[mi];
+    // column by column over the upper blocks (J ascending, I = 0..J): the
+    // longest products (small J) start first, and tiles that run side by side
+    // share the blocks of V row J
     int I, J;
-    upper_decode(local, M.nb, I, J);
+    column_decode(local, I, J);
     const int64_t D = (int64_t)M.nb * B, d = M.d;
     doublex4 acc[2][2];
     acc_zero(acc);

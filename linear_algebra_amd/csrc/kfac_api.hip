@@ -262,19 +262,22 @@ kfac_status_t kfac_pack_sym(int n, float* const* m, const int64_t* d, float* pac
     const size_t need = pack_ws(n);
     if (workspace == nullptr || !aligned(workspace, kAlign) || workspace_bytes < need) return KFAC_ERR_WORKSPACE;
 
+    // work units: pack chunks never cross a factor; unpack works on tiles
     std::vector<PackLayer> layers(n);
-    int64_t off = 0, tiles = 0;
+    int64_t off = 0, units = 0;
     for (int i = 0; i < n; ++i) {
         const int64_t t1 = ceil_div(d[i], kUnpackTile);
-        layers[i] = PackLayer{m[i], d[i], off, tiles, t1};
-        off += d[i] * (d[i] + 1) / 2;
-        tiles += t1 * (t1 + 1) / 2;
+        const int64_t elems = d[i] * (d[i] + 1) / 2;
+        layers[i] = PackLayer{m[i], d[i], off, units, t1};
+        off += elems;
+        units += (dir == KFAC_PACK) ? ceil_div(elems, kPackChunk) : t1 * (t1 + 1) / 2;
     }
     Carver c(workspace);
     PackLayer* dev = static_cast<PackLayer*>(c.take(sizeof(PackLayer) * n));
     hipError_t e = upload_table(dev, layers.data(), sizeof(PackLayer) * n, stream);
     if (e != hipSuccess) return KFAC_ERR_HIP;
-    if (dir == KFAC_PACK) return hip_status(launch_pack(dev, n, packed, off, stream));
+    if (dir == KFAC_PACK) return hip_status(launch_pack(dev, n, packed, units, stream));
+    const int64_t tiles = units;
     return hip_status(launch_unpack(dev, n, packed, tiles, stream));
 }
 

@@ -2,12 +2,10 @@
 // fused float32 buffer holding their upper triangles (incl. the diagonal),
 // row by row, layers back to back.  Both directions are bit-exact copies.
 //
-// Pack walks the fused buffer: each thread owns 4 consecutive packed
-// elements, so the writes are aligned 16-byte stores that tile the buffer
-// without gaps, and consecutive threads read consecutive entries of the same
-// matrix row.  The (layer, row, column) of a packed index comes from a
-// binary search over the layer offsets and the closed-form row start
-// i*d - i*(i-1)/2.
+// Pack walks the fused buffer in chunks that never cross a factor: the
+// workgroup finds its factor once, and lanes take consecutive packed
+// elements, so reads run along matrix rows and writes are contiguous.  The
+// row of a packed index comes from the closed-form row start i*d - i*(i-1)/2.
 //
 // Unpack works on 64 x 64 tiles of the upper block triangle of each matrix:
 // the tile's rows are read from the fused buffer (contiguous runs), staged in
@@ -20,7 +18,8 @@ namespace kfac {
 namespace {
 
 constexpr int PT = 256;
-constexpr int PER = 4;  // packed elements per thread
+constexpr int PACK_PER = kPackChunk / PT;  // packed elements per thread
+constexpr int PACK_CHUNK = kPackChunk;
 
 __device__ __forceinline__ int find_layer(const PackLayer* L, int n, int64_t p, bool by_tile) {
     int lo = 0, hi = n - 1;
@@ -45,40 +44,50 @@ __device__ __forceinline__ int64_t row_of(int64_t q, int64_t d) {
     return i;
 }
 
+// Row of the upper triangle of a d x d matrix holding local packed index q
+// (row i starts at i*d - i*(i-1)/2).  An fp32 square root lands within one
+// row of the answer for d <= 16384; integer checks settle it.
+__device__ __forceinline__ int64_t row_of_fast(int64_t q, int64_t d) {
+    const float a = 2.0f * (float)d + 1.0f;
+    int64_t i = (int64_t)((a - sqrtf(fmaxf(a * a - 8.0f * (float)q, 0.0f))) * 0.5f);
+    i = i < 0 ? 0 : (i > d - 1 ? d - 1 : i);
+    while (i > 0 && row_start(i, d) > q) --i;
+    while (i + 1 < d && row_start(i + 1, d) <= q) ++i;
+    return i;
+}
+
+// One workgroup copies PACK_CHUNK consecutive packed elements of a single
+// factor; thread t takes elements t + PT*s, so every wave instruction reads
+// a run of one matrix row and writes 256 contiguous bytes.
 __global__ __launch_bounds__(PT) void pack_kernel(const PackLayer* __restrict__ layers, int n,
-                                                  float* __restrict__ packed, int64_t total) {
-    const int64_t g = (int64_t)blockIdx.x * PT + threadIdx.x;
-    const int64_t p0 = g * PER;
-    if (p0 >= total) return;
-
-    int l = find_layer(layers, n, p0, false);
-    PackLayer L = layers[l];
-    int64_t q = p0 - L.off;
-    int64_t i = row_of(q, L.d);
-    int64_t j = i + (q - row_start(i, L.d));
-
-    float v[PER];
+                                                  float* __restrict__ packed, int64_t blocks) {
+    const int64_t blk = blockIdx.x;
+    if (blk >= blocks) return;
+    const PackLayer L = layers[find_layer(layers, n, blk, true)];
+    const int64_t d = L.d;
+    const int64_t total = d * (d + 1) / 2;
+    const int64_t q0 = (blk - L.tile_begin) * PACK_CHUNK;
+    // row of the first element from the closed form, later ones by walking
+    // forward (the next element is PT further on, at most a few rows down)
+    float v[PACK_PER];
+    int64_t q = q0 + threadIdx.x;
+    int64_t i = row_of_fast(q < total ? q : total - 1, d);
+    int64_t rs = row_start(i, d), re = rs + (d - i);   // [rs, re) are row i's packed indices
 #pragma unroll
-    for (int s = 0; s < PER; ++s) {
-        if (p0 + s < total) {
-            // a layer ends exactly where the next begins; skip empty ones
-            while (p0 + s >= L.off + L.d * (L.d + 1) / 2) {
-                L = layers[++l];
-                i = 0;
-                j = 0;
+    for (int s = 0; s < PACK_PER; ++s, q += PT) {
+        if (q < total) {
+            while (q >= re) {
+                ++i;
+                rs = re;
+                re += d - i;
             }
-            v[s] = L.m[i * L.d + j];
-            if (++j == L.d) { ++i; j = i; }
-        } else {
-            v[s] = 0.0f;
+            v[s] = L.m[i * d + i + (q - rs)];
         }
     }
-    if (p0 + PER <= total && ((reinterpret_cast<uintptr_t>(packed + p0) & 15) == 0)) {
-        *reinterpret_cast<float4*>(packed + p0) = make_float4(v[0], v[1], v[2], v[3]);
-    } else {
 #pragma unroll
-        for (int s = 0; s < PER; ++s)
-            if (p0 + s < total) packed[p0 + s] = v[s];
+    for (int s = 0; s < PACK_PER; ++s) {
+        const int64_t q = q0 + threadIdx.x + PT * s;
+        if (q < total) packed[L.off + q] = v[s];
     }
 }
 
@@ -130,11 +139,9 @@ __global__ __launch_bounds__(PT) void unpack_kernel(const PackLayer* __restrict_
 
 }  // namespace
 
-hipError_t launch_pack(const PackLayer* layers_dev, int n, float* packed, int64_t total, hipStream_t stream) {
-    if (total <= 0) return hipSuccess;
-    const int64_t threads = ceil_div(total, PER);
-    const int64_t blocks = ceil_div(threads, PT);
-    hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(PT), 0, stream, layers_dev, n, packed, total);
+hipError_t launch_pack(const PackLayer* layers_dev, int n, float* packed, int64_t blocks, hipStream_t stream) {
+    if (blocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(PT), 0, stream, layers_dev, n, packed, blocks);
     return hipGetLastError();
 }
 

@@ -196,3 +196,18 @@ def test_inverse_config5_ill_conditioned(gamma):
     assert np.all(info == 0), info
     worst = check_sampled(xs, zs, gamma, range(len(xs)), ncols=4)
     say(f"config 5 inverse gamma={float(gamma)}: worst sampled rel err {worst:.3e}")
+
+
+def test_inverse_well_conditioned_to_float32_rounding():
+    """With a condition number near 10 the only error left is the float32
+    rounding of the output: every matrix within 1e-6 of the oracle."""
+    rng = np.random.default_rng(21)
+    gamma = np.float32(0.5)
+    xs = [spd_f32(rng, d, 4 * d) for d in (64, 100, 257, 700)]
+    zs, info = gpu_inverse(xs, gamma)
+    assert np.all(info == 0)
+    for x, z in zip(xs, zs):
+        ref, _ = oracle.damped_inverse(x, gamma)
+        err = rel_fro(z, ref)
+        say("  well-conditioned d", x.shape[0], "err", err)
+        assert err <= 1e-6
