@@ -87,6 +87,62 @@ __device__ __forceinline__ float slab_load(__amdgpu_buffer_rsrc_t r, uint32_t of
     }
 }
 
+// Writes a finished 128 x 128 tile: to the split-K partial buffer when K is
+// split, else through the epilogue.  Output layout of a 32 x 32 MFMA block:
+// lane l holds column (l % 32); register r holds row 8*(r/4) + 4*(l/32) + (r%4).
+__device__ __forceinline__ void store_tile(const GemmProb& P, const GemmLaunch& L, const floatx16 (&sum)[2][2],
+                                           int kc, int t, int m0, int n0, int wm, int wn, int lane) {
+    const int khalf = lane >> 5;
+    float* part = (P.ksplit > 1) ? P.part + ((int64_t)kc * P.ntiles + t) * (BM * BM) : nullptr;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = wm * 64 + a * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
+                const int col = wn * 64 + b * 32 + (lane & 31);
+                if (part) {
+                    part[row * BM + col] = sum[a][b][r];
+                } else {
+                    store_elem(P, m0 + row, n0 + col, sum[a][b][r], L.eps, L.first_step);
+                }
+            }
+}
+
+// Tile and K-chunk of a work item.
+struct TileWork {
+    GemmProb P;
+    int kc, t, m0, n0, k_begin, k_end;
+    bool same, active;
+};
+
+__device__ __forceinline__ TileWork decode_item(const GemmLaunch& L, int64_t item) {
+    TileWork w;
+    w.P = L.probs[find_prob(L.probs, L.nprob, item, false)];
+    const GemmProb& P = w.P;
+    const int64_t q = item - P.item_begin;
+    w.kc = (int)(q / P.ntiles);
+    w.t = (int)(q % P.ntiles);
+    int ti, tj;
+    if (P.mode == kModeFactor) {
+        upper_decode(w.t, P.tiles_m, ti, tj);
+    } else {
+        ti = w.t / P.tiles_n;
+        tj = w.t % P.tiles_n;
+    }
+    w.m0 = ti * BM;
+    w.n0 = tj * BM;
+    w.k_begin = w.kc * P.kchunk;
+    w.k_end = min(P.K, w.k_begin + P.kchunk);
+    // factor tiles on the diagonal read the same columns for both operands
+    w.same = (P.a == P.b) && (w.m0 == w.n0);
+    const int wave = threadIdx.x >> 6;
+    // the wave below the diagonal of a diagonal factor tile has nothing to compute
+    w.active = !(P.mode == kModeFactor && ti == tj && (wave >> 1) > (wave & 1));
+    return w;
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(NT, 2) void gemm_tn_kernel(GemmLaunch L, int64_t items) {
     __shared__ __attribute__((aligned(16))) float As[2][BM * LDK];
@@ -94,31 +150,17 @@ __global__ __launch_bounds__(NT, 2) void gemm_tn_kernel(GemmLaunch L, int64_t it
 
     const int64_t item = xcd_remap(blockIdx.x, gridDim.x);
     if (item >= items) return;
-    const GemmProb P = L.probs[find_prob(L.probs, L.nprob, item, false)];
-
-    const int64_t w = item - P.item_begin;
-    const int kc = (int)(w / P.ntiles);
-    const int t = (int)(w % P.ntiles);
-    int ti, tj;
-    if (P.mode == kModeFactor) {
-        upper_decode(t, P.tiles_m, ti, tj);
-    } else {
-        ti = t / P.tiles_n;
-        tj = t % P.tiles_n;
-    }
-    const int m0 = ti * BM, n0 = tj * BM;
-    const int k_begin = kc * P.kchunk;
-    const int k_end = min(P.K, k_begin + P.kchunk);
-    // Factor tiles on the diagonal read the same columns for both operands.
-    const bool same = (P.a == P.b) && (m0 == n0);
+    const TileWork W = decode_item(L, item);
+    const GemmProb& P = W.P;
+    const int kc = W.kc, t = W.t, m0 = W.m0, n0 = W.n0, k_begin = W.k_begin, k_end = W.k_end;
+    const bool same = W.same;
     constexpr int esz = BF16 ? 2 : 4;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    // the wave below the diagonal of a diagonal factor tile has nothing to compute
-    const bool active = !(P.mode == kModeFactor && ti == tj && wm > wn);
+    const bool active = W.active;
 
     // Thread t loads column lc of the tile, slab rows lr8 .. lr8+7; the byte
     // offsets inside a slab are the same for every slab.
@@ -215,25 +257,133 @@ __global__ __launch_bounds__(NT, 2) void gemm_tn_kernel(GemmLaunch L, int64_t it
         __syncthreads();
     }
 
-    // Output layout of a 32 x 32 MFMA block: lane l holds column (l % 32);
-    // register r holds row 8*(r/4) + 4*(l/32) + (r%4).
-    const int khalf = lane >> 5;
-    const int ksplit = P.ksplit;
-    float* part = (ksplit > 1) ? P.part + ((int64_t)kc * P.ntiles + t) * (BM * BM) : nullptr;
+    store_tile(P, L, sum, kc, t, m0, n0, wm, wn, lane);
+}
+
+
+// bfloat16 inputs on v_mfma_f32_32x32x16_bf16 (products exact in float32,
+// float32 accumulation).  Slabs of 32 rows are staged as [m][k] bf16 with k
+// contiguous; a lane's eight k-values of a block are one 16-byte LDS read,
+// and each slab feeds 2 x 4 MFMAs per wave.  Elements are loaded one at a
+// time because rows of odd width are not 4-byte aligned.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+constexpr int BK16 = 32;
+constexpr int LDK16 = BK16 + 8;    // LDS row stride in bf16 (80 bytes)
+constexpr int LOADS16 = BK16 * BM / NT;   // 16 rows of one column per thread
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc16(const void* base, int64_t ld, int k0, int k_end) {
+    const char* p = static_cast<const char*>(base) + (int64_t)k0 * ld * 2;
+    const int rows = max(0, min(BK16, k_end - k0));
+    const int bytes = __builtin_amdgcn_readfirstlane(rows * (int)ld * 2);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p), (short)0, bytes, 0x00020000);
+}
+
+__global__ __launch_bounds__(NT, 2) void gemm_tn_bf16_kernel(GemmLaunch L, int64_t items) {
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDK16];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BM * LDK16];
+
+    const int64_t item = xcd_remap(blockIdx.x, gridDim.x);
+    if (item >= items) return;
+    const TileWork W = decode_item(L, item);
+    const GemmProb& P = W.P;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    // thread t loads column lc, slab rows lr16 .. lr16+15
+    const int lc = tid & (BM - 1);
+    const int lr16 = (tid >> 7) * LOADS16;
+    uint32_t offa[LOADS16], offb[LOADS16];
+#pragma unroll
+    for (int s = 0; s < LOADS16; ++s) {
+        const int row = lr16 + s;
+        offa[s] = (W.m0 + lc < P.M) ? (uint32_t)((row * P.lda + W.m0 + lc) * 2) : kOOB;
+        offb[s] = (W.n0 + lc < P.N) ? (uint32_t)((row * P.ldb + W.n0 + lc) * 2) : kOOB;
+    }
+    uint16_t ra[LOADS16], rb[LOADS16];
+    auto gload = [&](int k0) {
+        const __amdgpu_buffer_rsrc_t rA = slab_rsrc16(P.a, P.lda, k0, W.k_end);
+#pragma unroll
+        for (int s = 0; s < LOADS16; ++s) ra[s] = __builtin_amdgcn_raw_buffer_load_b16(rA, offa[s], 0, 0);
+        if (!W.same) {
+            const __amdgpu_buffer_rsrc_t rB = slab_rsrc16(P.b, P.ldb, k0, W.k_end);
+#pragma unroll
+            for (int s = 0; s < LOADS16; ++s) rb[s] = __builtin_amdgcn_raw_buffer_load_b16(rB, offb[s], 0, 0);
+        }
+    };
+    auto pack8 = [](const uint16_t* v) {
+        uint4 u;
+        u.x = (uint32_t)v[0] | ((uint32_t)v[1] << 16);
+        u.y = (uint32_t)v[2] | ((uint32_t)v[3] << 16);
+        u.z = (uint32_t)v[4] | ((uint32_t)v[5] << 16);
+        u.w = (uint32_t)v[6] | ((uint32_t)v[7] << 16);
+        return u;
+    };
+    auto sstore = [&](int buf) {
+        uint4* da = reinterpret_cast<uint4*>(&As[buf][lc * LDK16 + lr16]);
+        da[0] = pack8(ra);
+        da[1] = pack8(ra + 8);
+        if (!W.same) {
+            uint4* db = reinterpret_cast<uint4*>(&Bs[buf][lc * LDK16 + lr16]);
+            db[0] = pack8(rb);
+            db[1] = pack8(rb + 8);
+        }
+    };
+
+    floatx16 acc[2][2], sum[2][2];
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = wm * 64 + a * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
-                const int col = wn * 64 + b * 32 + (lane & 31);
-                if (part) {
-                    part[row * BM + col] = sum[a][b][r];
-                } else {
-                    store_elem(P, m0 + row, n0 + col, sum[a][b][r], L.eps, L.first_step);
+            for (int r = 0; r < 16; ++r) { acc[a][b][r] = 0.0f; sum[a][b][r] = 0.0f; }
+
+    const int nstages = (W.k_end - W.k_begin + BK16 - 1) / BK16;
+    if (nstages > 0) {
+        gload(W.k_begin);
+        sstore(0);
+    }
+    __syncthreads();
+
+    // lane l supplies rows/columns (l % 32) of its blocks; MFMA step s of a
+    // slab takes slab rows 16 s + 8 (l / 32) + 0..7
+    const int fr = lane & 31;
+    const int fk = (lane >> 5) * 8;
+    constexpr int SUB16 = kGemmSubK / BK16;
+
+    for (int st = 0; st < nstages; ++st) {
+        const int buf = st & 1;
+        if (st + 1 < nstages) gload(W.k_begin + (st + 1) * BK16);
+        if (W.active) {
+            const uint16_t* Ab = As[buf];
+            const uint16_t* Bb = W.same ? As[buf] : Bs[buf];
+#pragma unroll
+            for (int s = 0; s < BK16 / 16; ++s) {
+                bf16x8 fa[2], fb[2];
+#pragma unroll
+                for (int a = 0; a < 2; ++a) {
+                    fa[a] = *reinterpret_cast<const bf16x8*>(&Ab[(wm * 64 + a * 32 + fr) * LDK16 + 16 * s + fk]);
+                    fb[a] = *reinterpret_cast<const bf16x8*>(&Bb[(wn * 64 + a * 32 + fr) * LDK16 + 16 * s + fk]);
                 }
+                acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0], fb[0], acc[0][0], 0, 0, 0);
+                acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0], fb[1], acc[0][1], 0, 0, 0);
+                acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1], fb[0], acc[1][0], 0, 0, 0);
+                acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1], fb[1], acc[1][1], 0, 0, 0);
             }
+            if ((st + 1) % SUB16 == 0 || st + 1 == nstages) {
+#pragma unroll
+                for (int a = 0; a < 2; ++a)
+#pragma unroll
+                    for (int b = 0; b < 2; ++b) {
+                        sum[a][b] += acc[a][b];
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+                    }
+            }
+        }
+        if (st + 1 < nstages) sstore(buf ^ 1);
+        __syncthreads();
+    }
+    store_tile(P, L, sum, W.kc, W.t, W.m0, W.n0, wm, wn, lane);
 }
 
 // Sums the split-K partial tiles in chunk order and applies the epilogue.
@@ -283,7 +433,7 @@ __global__ __launch_bounds__(NT) void gemm_reduce_kernel(GemmLaunch L, int64_t s
 hipError_t launch_gemm(const GemmLaunch& L, int64_t items, hipStream_t stream, bool bf16) {
     if (items <= 0) return hipSuccess;
     if (bf16) {
-        hipLaunchKernelGGL(gemm_tn_kernel<true>, dim3((unsigned)items), dim3(NT), 0, stream, L, items);
+        hipLaunchKernelGGL(gemm_tn_bf16_kernel, dim3((unsigned)items), dim3(NT), 0, stream, L, items);
     } else {
         hipLaunchKernelGGL(gemm_tn_kernel<false>, dim3((unsigned)items), dim3(NT), 0, stream, L, items);
     }

@@ -101,11 +101,85 @@ size_t factors_ws(const FactorPlan& p, int n) {
 
 // --------------------------------------------------------- precondition --
 
+// Two launches of plain products per call: S^T = grad^T ginv, then
+// P = (S^T)^T ainv.  When a launch has too few 128 x 128 tiles to give every
+// CU several, K is split into equal chunks (partials summed in chunk order
+// by the reduce kernel) so the last round of tiles is not left half empty.
+struct PrecondPlan {
+    std::vector<GemmProb> p1, p2;
+    int64_t items1 = 0, items2 = 0, red1 = 0, red2 = 0;
+    size_t st_bytes = 0, part_bytes = 0;
+};
+
+constexpr int64_t kGemmSlots = 512;   // 256 CUs x 2 resident 128 x 128 tiles
+
+void plan_plain_launch(std::vector<GemmProb>& probs, int64_t& items, int64_t& red, int64_t& part_elems) {
+    int64_t tiles = 0;
+    double work = 0.0;
+    for (GemmProb& g : probs) {
+        g.tiles_m = (int32_t)ceil_div(g.M, kGemmTile);
+        g.tiles_n = (int32_t)ceil_div(g.N, kGemmTile);
+        g.ntiles = g.tiles_m * g.tiles_n;
+        tiles += g.ntiles;
+        work += (double)g.ntiles * g.K;
+    }
+    // aim for at least four tiles per slot; chunks of at least 256 rows
+    int64_t kc = INT64_MAX;
+    if (tiles < 4 * kGemmSlots) kc = std::max<int64_t>(256, align_up((int64_t)std::ceil(work / (4.0 * kGemmSlots)), 256));
+    items = red = part_elems = 0;
+    for (GemmProb& g : probs) {
+        const int64_t ks = (kc == INT64_MAX) ? 1 : std::max<int64_t>(1, ceil_div(g.K, kc));
+        g.ksplit = (int32_t)ks;
+        g.kchunk = (int32_t)align_up(ceil_div(g.K, ks), kGemmBK);
+        g.mode = kModePlain;
+        g.alpha = 1.0f;
+        g.item_begin = items;
+        g.red_begin = red;
+        items += (int64_t)g.ntiles * ks;
+        if (ks > 1) {
+            red += g.ntiles;
+            part_elems += (int64_t)g.ntiles * ks * kGemmTile * kGemmTile;
+        }
+    }
+}
+
+PrecondPlan plan_precondition(int n, const int64_t* d_g, const int64_t* d_a) {
+    PrecondPlan p;
+    p.p1.resize(n);
+    p.p2.resize(n);
+    for (int i = 0; i < n; ++i) {
+        GemmProb& a = p.p1[i];
+        std::memset(&a, 0, sizeof(a));
+        a.lda = d_a[i];
+        a.ldb = d_g[i];
+        a.ldc = d_g[i];
+        a.M = (int32_t)d_a[i];
+        a.N = (int32_t)d_g[i];
+        a.K = (int32_t)d_g[i];
+        GemmProb& b = p.p2[i];
+        std::memset(&b, 0, sizeof(b));
+        b.lda = d_g[i];
+        b.ldb = d_a[i];
+        b.ldc = d_a[i];
+        b.M = (int32_t)d_g[i];
+        b.N = (int32_t)d_a[i];
+        b.K = (int32_t)d_a[i];
+        p.st_bytes += align_up(sizeof(float) * (size_t)(d_g[i] * d_a[i]), 256);
+    }
+    int64_t part1 = 0, part2 = 0;
+    plan_plain_launch(p.p1, p.items1, p.red1, part1);
+    plan_plain_launch(p.p2, p.items2, p.red2, part2);
+    p.part_bytes = sizeof(float) * (size_t)std::max(part1, part2);   // the launches run one after the other
+    return p;
+}
+
 size_t precondition_ws(int n, const int64_t* d_g, const int64_t* d_a) {
+    const PrecondPlan p = plan_precondition(n, d_g, d_a);
     Carver c(nullptr);
     c.take(sizeof(GemmProb) * n);
     c.take(sizeof(GemmProb) * n);
-    for (int i = 0; i < n; ++i) c.take(sizeof(float) * (size_t)(d_g[i] * d_a[i]));
+    c.take(p.st_bytes);
+    c.take(p.part_bytes);
     return c.used;
 }
 
@@ -363,59 +437,45 @@ kfac_status_t kfac_precondition(int n, const float* const* ginv, const float* co
     const size_t need = precondition_ws(n, d_g, d_a);
     if (workspace == nullptr || !aligned(workspace, kAlign) || workspace_bytes < need) return KFAC_ERR_WORKSPACE;
 
+    PrecondPlan p = plan_precondition(n, d_g, d_a);
     Carver c(workspace);
     GemmProb* p1_dev = static_cast<GemmProb*>(c.take(sizeof(GemmProb) * n));
     GemmProb* p2_dev = static_cast<GemmProb*>(c.take(sizeof(GemmProb) * n));
-    std::vector<GemmProb> p1(n), p2(n);
-    int64_t items1 = 0, items2 = 0;
+    float* st_base = static_cast<float*>(c.take(p.st_bytes));
+    float* part = static_cast<float*>(c.take(p.part_bytes));
+    size_t st_off = 0;
+    int64_t part1 = 0, part2 = 0;
     for (int i = 0; i < n; ++i) {
-        float* st = static_cast<float*>(c.take(sizeof(float) * (size_t)(d_g[i] * d_a[i])));
-        // S^T [d_a][d_g] = grad^T . ginv   (ginv symmetric)
-        GemmProb& a = p1[i];
-        std::memset(&a, 0, sizeof(a));
+        float* st = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(st_base) + st_off);
+        st_off += align_up(sizeof(float) * (size_t)(d_g[i] * d_a[i]), 256);
+        GemmProb& a = p.p1[i];   // S^T [d_a][d_g] = grad^T . ginv   (ginv symmetric)
         a.a = grad[i];
         a.b = ginv[i];
         a.c = st;
-        a.lda = d_a[i];
-        a.ldb = d_g[i];
-        a.ldc = d_g[i];
-        a.M = (int32_t)d_a[i];
-        a.N = (int32_t)d_g[i];
-        a.K = (int32_t)d_g[i];
-        // P [d_g][d_a] = (S^T)^T . ainv
-        GemmProb& b = p2[i];
-        std::memset(&b, 0, sizeof(b));
+        GemmProb& b = p.p2[i];   // P [d_g][d_a] = (S^T)^T . ainv
         b.a = st;
         b.b = ainv[i];
         b.c = out[i];
-        b.lda = d_g[i];
-        b.ldb = d_a[i];
-        b.ldc = d_a[i];
-        b.M = (int32_t)d_g[i];
-        b.N = (int32_t)d_a[i];
-        b.K = (int32_t)d_a[i];
-        for (GemmProb* g : {&a, &b}) {
-            g->tiles_m = (int32_t)ceil_div(g->M, kGemmTile);
-            g->tiles_n = (int32_t)ceil_div(g->N, kGemmTile);
-            g->ntiles = g->tiles_m * g->tiles_n;
-            g->ksplit = 1;
-            g->kchunk = (int32_t)align_up(g->K, kGemmBK);
-            g->mode = kModePlain;
-            g->alpha = 1.0f;
+        if (a.ksplit > 1) {
+            a.part = part + part1;
+            part1 += (int64_t)a.ntiles * a.ksplit * kGemmTile * kGemmTile;
         }
-        a.item_begin = items1;
-        b.item_begin = items2;
-        items1 += a.ntiles;
-        items2 += b.ntiles;
+        if (b.ksplit > 1) {
+            b.part = part + part2;
+            part2 += (int64_t)b.ntiles * b.ksplit * kGemmTile * kGemmTile;
+        }
     }
-    hipError_t e = upload_table(p1_dev, p1.data(), sizeof(GemmProb) * n, stream);
-    if (e == hipSuccess) e = upload_table(p2_dev, p2.data(), sizeof(GemmProb) * n, stream);
+    hipError_t e = upload_table(p1_dev, p.p1.data(), sizeof(GemmProb) * n, stream);
+    if (e == hipSuccess) e = upload_table(p2_dev, p.p2.data(), sizeof(GemmProb) * n, stream);
     if (e != hipSuccess) return KFAC_ERR_HIP;
     GemmLaunch L1{p1_dev, n, 0, 0.0f, 0};
-    e = launch_gemm(L1, items1, stream, false);
+    e = launch_gemm(L1, p.items1, stream, false);
+    if (e == hipSuccess) e = launch_gemm_reduce(L1, p.red1, stream);
     if (e != hipSuccess) return KFAC_ERR_HIP;
     GemmLaunch L2{p2_dev, n, 0, 0.0f, 0};
-    return hip_status(launch_gemm(L2, items2, stream, false));
+    e = launch_gemm(L2, p.items2, stream, false);
+    if (e == hipSuccess) e = launch_gemm_reduce(L2, p.red2, stream);
+    return hip_status(e);
 }
 
 }  // extern "C"
