@@ -47,17 +47,52 @@ def algorithmic_work(cfg):
                 pack_bytes=b_pack, unpack_bytes=b_unpack, packed=packed)
 
 
-def cpu_baseline(cfg, data, budget_s=30.0):
+def kernel_source_sha256():
+    """Hash of the library's kernel sources, the key of stored counter data."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "linear_algebra_amd", "csrc", "*"))):
+        if p.endswith((".hip", ".h", ".cpp")):
+            h.update(os.path.basename(p).encode())
+            with open(p, "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, stage):
+    """HBM bytes per call (FETCH_SIZE + WRITE_SIZE, calibrated) of a stage,
+    from profiles/hbm_traffic.json, or None when none was taken for this
+    workload and stage or the kernels have changed since."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            doc = json.load(f)
+    except (OSError, ValueError):
+        return None
+    sha = kernel_source_sha256()
+    for e in doc.get("entries", []):
+        if e.get("workload") == workload and e.get("stage") == stage and e.get("kernel_source_sha256") == sha:
+            return int(e["fetch_bytes"]) + int(e["write_bytes"])
+    return None
+
+
+def cpu_baseline(cfg, data, budget_s=25.0, min_s=10.0):
     """The fp64 oracle on the host cores, over a bounded sample of the step:
-    whole layers are added (A and G factors, both inverses, the
-    preconditioned gradient) until the budget is spent; the rate is the
-    sample's algorithmic flops over its time."""
+    whole layers (A and G factors, running average, pack/unpack, both
+    inverses, the preconditioned gradient) are added in order, wrapping
+    round to the first layer when a step is done in under `min_s`, until
+    `min_s` is reached or the budget is spent; the rate is the sample's
+    algorithmic flops over its time."""
     import numpy as np
     import oracle
 
     eps, gamma = np.float32(cfg.eps), np.float32(cfg.gammas[0])
     flops, spent, done = 0, 0.0, 0
-    for li, layer in enumerate(cfg.layers):
+    order = list(range(cfg.n_layers))
+    while True:
+        li = order[done % len(order)]
+        layer = cfg.layers[li]
         a, g, grad = data[li]
         t0 = time.perf_counter()
         fa = oracle.factor(oracle.upcast(a, cfg.in_dtype))
@@ -75,7 +110,7 @@ def cpu_baseline(cfg, data, budget_s=30.0):
         for d in dims:
             flops += layer.rows * d * (d + 1) + d ** 3
         flops += 2 * layer.d_g * layer.d_a * (layer.d_g + layer.d_a)
-        if spent >= budget_s:
+        if spent >= budget_s or (done % len(order) == 0 and spent >= min_s):
             break
     try:
         cores = len(os.sched_getaffinity(0))
@@ -87,8 +122,73 @@ def cpu_baseline(cfg, data, budget_s=30.0):
         "unit": "TFLOP/s",
         "cores": min(cores, threads),
         "kind": "oracle",
-        "sample": f"{done} of {cfg.n_layers} layers of one step (factors, running average, pack/unpack, "
-                  f"both damped inverses, preconditioned gradient), fp64, {spent:.1f} s",
+        "sample": f"{done} layer passes over the {cfg.n_layers} layers of one step (factors, running average, "
+                  f"pack/unpack, both damped inverses, preconditioned gradient), fp64, {spent:.1f} s",
+    }
+
+
+def sweep_inverse(dims=(64, 128, 256, 512, 768, 1024, 1536, 2048, 3072, 4096, 6144, 8192), gamma=1e-3):
+    """Inverse time of one damped factor against its dimension: the
+    computation performance model of "Accelerating Distributed K-FAC with
+    Smart Parallelism of Computing and Communication Tasks" (Eq. 26 and
+    Fig. 8: d in [64, 8192], mean of 100 runs after 10 warm-ups; fewer runs
+    above d = 2048 to keep the sweep short).  Inputs are factors
+    (1/rows) a^T a of ReLU(N(0,1)) draws with rows = 2d.  Eq. 26 itself did
+    not survive on the page; it is read as t = alpha exp(beta d), fitted by
+    least squares on log t, and set against the cubic law t = a + b d^3."""
+    import numpy as np
+    import torch
+
+    import linear_algebra_amd as la
+
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    rows_out = []
+    for d in dims:
+        x = torch.randn(2 * d, d, device=dev, generator=gen).clamp_(min=0.0)
+        m = torch.zeros(d, d, device=dev)
+        la.kfac_factors([x], [m], 0.0, True)
+        z = torch.empty_like(m)
+        info = torch.zeros(1, dtype=torch.int32, device=dev)
+        runs = 100 if d <= 2048 else (30 if d <= 4096 else 10)
+        for _ in range(10):
+            la.kfac_damped_inverse([m], gamma, [z], info)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(runs):
+            la.kfac_damped_inverse([m], gamma, [z], info)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / runs
+        if int(info.item()) != 0:
+            raise RuntimeError(f"inverse failed at d={d}")
+        rows_out.append({"d": d, "ms": round(ms, 4), "runs": runs,
+                         "tflops_alg": round(d ** 3 / (ms * 1e-3) / 1e12, 3)})
+        print(f"sweep: d={d} {ms:.3f} ms", file=sys.stderr, flush=True)
+        del x, m, z
+    d = np.array([r["d"] for r in rows_out], dtype=np.float64)
+    t = np.array([r["ms"] for r in rows_out], dtype=np.float64)
+    # cubic: least squares on t = a + b d^3
+    A = np.stack([np.ones_like(d), d ** 3], axis=1)
+    (a3, b3), *_ = np.linalg.lstsq(A, t, rcond=None)
+    # exponential: least squares on log t = log a + b d
+    B = np.stack([np.ones_like(d), d], axis=1)
+    (la_, be), *_ = np.linalg.lstsq(B, np.log(t), rcond=None)
+    # chain + bulk: t = a d + b d^3 (a sequential pass over d/64 diagonal
+    # blocks plus cubic block-product work), relative least squares
+    C = np.stack([d / t, d ** 3 / t], axis=1)
+    (ac, bc), *_ = np.linalg.lstsq(C, np.ones_like(t), rcond=None)
+
+    def rel_rms(pred):
+        return float(np.sqrt(np.mean(((pred - t) / t) ** 2)))
+    return {
+        "metric": "damped inverse time vs dimension (computation performance model)",
+        "gamma": gamma, "points": rows_out,
+        "fit_cubic": {"a_ms": float(a3), "b_ms_per_d3": float(b3), "rel_rms": rel_rms(a3 + b3 * d ** 3)},
+        "fit_exponential": {"a_ms": float(np.exp(la_)), "b_per_d": float(be), "rel_rms": rel_rms(np.exp(la_ + be * d))},
+        "fit_chain_cubic": {"a_ms_per_d": float(ac), "b_ms_per_d3": float(bc), "rel_rms": rel_rms(ac * d + bc * d ** 3)},
     }
 
 
@@ -100,6 +200,8 @@ def main(argv=None):
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=25.0)
+    ap.add_argument("--sweep-inverse", action="store_true",
+                    help="time kfac_damped_inverse on single matrices of d in [64, 8192] and fit time models")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -114,6 +216,9 @@ def main(argv=None):
     from workloads import CONFIGS, gen_layer_step
 
     la.load_library()
+    if args.sweep_inverse:
+        print(json.dumps(sweep_inverse()), flush=True)
+        return 0
     dev = torch.device("cuda:0")
     cfg = CONFIGS[args.config]
     L = cfg.layers
@@ -213,7 +318,7 @@ def main(argv=None):
     dom = max(stages, key=lambda k: stage_ms[k])
     bound, rate, peak, unit = stage_rate[dom]
     roofline = {"bound": bound, "stage": dom, "achieved": round(rate / scale[unit], 3), "peak": peak / scale[unit],
-                "unit": unit, "frac": round(rate / peak, 4), "traffic": None}
+                "unit": unit, "frac": round(rate / peak, 4), "traffic": measured_traffic(cfg.name, dom)}
 
     result = {
         "metric": "K-FAC step ms (factors+inverse+precondition) & TFLOP/s vs MFMA peak, 1 GPU",

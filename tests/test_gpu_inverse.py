@@ -211,3 +211,32 @@ def test_inverse_well_conditioned_to_float32_rounding():
         err = rel_fro(z, ref)
         say("  well-conditioned d", x.shape[0], "err", err)
         assert err <= 1e-6
+
+
+@pytest.mark.timeout(400)
+def test_inverse_max_dimension_8192():
+    """The largest dimension of the inverse-time sweep, d = 8192, against
+    oracle columns, and the residual (X + gamma I) z_j - e_j of those
+    columns in fp64."""
+    d, gamma = 8192, np.float32(1e-3)
+    rng = np.random.default_rng(8192)
+    a = np.maximum(rng.standard_normal((d, d), dtype=np.float32), 0)
+    x = ((a.T @ a) / np.float32(d)).astype(np.float32)
+    x = np.triu(x) + np.triu(x, 1).T
+    say("inverse d=8192")
+    zs, info = gpu_inverse([x], gamma)
+    assert info[0] == 0
+    z = zs[0]
+    cols = np.array([0, 1234, 5000, d - 1])
+    ref, rinfo = oracle.damped_inverse_columns(x, gamma, cols)
+    assert rinfo == 0
+    err = rel_fro(z[:, cols].T, ref)
+    xd = x.astype(np.float64) + float(gamma) * np.eye(d)
+    res = xd @ z[:, cols].astype(np.float64) - np.eye(d)[:, cols]
+    say(f"inverse d=8192: rel err {err:.3e}, max residual {np.abs(res).max():.3e}")
+    assert err <= TOL
+    # backward error of a float32-stored inverse: a few units of float32
+    # rounding times ||X + gamma I|| ||z_j||
+    for q in range(len(cols)):
+        bound = 64 * 2.0 ** -24 * np.linalg.norm(xd, 1) * np.abs(z[:, cols[q]]).sum()
+        assert np.abs(res[:, q]).max() <= bound
