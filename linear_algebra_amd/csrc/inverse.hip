@@ -4,13 +4,13 @@
 // Each matrix is padded with the identity to D = nb * 64 and processed in
 // 64 x 64 blocks in a float64 workspace W (row-major D x D):
 //
-//   prepare   W = sym(X) + gamma I (upper blocks), and the Cholesky of the
-//             first diagonal block;
-//   potrf     for k = 0 .. nb-2 (right-looking, upper: Y = U^T U)
-//               trsm  U_kj = U_kk^-T W_kj           (j > k)
-//               syrk  W_ij -= U_ki^T U_kj           (k < i <= j); the
-//                     workgroup that updates block (k+1, k+1) then factors it
-//                     and inverts its triangle (one wave, registers);
+//   prepare   W = sym(X) + gamma I (upper blocks), identity in the padding;
+//   potrf     for k = 0 .. nb-1 (right-looking, upper: Y = U^T U)
+//               panel every workgroup of row k factors the diagonal block
+//                     (k, k) and inverts its triangle (16-row strips, see
+//                     factor_diagonal), then solves one block of the row:
+//                     U_kj = U_kk^-T W_kj             (j > k)
+//               syrk  W_ij -= U_ki^T U_kj           (k < i <= j);
 //   trtri     V = U^-1 by recursive doubling over groups of blocks: for
 //             sibling groups G1, G2 (G1 before G2)
 //               V_12 = -V_11 . (U_12 . V_22)
@@ -164,108 +164,237 @@ __device__ __forceinline__ double readlane_f64(double v, int lane) {
     return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
 }
 
-// 1/sqrt(x) to double precision: the hardware estimate refined by two Newton
-// steps y <- y (3 - x y^2) / 2 (quadratic convergence).  Shorter on the
-// pivot chain than a square root followed by a division.
+// 1/sqrt(x) to double precision: the hardware estimate (relative error
+// about 5e-8) refined by one third-order step, y <- y + y r (1/2 + 3/8 r)
+// with r = 1 - x y^2 (the series of (1 - r)^(-1/2)), which cubes the error;
+// four dependent operations on the pivot chain.
 __device__ __forceinline__ double rsqrt_refined(double x) {
-    double y = __builtin_amdgcn_rsq(x);
-    const double h = 0.5 * x;
-    y = y * fma(-h * y, y, 1.5);
-    y = y * fma(-h * y, y, 1.5);
-    return y;
+    const double y = __builtin_amdgcn_rsq(x);
+    const double r = fma(-x * y, y, 1.0);
+    return fma(y * r, fma(0.375, r, 0.5), y);
 }
 
-// LDS scratch of factor_diagonal: two published rows, the reciprocals of the
-// diagonal, and one failure slot per wave.
+constexpr int SB = 16;          // strip height and leaf block edge
+constexpr int NS = B / SB;      // strips per diagonal block
+
+// LDS scratch of factor_diagonal: 1 / U_cc of every pivot, one failure
+// slot per strip.
 struct PanelScratch {
-    double row[2][B];
-    double rdiag[B];
-    int fail[NT / 64];
+    double row[B];      // the current pivot row of the strip being factored
+    double ydiag[B];
+    int fail[NS];
 };
 
-constexpr int RS = B / 4;   // rows of the diagonal block per wave
+// acc += (neg ? -1 : 1) A B over K = 16 for 16 x 16 blocks in LDS (row
+// stride LD): A[i][k] = X[xr + i][xc + k], or X[xr + k][xc + i] when `at`;
+// B[k][j] = Y[yr + k][yc + j].  Lane l feeds A[l % 16][4c + l / 16] and
+// B[4c + l / 16][l % 16] to k-chunk c of v_mfma_f64_16x16x4f64.
+__device__ __forceinline__ void mm16(doublex4& acc, const double* X, int xr, int xc, bool at, const double* Y,
+                                     int yr, int yc, bool neg) {
+    const int l = threadIdx.x & 63, li = l & 15, lk = l >> 4;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+        const int k = 4 * kc + lk;
+        double a = at ? X[(xr + k) * LD + xc + li] : X[(xr + li) * LD + xc + k];
+        const double b = Y[(yr + k) * LD + yc + li];
+        if (neg) a = -a;
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc, 0, 0, 0);
+    }
+}
+// 16 x 16 block <-> accumulator (lane l: column l % 16, rows l / 16 + 4r).
+__device__ __forceinline__ void load16(doublex4& acc, const double* X, int r0, int c0) {
+    const int l = threadIdx.x & 63;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = X[(r0 + (l >> 4) + 4 * r) * LD + c0 + (l & 15)];
+}
+__device__ __forceinline__ void store16(const doublex4& acc, double* X, int r0, int c0) {
+    const int l = threadIdx.x & 63;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) X[(r0 + (l >> 4) + 4 * r) * LD + c0 + (l & 15)] = acc[r];
+}
+__device__ __forceinline__ doublex4 zero4() {
+    doublex4 z;
+    z[0] = z[1] = z[2] = z[3] = 0.0;
+    return z;
+}
+
+// Cholesky of strip s (rows SB*s .. SB*s + 15 of the diagonal block, already
+// updated by the strips above it).  Lane j holds column (SB*s + j) mod 64 in
+// u[0..15], so the strip's own diagonal block sits in lanes 0..15; the
+// wrapped lanes (columns left of the strip) carry values nobody reads.
+// Pivot c takes the diagonal entry from lane c, scales row c by its inverse
+// square root (stored as ydiag = 1 / U_cc) and subtracts the rank-one update
+// from the rows below.  Row c + 1 gets its update first, through a
+// cross-lane read, so that pivot c + 1's square-root chain runs beside the
+// other rows' updates, which read row c back from LDS (same address in
+// every lane).  Returns the 1-based column of the first pivot that is not
+// positive or not finite, or 0.
+__device__ __forceinline__ int strip_factor(double (&u)[SB], PanelScratch& S, int s, int j) {
+    int failed = 0;
+    double piv = readlane_f64(u[0], 0);
+    double yc = rsqrt_refined(piv);
+#pragma unroll
+    for (int c = 0; c < SB; ++c) {
+        failed = (failed == 0 && !(piv > 0.0 && piv <= DBL_MAX)) ? SB * s + c + 1 : failed;
+        S.ydiag[SB * s + c] = yc;   // every lane, same value: no branch per pivot
+        u[c] *= yc;   // lane c holds the pivot itself: U_cc = piv / sqrt(piv)
+        if (c + 1 < SB) {
+            if (c + 2 < SB) S.row[j] = u[c];
+            u[c + 1] = fma(-readlane_f64(u[c], c + 1), u[c], u[c + 1]);
+            const double pn = readlane_f64(u[c + 1], c + 1);
+            const double yn = rsqrt_refined(pn);
+#pragma unroll
+            for (int t = c + 2; t < SB; ++t) u[t] = fma(-S.row[t], u[c], u[t]);
+            piv = pn;
+            yc = yn;
+        }
+        // keep each step's reads within the step: hoisted, they hold too
+        // many registers
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    return failed;
+}
+
+// V_qq = U_qq^-1 of strip q's 16 x 16 diagonal block, lane j < 16 computing
+// column SB*q + j: solves U V = I from the last row up; row t is scaled by
+// 1 / U_tt and then eliminated from the rows above.  U_qq is read from P
+// (same address in every lane); V_qq is written into the diagonal block
+// (q, q) of Q.
+__device__ __forceinline__ void leaf_inverse(const double* P, const double* ydiag, int q, int j, double* Q) {
+    const double* yq = ydiag + SB * q;
+    double v[SB];
+#pragma unroll
+    for (int k = 0; k < SB; ++k) v[k] = (j == k) ? 1.0 : 0.0;
+#pragma unroll
+    for (int t = SB - 1; t >= 0; --t) {
+        // U_qq[k][t] = P[off + k * LD + t]; the offset is tied to the
+        // previous step's result so that the reads of a step cannot be
+        // hoisted further than one step ahead (all 120 of them live at once
+        // would not fit in registers)
+        int off = SB * q * (LD + 1);
+        if (t + 1 < SB) asm volatile("" : "+s"(off) : "v"(v[t + 1]));
+        v[t] *= yq[t];
+#pragma unroll
+        for (int k = 0; k < t; ++k) v[k] = fma(-P[off + k * LD + t], v[t], v[k]);
+    }
+    if (j < SB) {
+        double* V = Q + SB * q * (LD + 1);
+#pragma unroll
+        for (int k = 0; k < SB; ++k) V[k * LD + j] = v[k];
+    }
+}
 
 // Cholesky P = U^T U and V = U^-1 of the 64 x 64 diagonal block in LDS
-// (upper triangle of P read; U written back with zeros below the diagonal,
-// V into Q).  Wave w keeps rows 16w..16w+15 of every column in registers
-// (lane j owns column j).  Right-looking: at step c the wave that owns row c
-// takes the pivot from lane c, scales the row and publishes it through LDS
-// (two alternating rows); after one barrier every wave subtracts the
-// rank-one update from its rows below c.  The steps run as 4 rolled rounds
-// of 16 unrolled steps, so register slots are compile-time constants while
-// the code stays small.  V solves U V = I from the bottom row up with the
-// same layout: row k is divided by U_kk, published, and eliminated from the
-// rows above.  Returns the 1-based column of the first pivot that is not
-// positive or not finite, or 0 (in every thread).
+// (upper triangle of P read; V written to Q with zeros below the diagonal;
+// P is left holding U in its upper blocks and scratch below).  Recursive in
+// 16-row strips: wave s factors strip s in registers (no block barrier per
+// pivot), then all waves subtract the strip's product from the trailing
+// 16 x 16 blocks on the matrix cores.  While wave s + 1 factors its strip,
+// wave s inverts its own 16 x 16 leaf.  The leaves are joined by two levels
+// of doubling, V_12 = -V_11 (U_12 V_22), as 16 x 16 block products; the
+// inner products are parked in P's lower blocks.  Returns the 1-based column
+// of the first pivot that is not positive or not finite, or 0 (in every
+// thread).
 __device__ int factor_diagonal(double* P, double* Q, PanelScratch& S) {
-    const int w = threadIdx.x >> 6, j = threadIdx.x & 63;
-    double a[RS];
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), j = threadIdx.x & 63;
+    static_assert(NS == 4 && NT == 256, "one wave per strip");
+    // zero Q's six 16 x 16 blocks below the diagonal (no branches)
+    {
+        const int r = threadIdx.x >> 4, c = threadIdx.x & 15;
+        constexpr int lower[6][2] = {{1, 0}, {2, 0}, {2, 1}, {3, 0}, {3, 1}, {3, 2}};
+#pragma unroll
+        for (int q = 0; q < 6; ++q) Q[(SB * lower[q][0] + r) * LD + SB * lower[q][1] + c] = 0.0;
+    }
     __syncthreads();
-#pragma unroll
-    for (int s = 0; s < RS; ++s) a[s] = P[(RS * w + s) * LD + j];
-    int failed = 0;
+    double u[SB];
 #pragma unroll 1
-    for (int wb = 0; wb < 4; ++wb) {
+    for (int s = 0; s < NS; ++s) {
+        if (w == s) {
+            const int col = (SB * s + j) & (B - 1);
 #pragma unroll
-        for (int s = 0; s < RS; ++s) {
-            const int c = RS * wb + s;
-            double* Rc = S.row[s & 1];
-            if (w == wb) {
-                const double piv = readlane_f64(a[s], c);
-                failed = (failed == 0 && !(piv > 0.0 && piv <= DBL_MAX)) ? c + 1 : failed;
-                const double y = rsqrt_refined(piv);
-                a[s] = (j == c) ? piv * y : a[s] * y;
-                Rc[j] = a[s];
+            for (int c = 0; c < SB; ++c) u[c] = P[(SB * s + c) * LD + col];
+            const int f = strip_factor(u, S, s, j);
+#pragma unroll
+            for (int c = 0; c < SB; ++c) P[(SB * s + c) * LD + col] = u[c];
+            if (j == 0) S.fail[s] = f;
+        } else if (w == s - 1) {
+            leaf_inverse(P, S.ydiag, w, j, Q);
+        }
+        __syncthreads();
+        if (s + 1 < NS) {
+            // trailing blocks (b, c), s < b <= c, numbered row by row
+            const int n = (NS - 1 - s) * (NS - s) / 2;
+            for (int q = w; q < n; q += NT / 64) {
+                int b = s + 1, r = q;
+                while (r >= NS - b) {
+                    r -= NS - b;
+                    ++b;
+                }
+                const int c = b + r;
+                doublex4 acc;
+                load16(acc, P, SB * b, SB * c);
+                mm16(acc, P, SB * s, SB * b, true, P, SB * s, SB * c, true);
+                store16(acc, P, SB * b, SB * c);
             }
             __syncthreads();
-            const double uj = Rc[j];
-            if (w == wb) {
-#pragma unroll
-                for (int t = s + 1; t < RS; ++t) a[t] = fma(-Rc[RS * w + t], uj, a[t]);
-            } else if (w > wb) {
-#pragma unroll
-                for (int t = 0; t < RS; ++t) a[t] = fma(-Rc[RS * w + t], uj, a[t]);
-            }
         }
     }
-    if (j == 0) S.fail[w] = failed;
-#pragma unroll
-    for (int s = 0; s < RS; ++s) {
-        const int i = RS * w + s;
-        P[i * LD + j] = (j >= i) ? a[s] : 0.0;
-        a[s] = (i == j) ? 1.0 : 0.0;
-    }
+    if (w == NS - 1) leaf_inverse(P, S.ydiag, w, j, Q);
     __syncthreads();
-    if (threadIdx.x < B) S.rdiag[threadIdx.x] = 1.0 / P[threadIdx.x * LD + threadIdx.x];
-    __syncthreads();
-#pragma unroll 1
-    for (int wb = 3; wb >= 0; --wb) {
+    // doubling, 16 -> 32: V_01, V_23; and T_02 = U_02 V_22, T_12 = U_12 V_22
+    // parked in P's blocks (2, 0), (2, 1)
+    {
+        doublex4 t = zero4(), v = zero4();
+        if (w == 0 || w == 1) {
+            const int o = 32 * w;   // pair (0, 1) or (2, 3)
+            mm16(t, P, o, o + 16, false, Q, o + 16, o + 16, false);          // T = U_ab V_bb
+            const int l = threadIdx.x & 63, li = l & 15, lk = l >> 4;
 #pragma unroll
-        for (int s = RS - 1; s >= 0; --s) {
-            const int k = RS * wb + s;
-            double* Rk = S.row[s & 1];
-            if (w == wb) {
-                a[s] *= S.rdiag[k];
-                Rk[j] = a[s];
-            }
-            __syncthreads();
-            const double vj = Rk[j];
-            if (w == wb) {
-#pragma unroll
-                for (int t = 0; t < s; ++t) a[t] = fma(-P[(RS * w + t) * LD + k], vj, a[t]);
-            } else if (w < wb) {
-#pragma unroll
-                for (int t = 0; t < RS; ++t) a[t] = fma(-P[(RS * w + t) * LD + k], vj, a[t]);
-            }
+            for (int kc = 0; kc < 4; ++kc)                                      // V_ab = -V_aa T
+                v = __builtin_amdgcn_mfma_f64_16x16x4f64(-Q[(o + li) * LD + o + 4 * kc + lk], t[kc], v, 0, 0, 0);
+            store16(v, Q, o, o + 16);
+        } else {
+            const int a = w - 2;    // T_a2 = U_a2 V_22
+            mm16(t, P, 16 * a, 32, false, Q, 32, 32, false);
+            store16(t, P, 32, 16 * a);
         }
     }
-#pragma unroll
-    for (int s = 0; s < RS; ++s) Q[(RS * w + s) * LD + j] = a[s];
     __syncthreads();
-    // pivots are visited in order, so the first failure is the smallest code
+    // 32 -> 64, first half: T_03, T_13 parked in (3, 0), (3, 1); V_12, V_02
+    {
+        doublex4 t = zero4();
+        if (w <= 1) {
+            const int a = w;        // T_a3 = U_a2 V_23 + U_a3 V_33
+            mm16(t, P, 16 * a, 32, false, Q, 32, 48, false);
+            mm16(t, P, 16 * a, 48, false, Q, 48, 48, false);
+            store16(t, P, 48, 16 * a);
+        } else if (w == 2) {        // V_12 = -V_11 T_12
+            mm16(t, Q, 16, 16, false, P, 32, 16, true);
+            store16(t, Q, 16, 32);
+        } else {                    // V_02 = -(V_00 T_02 + V_01 T_12)
+            mm16(t, Q, 0, 0, false, P, 32, 0, true);
+            mm16(t, Q, 0, 16, false, P, 32, 16, true);
+            store16(t, Q, 0, 32);
+        }
+    }
+    __syncthreads();
+    // second half: V_03 = -(V_00 T_03 + V_01 T_13), V_13 = -V_11 T_13
+    {
+        doublex4 t = zero4();
+        if (w == 0) {
+            mm16(t, Q, 0, 0, false, P, 48, 0, true);
+            mm16(t, Q, 0, 16, false, P, 48, 16, true);
+            store16(t, Q, 0, 48);
+        } else if (w == 1) {
+            mm16(t, Q, 16, 16, false, P, 48, 16, true);
+            store16(t, Q, 16, 48);
+        }
+    }
+    __syncthreads();
+    // strips are factored in order, so the first failure is the smallest code
     int f = 0;
 #pragma unroll
-    for (int q = 0; q < NT / 64; ++q) {
+    for (int q = 0; q < NS; ++q) {
         const int v = S.fail[q];
         f = (v != 0 && (f == 0 || v < f)) ? v : f;
     }
@@ -318,10 +447,10 @@ __global__ __launch_bounds__(NT) void inv_prepare_kernel(InvLaunch L, int64_t ti
 // blocks to the right, solves one of them: U_kj = U_kk^-T W_kj.  The
 // workgroup of the first such block (or the only one) stores U_kk^-1 and the
 // failure code.
-__global__ __launch_bounds__(NT) void inv_panel_trsm_kernel(InvLaunch L, int64_t tiles) {
+__global__ __launch_bounds__(NT, 2) void inv_panel_trsm_kernel(InvLaunch L, int64_t tiles) {
+    __shared__ PanelScratch R;
     __shared__ double As[B * LD];
     __shared__ double Bs[B * LD];
-    __shared__ PanelScratch R;
     int mi;
     int64_t local;
     if (!locate(L, kInvPanel, xcd_remap(blockIdx.x, gridDim.x), mi, local)) return;
@@ -338,7 +467,7 @@ __global__ __launch_bounds__(NT) void inv_panel_trsm_kernel(InvLaunch L, int64_t
         fetch(ra, Blk{Wkk, D, false});
         put(As, ra, false);
     }
-    const int f = factor_diagonal(As, Bs, R);   // As: U_kk, Bs: U_kk^-1
+    const int f = factor_diagonal(As, Bs, R);   // Bs: U_kk^-1 (As is scratch now)
     // W_kk itself is left as it is: other workgroups of this launch read it,
     // and no later step reads a diagonal block of W (they use dinv).
     if (local == 0) {
