@@ -110,6 +110,8 @@ struct InvLaunch {
     int32_t nbuckets;
     int32_t step;         // k for potrf steps, level for trtri
     double gamma;
+    int64_t split;        // potrf step launch: blocks [0, split) are row-k blocks
+    int64_t tail_first;   // potrf step launch: first block of the trailing update
 };
 
 // Tiles each inverse kernel needs per matrix with nb blocks per edge at a
@@ -124,9 +126,9 @@ __host__ __device__ inline int64_t inv_tiles(int kind, int64_t nb, int64_t step)
             return nb * (nb + 1) / 2;
         case kInvPanel:  // one workgroup per block right of the diagonal, at least one
             return nb > step ? (nb - step - 1 > 1 ? nb - step - 1 : 1) : 0;
-        case kInvSyrk: {
+        case kInvSyrk: {  // step k applies step k-1's update to blocks (i, j), k < i <= j
             const int64_t t = nb - step - 1;
-            return t > 0 ? t * (t + 1) / 2 : 0;
+            return step >= 1 && t > 0 ? t * (t + 1) / 2 : 0;
         }
         case kInvTrtri: {
             // level >= 1 joins pairs of groups of h = 2^(level-1) blocks
@@ -140,8 +142,7 @@ __host__ __device__ inline int64_t inv_tiles(int kind, int64_t nb, int64_t step)
 }
 
 hipError_t launch_inv_prepare(const InvLaunch& L, int64_t tiles, hipStream_t s);
-hipError_t launch_inv_panel_trsm(const InvLaunch& L, int64_t tiles, hipStream_t s);
-hipError_t launch_inv_syrk(const InvLaunch& L, int64_t tiles, hipStream_t s);
+hipError_t launch_inv_step(const InvLaunch& L, int64_t tiles, hipStream_t s);
 hipError_t launch_inv_trtri_a(const InvLaunch& L, int64_t tiles, hipStream_t s);
 hipError_t launch_inv_trtri_b(const InvLaunch& L, int64_t tiles, hipStream_t s);
 hipError_t launch_inv_lauum(const InvLaunch& L, int64_t tiles, hipStream_t s);

@@ -5,12 +5,15 @@
 // 64 x 64 blocks in a float64 workspace W (row-major D x D):
 //
 //   prepare   W = sym(X) + gamma I (upper blocks), identity in the padding;
-//   potrf     for k = 0 .. nb-1 (right-looking, upper: Y = U^T U)
-//               panel every workgroup of row k factors the diagonal block
-//                     (k, k) and inverts its triangle (16-row strips, see
-//                     factor_diagonal), then solves one block of the row:
-//                     U_kj = U_kk^-T W_kj             (j > k)
-//               syrk  W_ij -= U_ki^T U_kj           (k < i <= j);
+//   potrf     right-looking, upper (Y = U^T U), one launch per step k with
+//             a look-ahead of one step:
+//               row k     W_kj -= U_{k-1,k}^T U_{k-1,j}   (j >= k); then
+//                         every row-k workgroup factors the diagonal block
+//                         and inverts its triangle (16-row strips, see
+//                         factor_diagonal) and solves one block of the row:
+//                         U_kj = U_kk^-T W_kj           (j > k)
+//               trailing  W_ij -= U_{k-1,i}^T U_{k-1,j} (k < i <= j), in
+//                         the same launch, beside the row-k workgroups;
 //   trtri     V = U^-1 by recursive doubling over groups of blocks: for
 //             sibling groups G1, G2 (G1 before G2)
 //               V_12 = -V_11 . (U_12 . V_22)
@@ -23,9 +26,9 @@
 // largest first; every launch covers every matrix that has work at that
 // step, so independent inverses of different layers run side by side.
 //
-// Block products stage 64 x 64 operand blocks in LDS; the next pair of
-// blocks is fetched into registers while the matrix cores work on the
-// current pair.
+// Block products stage their operands in LDS in halves of 32 k-columns,
+// double buffered, so that the next half is written and the one after it
+// fetched while the matrix cores work on the current one.
 #include <float.h>
 
 #include "device_common.h"
@@ -103,28 +106,109 @@ __device__ __forceinline__ void mma_block(doublex4 (&acc)[2][2], const double* A
     }
 }
 
-// acc += sum_{t in [t0, t1)} A_t B_t^T (in the LDS convention of mma_block),
-// with the blocks of step t given by srcA(t), srcB(t).  `same` reuses the A
-// block for B.  Loads of step t+1 are in flight during the products of step t.
+// Products of many blocks stage their operands in halves of 32 k-columns,
+// double buffered: while the matrix cores work on one half, the next half is
+// written to LDS and the half after it is loaded from memory, with one
+// barrier per half.  Four staged halves (A and B, two buffers each) take as
+// much LDS as two whole blocks, so two workgroups still share a CU.
+constexpr int KH = 32;            // k-columns per half
+constexpr int LDH = KH + 1;       // LDS row stride of a staged half (doubles)
+constexpr int HB = B * LDH;       // doubles per staged half
+constexpr int HPER = B * KH / NT; // half-block elements per thread (8)
+constexpr int STAGE = 4 * HB;     // LDS doubles of the staging area
+
+// Half h of block b, as [m][k] with k in [32h, 32h + 32): for an untransposed
+// block m is its row and k its column, for a transposed one the reverse.
+// Each wave reads 256- or 512-byte row segments.
+__device__ __forceinline__ void fetch_half(double (&v)[HPER], const Blk& b, int h) {
+    const int t = threadIdx.x;
+    if (!b.trans) {
+        const int c = KH * h + (t & 31), r = t >> 5;
+#pragma unroll
+        for (int s = 0; s < HPER; ++s) v[s] = b.p[(int64_t)(r + 8 * s) * b.ld + c];
+    } else {
+        const int c = t & 63, r = KH * h + (t >> 6);
+#pragma unroll
+        for (int s = 0; s < HPER; ++s) v[s] = b.p[(int64_t)(r + 4 * s) * b.ld + c];
+    }
+}
+__device__ __forceinline__ void put_half(double* S, const double (&v)[HPER], bool trans) {
+    const int t = threadIdx.x;
+    if (!trans) {
+        const int k = t & 31, m = t >> 5;
+#pragma unroll
+        for (int s = 0; s < HPER; ++s) S[(m + 8 * s) * LDH + k] = v[s];
+    } else {
+        const int m = t & 63, k = t >> 6;
+#pragma unroll
+        for (int s = 0; s < HPER; ++s) S[m * LDH + k + 4 * s] = v[s];
+    }
+}
+
+// acc[m][n] += (neg ? -1 : 1) * sum_k A[m][k] B[n][k] over one staged half;
+// the wave layout of mma_block.
+__device__ __forceinline__ void mma_half(doublex4 (&acc)[2][2], const double* A, const double* Bm, bool neg) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wr = wave >> 1, wc = wave & 1;
+    const int li = lane & 15, lk = lane >> 4;
+    const double* a0p = A + (wr * 32 + li) * LDH + lk;
+    const double* a1p = a0p + 16 * LDH;
+    const double* b0p = Bm + (wc * 32 + li) * LDH + lk;
+    const double* b1p = b0p + 16 * LDH;
+#pragma unroll
+    for (int k0 = 0; k0 < KH; k0 += 4) {
+        double a0 = a0p[k0], a1 = a1p[k0];
+        const double b0 = b0p[k0], b1 = b1p[k0];
+        if (neg) { a0 = -a0; a1 = -a1; }
+        acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, acc[0][0], 0, 0, 0);
+        acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, acc[0][1], 0, 0, 0);
+        acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, acc[1][0], 0, 0, 0);
+        acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, acc[1][1], 0, 0, 0);
+    }
+}
+
+// acc += (neg ? -1 : 1) sum_{t in [t0, t1)} A_t B_t^T, A_t and B_t the
+// 64 x 64 blocks srcA(t), srcB(t) (staged as [m][k]); `same` reuses A for B.
+// S is the staging area (STAGE doubles of LDS).  Each half's loads are in
+// flight for one half of products before they are written to LDS.  Ends
+// with a barrier, so S may be reused at once.
 template <typename FA, typename FB>
-__device__ __forceinline__ void block_gemm(doublex4 (&acc)[2][2], double* As, double* Bs, int t0, int t1,
-                                           FA srcA, FB srcB, bool neg, bool same) {
+__device__ __forceinline__ void block_gemm(doublex4 (&acc)[2][2], double* S, int t0, int t1, FA srcA, FB srcB,
+                                           bool neg, bool same) {
     if (t0 >= t1) return;
-    double ra[PER], rb[PER];
-    fetch(ra, srcA(t0));
-    if (!same) fetch(rb, srcB(t0));
+    double* A0 = S;
+    double* A1 = S + HB;
+    double* B0 = same ? A0 : S + 2 * HB;
+    double* B1 = same ? A1 : S + 3 * HB;
+    double ra0[HPER], rb0[HPER], ra1[HPER], rb1[HPER];
+    fetch_half(ra0, srcA(t0), 0);
+    if (!same) fetch_half(rb0, srcB(t0), 0);
+    fetch_half(ra1, srcA(t0), 1);
+    if (!same) fetch_half(rb1, srcB(t0), 1);
+    __syncthreads();   // earlier users of S are done
+    put_half(A0, ra0, srcA(t0).trans);
+    if (!same) put_half(B0, rb0, srcB(t0).trans);
+    __syncthreads();
     for (int t = t0; t < t1; ++t) {
-        const bool ta = srcA(t).trans;
-        const bool tb = same ? ta : srcB(t).trans;
-        __syncthreads();
-        put(As, ra, ta);
-        if (!same) put(Bs, rb, tb);
-        __syncthreads();
-        if (t + 1 < t1) {
-            fetch(ra, srcA(t + 1));
-            if (!same) fetch(rb, srcB(t + 1));
+        const bool more = t + 1 < t1;
+        // half 1 of step t into buffer 1; half 0 of step t + 1 in flight
+        put_half(A1, ra1, srcA(t).trans);
+        if (!same) put_half(B1, rb1, srcB(t).trans);
+        if (more) {
+            fetch_half(ra0, srcA(t + 1), 0);
+            if (!same) fetch_half(rb0, srcB(t + 1), 0);
         }
-        mma_block(acc, As, same ? As : Bs, neg);
+        mma_half(acc, A0, B0, neg);
+        __syncthreads();
+        // half 0 of step t + 1 into buffer 0; its half 1 in flight
+        if (more) {
+            put_half(A0, ra0, srcA(t + 1).trans);
+            if (!same) put_half(B0, rb0, srcB(t + 1).trans);
+            fetch_half(ra1, srcA(t + 1), 1);
+            if (!same) fetch_half(rb1, srcB(t + 1), 1);
+        }
+        mma_half(acc, A1, B1, neg);
+        __syncthreads();
     }
 }
 
@@ -442,84 +526,102 @@ __global__ __launch_bounds__(NT) void inv_prepare_kernel(InvLaunch L, int64_t ti
     }
 }
 
-// Step k of potrf, first half: every workgroup factors the diagonal block
-// (k, k) (already updated by the previous steps) and, when the matrix has
-// blocks to the right, solves one of them: U_kj = U_kk^-T W_kj.  The
-// workgroup of the first such block (or the only one) stores U_kk^-1 and the
-// failure code.
-__global__ __launch_bounds__(NT, 2) void inv_panel_trsm_kernel(InvLaunch L, int64_t tiles) {
-    __shared__ PanelScratch R;
-    __shared__ double As[B * LD];
-    __shared__ double Bs[B * LD];
-    int mi;
-    int64_t local;
-    if (!locate(L, kInvPanel, xcd_remap(blockIdx.x, gridDim.x), mi, local)) return;
-    const InvMat M = L.mats[mi];
+// Step k of potrf, row k.  The workgroup of block (k, j) first applies step
+// k-1's update to the diagonal block (k, k) and to its own block, then
+// factors the diagonal block and inverts its triangle (every row-k
+// workgroup of a matrix does so redundantly, so no launch boundary separates
+// the two), and solves U_kj = U_kk^-T W_kj.  The workgroup of the first such
+// block (or of the diagonal alone, in a matrix's last step) stores U_kk^-1
+// and the failure code.  Diagonal blocks of W are not written: later steps
+// read dinv.
+__device__ __forceinline__ void potrf_row_block(const InvLaunch& L, const InvMat& M, int64_t local, double* As,
+                                                double* Bs, PanelScratch& R) {
     const int k = L.step;
     const int64_t D = (int64_t)M.nb * B;
-    double* Wkk = M.w + (int64_t)k * B * D + (int64_t)k * B;
     const bool has_right = k + 1 < M.nb;
     const int J = k + 1 + (int)local;
-    double rb[PER];
-    if (has_right) fetch(rb, Blk{M.w + (int64_t)k * B * D + (int64_t)J * B, D, false});
-    {
-        double ra[PER];
-        fetch(ra, Blk{Wkk, D, false});
-        put(As, ra, false);
+    double* Wkk = M.w + (int64_t)k * B * D + (int64_t)k * B;
+    double* Wkj = M.w + (int64_t)k * B * D + (int64_t)J * B;
+    doublex4 dk[2][2], wj[2][2];
+    acc_load(dk, Wkk, D);
+    if (has_right) acc_load(wj, Wkj, D);
+    if (k > 0) {
+        const double* prev = M.w + (int64_t)(k - 1) * B * D;
+        double ra[PER], rb[PER];
+        fetch(ra, Blk{prev + (int64_t)k * B, D, true});
+        if (has_right) fetch(rb, Blk{prev + (int64_t)J * B, D, true});
+        put(As, ra, true);
+        if (has_right) put(Bs, rb, true);
+        __syncthreads();
+        mma_block(dk, As, As, true);
+        if (has_right) mma_block(wj, As, Bs, true);
+        __syncthreads();
     }
-    const int f = factor_diagonal(As, Bs, R);   // Bs: U_kk^-1 (As is scratch now)
-    // W_kk itself is left as it is: other workgroups of this launch read it,
-    // and no later step reads a diagonal block of W (they use dinv).
+    acc_to_lds(dk, Bs);
+    const int f = factor_diagonal(Bs, As, R);   // As: U_kk^-1
     if (local == 0) {
         const int r0 = threadIdx.x >> 6, c = threadIdx.x & 63;
 #pragma unroll
         for (int s = 0; s < PER; ++s) {
             const int r = r0 + 4 * s;
-            M.dinv[(int64_t)k * BB + r * B + c] = Bs[r * LD + c];
+            M.dinv[(int64_t)k * BB + r * B + c] = As[r * LD + c];
         }
         record_info(M, k, f);
     }
     if (!has_right) return;
-    // A[r][t] = Uinv_kk[t][r]: stage U_kk^-1 transposed over As, W_kj transposed in Bs
-    __syncthreads();
     {
         const int r0 = threadIdx.x >> 6, c = threadIdx.x & 63;
         double q[PER];
 #pragma unroll
-        for (int s = 0; s < PER; ++s) q[s] = Bs[(r0 + 4 * s) * LD + c];
+        for (int s = 0; s < PER; ++s) q[s] = As[(r0 + 4 * s) * LD + c];
         __syncthreads();
         put(As, q, true);
-        put(Bs, rb, true);
+        for_acc([&](int a, int b, int r, int row, int col) { Bs[col * LD + row] = wj[a][b][r]; });
     }
     __syncthreads();
     doublex4 acc[2][2];
     acc_zero(acc);
     mma_block(acc, As, Bs, false);
-    acc_store(acc, M.w + (int64_t)k * B * D + (int64_t)J * B, D);
+    acc_store(acc, Wkj, D);
 }
 
-// Step k of potrf, second half: trailing update W_ij -= U_ki^T U_kj.
-__global__ __launch_bounds__(NT) void inv_syrk_kernel(InvLaunch L, int64_t tiles) {
-    __shared__ double As[B * LD];
-    __shared__ double Bs[B * LD];
+// Step k of potrf with a look-ahead of one step.  Workgroups [0, split) are
+// the row-k blocks of every matrix, the critical path: they come first in
+// the dispatch and keep its order, so the hardware spreads them over the
+// XCDs.  Workgroups from tail_first (a multiple of 8, so that the XCD of a
+// workgroup is still its index mod 8) apply step k-1's update
+// W_ij -= U_{k-1,i}^T U_{k-1,j} to the blocks k < i <= j, XCD by XCD.
+__global__ __launch_bounds__(NT, 2) void inv_step_kernel(InvLaunch L, int64_t tiles) {
+    __shared__ PanelScratch R;
+    __shared__ double S[STAGE];
+    static_assert(STAGE >= 2 * B * LD, "two 64 x 64 blocks fit in the staging area");
+    double* As = S;
+    double* Bs = S + B * LD;
     int mi;
     int64_t local;
-    if (!locate(L, kInvSyrk, xcd_remap(blockIdx.x, gridDim.x), mi, local)) return;
+    const int64_t b = blockIdx.x;
+    if (b < L.split) {
+        if (!locate(L, kInvPanel, b, mi, local)) return;
+        potrf_row_block(L, L.mats[mi], local, As, Bs, R);
+        return;
+    }
+    if (b < L.tail_first) return;
+    const int64_t item = xcd_remap(b - L.tail_first, (int64_t)gridDim.x - L.tail_first);
+    if (!locate(L, kInvSyrk, item, mi, local)) return;
     const InvMat M = L.mats[mi];
     const int k = L.step;
     const int T = M.nb - k - 1;
-    int a, b;
-    upper_decode(local, T, a, b);
-    const int I = k + 1 + a, J = k + 1 + b;
+    int a, c;
+    upper_decode(local, T, a, c);
+    const int I = k + 1 + a, J = k + 1 + c;
     const int64_t D = (int64_t)M.nb * B;
     double* Wij = M.w + (int64_t)I * B * D + (int64_t)J * B;
-    const double* rowk = M.w + (int64_t)k * B * D;
+    const double* prev = M.w + (int64_t)(k - 1) * B * D;
     doublex4 acc[2][2];
     acc_load(acc, Wij, D);
-    // A[r][t] = U_ki[t][r], B[c][t] = U_kj[t][c]
-    block_gemm(acc, As, Bs, 0, 1,
-               [&](int) { return Blk{rowk + (int64_t)I * B, D, true}; },
-               [&](int) { return Blk{rowk + (int64_t)J * B, D, true}; }, true, I == J);
+    block_gemm(acc, S, 0, 1,
+               [&](int) { return Blk{prev + (int64_t)I * B, D, true}; },
+               [&](int) { return Blk{prev + (int64_t)J * B, D, true}; }, true, I == J);
     acc_store(acc, Wij, D);
 }
 
@@ -550,8 +652,7 @@ __device__ __forceinline__ void trtri_decode(int64_t local, int nb, int lvl, int
 
 // T_IJ = sum_{t in G2, t <= J} U_It V_tJ, parked in W's lower block (J, I).
 __global__ __launch_bounds__(NT) void inv_trtri_a_kernel(InvLaunch L, int64_t tiles) {
-    __shared__ double As[B * LD];
-    __shared__ double Bs[B * LD];
+    __shared__ double S[STAGE];
     int mi;
     int64_t local;
     if (!locate(L, kInvTrtri, xcd_remap(blockIdx.x, gridDim.x), mi, local)) return;
@@ -561,7 +662,7 @@ __global__ __launch_bounds__(NT) void inv_trtri_a_kernel(InvLaunch L, int64_t ti
     const int64_t D = (int64_t)M.nb * B;
     doublex4 acc[2][2];
     acc_zero(acc);
-    block_gemm(acc, As, Bs, g1_end, J + 1,
+    block_gemm(acc, S, g1_end, J + 1,
                [&](int t) { return Blk{M.w + (int64_t)I * B * D + (int64_t)t * B, D, false}; },   // U_It
                [&](int t) {                                                                     // V_tJ
                    return t == J ? Blk{M.dinv + (int64_t)J * BB, B, true}
@@ -573,8 +674,7 @@ __global__ __launch_bounds__(NT) void inv_trtri_a_kernel(InvLaunch L, int64_t ti
 
 // V_IJ = - sum_{t in G1, t >= I} V_It T_tJ, written over U_IJ.
 __global__ __launch_bounds__(NT) void inv_trtri_b_kernel(InvLaunch L, int64_t tiles) {
-    __shared__ double As[B * LD];
-    __shared__ double Bs[B * LD];
+    __shared__ double S[STAGE];
     int mi;
     int64_t local;
     if (!locate(L, kInvTrtri, xcd_remap(blockIdx.x, gridDim.x), mi, local)) return;
@@ -584,7 +684,7 @@ __global__ __launch_bounds__(NT) void inv_trtri_b_kernel(InvLaunch L, int64_t ti
     const int64_t D = (int64_t)M.nb * B;
     doublex4 acc[2][2];
     acc_zero(acc);
-    block_gemm(acc, As, Bs, I, g1_end,
+    block_gemm(acc, S, I, g1_end,
                [&](int t) {                                                                     // V_It
                    return t == I ? Blk{M.dinv + (int64_t)I * BB, B, false}
                                  : Blk{M.w + (int64_t)I * B * D + (int64_t)t * B, D, false};
@@ -596,8 +696,9 @@ __global__ __launch_bounds__(NT) void inv_trtri_b_kernel(InvLaunch L, int64_t ti
 
 // Z_IJ = sum_{t >= J} V_It V_Jt^T for I <= J; float32 out, both triangles.
 __global__ __launch_bounds__(NT) void inv_lauum_kernel(InvLaunch L, int64_t tiles) {
-    __shared__ double As[B * LD];
-    __shared__ double Bs[B * LD];
+    __shared__ double S[STAGE];
+    static_assert(STAGE >= B * LD, "the output is transposed through the staging area");
+    double* As = S;
     int mi;
     int64_t local;
     if (!locate(L, kInvLauum, xcd_remap(blockIdx.x, gridDim.x), mi, local)) return;
@@ -614,7 +715,7 @@ __global__ __launch_bounds__(NT) void inv_lauum_kernel(InvLaunch L, int64_t tile
         return t == row ? Blk{M.dinv + (int64_t)row * BB, B, false}
                         : Blk{M.w + (int64_t)row * B * D + (int64_t)t * B, D, false};
     };
-    block_gemm(acc, As, Bs, J, M.nb, [&](int t) { return V(I, t); }, [&](int t) { return V(J, t); }, false,
+    block_gemm(acc, S, J, M.nb, [&](int t) { return V(I, t); }, [&](int t) { return V(J, t); }, false,
                I == J);
     __syncthreads();
     acc_to_lds(acc, As);
@@ -650,8 +751,7 @@ hipError_t launch(K kernel, const InvLaunch& L, int64_t tiles, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_inv_prepare(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_prepare_kernel, L, t, s); }
-hipError_t launch_inv_panel_trsm(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_panel_trsm_kernel, L, t, s); }
-hipError_t launch_inv_syrk(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_syrk_kernel, L, t, s); }
+hipError_t launch_inv_step(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_step_kernel, L, t, s); }
 hipError_t launch_inv_trtri_a(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_trtri_a_kernel, L, t, s); }
 hipError_t launch_inv_trtri_b(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_trtri_b_kernel, L, t, s); }
 hipError_t launch_inv_lauum(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_lauum_kernel, L, t, s); }

@@ -394,12 +394,16 @@ kfac_status_t kfac_damped_inverse(int n, const float* const* x, const int64_t* d
     if (e == hipSuccess) e = upload_table(buckets_dev, p.buckets.data(), sizeof(InvBucket) * p.buckets.size(), stream);
     if (e != hipSuccess) return KFAC_ERR_HIP;
 
-    InvLaunch L{mats_dev, buckets_dev, (int32_t)p.buckets.size(), 0, (double)gamma};
+    InvLaunch L{mats_dev, buckets_dev, (int32_t)p.buckets.size(), 0, (double)gamma, 0, 0};
     e = launch_inv_prepare(L, bucket_tiles(p, kInvPrepare, 0), stream);
     for (int k = 0; e == hipSuccess && k < p.nbmax; ++k) {
+        // row-k blocks of every matrix in the first workgroups (spread over the
+        // XCDs as dispatched), then the trailing update from a multiple of 8
         L.step = k;
-        e = launch_inv_panel_trsm(L, bucket_tiles(p, kInvPanel, k), stream);
-        if (e == hipSuccess && k + 1 < p.nbmax) e = launch_inv_syrk(L, bucket_tiles(p, kInvSyrk, k), stream);
+        L.split = bucket_tiles(p, kInvPanel, k);
+        const int64_t trail = bucket_tiles(p, kInvSyrk, k);
+        L.tail_first = trail > 0 ? (L.split + 7) / 8 * 8 : L.split;
+        e = launch_inv_step(L, L.tail_first + trail, stream);
     }
     for (int lvl = 1; e == hipSuccess && (1 << (lvl - 1)) < p.nbmax; ++lvl) {
         L.step = lvl;
