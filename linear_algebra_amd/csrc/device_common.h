@@ -21,6 +21,17 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t count) {
     return x * q + (x < r ? x : r) + local;
 }
 
+// For launches whose items differ in cost (long and short products), a
+// contiguous range per XCD leaves some XCDs with far more work than others.
+// Here the XCDs take runs of C consecutive items in turn (XCD x gets runs x,
+// x + 8, ...), which keeps neighbours together and balances the load.  The
+// grid must be a multiple of 8 C; it is a bijection on [0, gridDim.x).
+template <int C>
+__device__ __forceinline__ int64_t xcd_runs(int64_t b) {
+    const int64_t x = b & 7, local = b >> 3;
+    return ((local / C) * 8 + x) * C + local % C;
+}
+
 // Row-major enumeration of the upper triangle (i <= j) of a T x T grid:
 // row i holds T - i entries.  t in [0, T(T+1)/2).
 __device__ __forceinline__ void upper_decode(int64_t t, int64_t T, int& i, int& j) {

@@ -42,6 +42,7 @@ constexpr int LD = B + 1;      // LDS row stride in doubles (conflict-free colum
 constexpr int NT = kInvThreads;
 constexpr int BB = B * B;
 constexpr int PER = BB / NT;   // block elements per thread (16)
+constexpr int kRun = 16;       // items per XCD run in launches of uneven items (trtri, lauum)
 
 // Which matrix and which of its tiles a workgroup owns.
 __device__ __forceinline__ bool locate(const InvLaunch& L, int kind, int64_t tile, int& mat, int64_t& local) {
@@ -655,7 +656,8 @@ __global__ __launch_bounds__(NT) void inv_trtri_a_kernel(InvLaunch L, int64_t ti
     __shared__ double S[STAGE];
     int mi;
     int64_t local;
-    if (!locate(L, kInvTrtri, xcd_remap(blockIdx.x, gridDim.x), mi, local)) return;
+    const int64_t item = xcd_runs<kRun>(blockIdx.x);
+    if (item >= tiles || !locate(L, kInvTrtri, item, mi, local)) return;
     const InvMat M = L.mats[mi];
     int I, J, g1_end;
     trtri_decode(local, M.nb, L.step, I, J, g1_end);
@@ -677,7 +679,8 @@ __global__ __launch_bounds__(NT) void inv_trtri_b_kernel(InvLaunch L, int64_t ti
     __shared__ double S[STAGE];
     int mi;
     int64_t local;
-    if (!locate(L, kInvTrtri, xcd_remap(blockIdx.x, gridDim.x), mi, local)) return;
+    const int64_t item = xcd_runs<kRun>(blockIdx.x);
+    if (item >= tiles || !locate(L, kInvTrtri, item, mi, local)) return;
     const InvMat M = L.mats[mi];
     int I, J, g1_end;
     trtri_decode(local, M.nb, L.step, I, J, g1_end);
@@ -701,7 +704,8 @@ __global__ __launch_bounds__(NT) void inv_lauum_kernel(InvLaunch L, int64_t tile
     double* As = S;
     int mi;
     int64_t local;
-    if (!locate(L, kInvLauum, xcd_remap(blockIdx.x, gridDim.x), mi, local)) return;
+    const int64_t item = xcd_runs<kRun>(blockIdx.x);
+    if (item >= tiles || !locate(L, kInvLauum, item, mi, local)) return;
     const InvMat M = L.mats[mi];
     // column by column over the upper blocks (J ascending, I = 0..J): the
     // longest products (small J) start first, and tiles that run side by side
@@ -742,9 +746,10 @@ __global__ __launch_bounds__(NT) void inv_lauum_kernel(InvLaunch L, int64_t tile
 }
 
 template <typename K>
-hipError_t launch(K kernel, const InvLaunch& L, int64_t tiles, hipStream_t s) {
+hipError_t launch(K kernel, const InvLaunch& L, int64_t tiles, hipStream_t s, bool runs = false) {
     if (tiles <= 0) return hipSuccess;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)tiles), dim3(NT), 0, s, L, tiles);
+    const int64_t grid = runs ? (tiles + 8 * kRun - 1) / (8 * kRun) * (8 * kRun) : tiles;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(NT), 0, s, L, tiles);
     return hipGetLastError();
 }
 
@@ -752,8 +757,8 @@ hipError_t launch(K kernel, const InvLaunch& L, int64_t tiles, hipStream_t s) {
 
 hipError_t launch_inv_prepare(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_prepare_kernel, L, t, s); }
 hipError_t launch_inv_step(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_step_kernel, L, t, s); }
-hipError_t launch_inv_trtri_a(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_trtri_a_kernel, L, t, s); }
-hipError_t launch_inv_trtri_b(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_trtri_b_kernel, L, t, s); }
-hipError_t launch_inv_lauum(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_lauum_kernel, L, t, s); }
+hipError_t launch_inv_trtri_a(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_trtri_a_kernel, L, t, s, true); }
+hipError_t launch_inv_trtri_b(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_trtri_b_kernel, L, t, s, true); }
+hipError_t launch_inv_lauum(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_lauum_kernel, L, t, s, true); }
 
 }  // namespace kfac
