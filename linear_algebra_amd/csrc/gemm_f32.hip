@@ -27,6 +27,8 @@ namespace {
 constexpr int BM = kGemmTile;
 constexpr int BK = kGemmBK;
 constexpr int NT = kGemmThreads;
+constexpr int kGemmRun = 16;        // items per XCD run in large launches
+constexpr int64_t kGemmRunsMin = 2048;
 constexpr int LOADS = BK * BM / NT;  // elements of one operand slab per thread (8)
 constexpr int SUB_STAGES = kGemmSubK / BK;
 
@@ -148,7 +150,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_tn_kernel(GemmLaunch L, int64_t it
     __shared__ __attribute__((aligned(16))) float As[2][BM * LDK];
     __shared__ __attribute__((aligned(16))) float Bs[2][BM * LDK];
 
-    const int64_t item = xcd_remap(blockIdx.x, gridDim.x);
+    const int64_t item = L.runs ? xcd_runs<kGemmRun>(blockIdx.x) : xcd_remap(blockIdx.x, gridDim.x);
     if (item >= items) return;
     const TileWork W = decode_item(L, item);
     const GemmProb& P = W.P;
@@ -282,7 +284,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_tn_bf16_kernel(GemmLaunch L, int64
     __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDK16];
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BM * LDK16];
 
-    const int64_t item = xcd_remap(blockIdx.x, gridDim.x);
+    const int64_t item = L.runs ? xcd_runs<kGemmRun>(blockIdx.x) : xcd_remap(blockIdx.x, gridDim.x);
     if (item >= items) return;
     const TileWork W = decode_item(L, item);
     const GemmProb& P = W.P;
@@ -432,10 +434,18 @@ __global__ __launch_bounds__(NT) void gemm_reduce_kernel(GemmLaunch L, int64_t s
 
 hipError_t launch_gemm(const GemmLaunch& L, int64_t items, hipStream_t stream, bool bf16) {
     if (items <= 0) return hipSuccess;
+    // Items of different problems differ in cost (K chunks of different
+    // length, diagonal tiles with an idle wave).  Large launches hand items to
+    // the XCDs in runs, so that no XCD gets a range of only expensive ones;
+    // small launches (fewer items than a few rounds of the chip) keep one
+    // contiguous range per XCD.
+    GemmLaunch R = L;
+    R.runs = items >= kGemmRunsMin ? 1 : 0;
+    const int64_t grid = R.runs ? (items + 8 * kGemmRun - 1) / (8 * kGemmRun) * (8 * kGemmRun) : items;
     if (bf16) {
-        hipLaunchKernelGGL(gemm_tn_bf16_kernel, dim3((unsigned)items), dim3(NT), 0, stream, L, items);
+        hipLaunchKernelGGL(gemm_tn_bf16_kernel, dim3((unsigned)grid), dim3(NT), 0, stream, R, items);
     } else {
-        hipLaunchKernelGGL(gemm_tn_kernel<false>, dim3((unsigned)items), dim3(NT), 0, stream, L, items);
+        hipLaunchKernelGGL(gemm_tn_kernel<false>, dim3((unsigned)grid), dim3(NT), 0, stream, R, items);
     }
     return hipGetLastError();
 }

@@ -59,7 +59,7 @@ struct GemmLaunch {
     int32_t nprob;
     int32_t first_step;
     float eps;
-    int32_t pad_;
+    int32_t runs;         // set by launch_gemm: items go to XCDs in runs (large launches)
 };
 
 hipError_t launch_gemm(const GemmLaunch& L, int64_t items, hipStream_t stream, bool bf16);
