@@ -119,6 +119,15 @@ struct InvLaunch {
 // sizes the grids, and the kernels, which decode their tile index.
 enum InvKind : int32_t { kInvPrepare = 0, kInvPanel = 1, kInvSyrk = 2, kInvTrtri = 3, kInvLauum = 4 };
 
+// Groups of 2^l blocks leave a last level that joins almost all blocks with
+// a handful when nb is just above a power of two (33 = 32 + 1): a few long
+// products on a nearly idle chip.  Such matrices use a balanced binary tree.
+__host__ __device__ inline bool trtri_balanced(int64_t nb) {
+    int64_t p = 1;
+    while (2 * p < nb) p *= 2;          // p < nb <= 2p
+    return nb > 2 && nb - p <= p / 8;
+}
+
 __host__ __device__ inline int64_t inv_tiles(int kind, int64_t nb, int64_t step) {
     switch (kind) {
         case kInvPrepare:
@@ -131,8 +140,18 @@ __host__ __device__ inline int64_t inv_tiles(int kind, int64_t nb, int64_t step)
             return step >= 1 && t > 0 ? t * (t + 1) / 2 : 0;
         }
         case kInvTrtri: {
-            // level >= 1 joins pairs of groups of h = 2^(level-1) blocks
-            const int64_t h = int64_t(1) << (step - 1), g = 2 * h;
+            // launch `step` (0 = bottom) serves level step + 1 of groups of
+            // 2^l blocks, or, for nb just above a power of two, depth
+            // D - 1 - step of the balanced tree (D = ceil(log2 nb))
+            int D = 0;
+            while ((int64_t(1) << D) < nb) ++D;
+            if (step >= D) return 0;
+            if (trtri_balanced(nb)) {
+                const int d = D - 1 - (int)step;
+                const int64_t s2 = (nb + (int64_t(1) << (d + 1)) - 1) >> (d + 1);
+                return (int64_t(1) << d) * s2 * s2;
+            }
+            const int64_t h = int64_t(1) << step, g = 2 * h;
             const int64_t full = nb / g, rem = nb % g;
             return full * h * h + (rem > h ? h * (rem - h) : 0);
         }

@@ -14,11 +14,13 @@
 //                         U_kj = U_kk^-T W_kj           (j > k)
 //               trailing  W_ij -= U_{k-1,i}^T U_{k-1,j} (k < i <= j), in
 //                         the same launch, beside the row-k workgroups;
-//   trtri     V = U^-1 by recursive doubling over groups of blocks: for
-//             sibling groups G1, G2 (G1 before G2)
+//   trtri     V = U^-1 by recursive doubling over groups of blocks, from the
+//             leaves up: for sibling groups G1, G2 (G1 before G2)
 //               V_12 = -V_11 . (U_12 . V_22)
-//             two launches per level, log2(nb) levels; the inner product is
-//             parked in the unused lower triangle of W;
+//             two launches per level, ceil(log2(nb)) levels; the groups are
+//             runs of 2^l blocks, or a balanced binary tree when nb is just
+//             above a power of two; the inner product is parked in the
+//             unused lower triangle of W;
 //   lauum     Z = V V^T (upper blocks), written as float32 to both triangles.
 //
 // Diagonal blocks of V are the inverses of the diagonal blocks of U, kept in
@@ -626,11 +628,32 @@ __global__ __launch_bounds__(NT, 2) void inv_step_kernel(InvLaunch L, int64_t ti
     acc_store(acc, Wij, D);
 }
 
-// Tile of level `lvl` of the doubling: group m joins G1 = [m*2h, m*2h + h)
-// and G2 = [m*2h + h, min(m*2h + 2h, nb)); the tile is block (I, J),
-// I in G1, J in G2.
-__device__ __forceinline__ void trtri_decode(int64_t local, int nb, int lvl, int& I, int& J, int& g1_end) {
-    const int h = 1 << (lvl - 1), g = 2 * h;
+// Slot `local` of trtri launch `step` (0 = bottom) of a matrix of nb blocks.
+// Groups of 2^l blocks: level l = step + 1 joins G1 = [m*2h, m*2h + h) and
+// G2 = [m*2h + h, min(m*2h + 2h, nb)), h = 2^step.  Balanced tree (nb just
+// above a power of two): depth d = D - 1 - step, node n covers
+// [n nb / 2^d, (n + 1) nb / 2^d) and joins its children G1 = [lo, mid),
+// G2 = [mid, hi) in s2 x s2 slots, of which those beyond |G1| x |G2| have
+// no work.  The slot is block (I, J), I in G1, J in G2.
+__device__ __forceinline__ bool trtri_decode(int64_t local, int nb, int step, int& I, int& J, int& g1_end) {
+    if (trtri_balanced(nb)) {
+        int D = 0;
+        while ((1 << D) < nb) ++D;
+        const int d = D - 1 - step;
+        const int s2 = (nb + (1 << (d + 1)) - 1) >> (d + 1);
+        const int n = (int)(local / ((int64_t)s2 * s2));
+        const int r = (int)(local % ((int64_t)s2 * s2));
+        const int bi = r / s2, bj = r % s2;
+        const int lo = (int)(((int64_t)n * nb) >> d);
+        const int mid = (int)(((int64_t)(2 * n + 1) * nb) >> (d + 1));
+        const int hi = (int)(((int64_t)(n + 1) * nb) >> d);
+        if (bi >= mid - lo || bj >= hi - mid) return false;
+        I = lo + bi;
+        J = mid + bj;
+        g1_end = mid;
+        return true;
+    }
+    const int h = 1 << step, g = 2 * h;
     const int full = nb / g;
     const int64_t hh = (int64_t)h * h;
     int m, bi, bj;
@@ -649,6 +672,7 @@ __device__ __forceinline__ void trtri_decode(int64_t local, int nb, int lvl, int
     I = m * g + bi;
     J = m * g + h + bj;
     g1_end = m * g + h;
+    return true;
 }
 
 // T_IJ = sum_{t in G2, t <= J} U_It V_tJ, parked in W's lower block (J, I).
@@ -660,7 +684,7 @@ __global__ __launch_bounds__(NT) void inv_trtri_a_kernel(InvLaunch L, int64_t ti
     if (item >= tiles || !locate(L, kInvTrtri, item, mi, local)) return;
     const InvMat M = L.mats[mi];
     int I, J, g1_end;
-    trtri_decode(local, M.nb, L.step, I, J, g1_end);
+    if (!trtri_decode(local, M.nb, L.step, I, J, g1_end)) return;
     const int64_t D = (int64_t)M.nb * B;
     doublex4 acc[2][2];
     acc_zero(acc);
@@ -683,7 +707,7 @@ __global__ __launch_bounds__(NT) void inv_trtri_b_kernel(InvLaunch L, int64_t ti
     if (item >= tiles || !locate(L, kInvTrtri, item, mi, local)) return;
     const InvMat M = L.mats[mi];
     int I, J, g1_end;
-    trtri_decode(local, M.nb, L.step, I, J, g1_end);
+    if (!trtri_decode(local, M.nb, L.step, I, J, g1_end)) return;
     const int64_t D = (int64_t)M.nb * B;
     doublex4 acc[2][2];
     acc_zero(acc);

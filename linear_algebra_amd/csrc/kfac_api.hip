@@ -405,7 +405,7 @@ kfac_status_t kfac_damped_inverse(int n, const float* const* x, const int64_t* d
         L.tail_first = trail > 0 ? (L.split + 7) / 8 * 8 : L.split;
         e = launch_inv_step(L, L.tail_first + trail, stream);
     }
-    for (int lvl = 1; e == hipSuccess && (1 << (lvl - 1)) < p.nbmax; ++lvl) {
+    for (int lvl = 0; e == hipSuccess && (1 << lvl) < p.nbmax; ++lvl) {   // bottom level first
         L.step = lvl;
         const int64_t t = bucket_tiles(p, kInvTrtri, lvl);
         e = launch_inv_trtri_a(L, t, stream);
