@@ -117,7 +117,7 @@ struct InvLaunch {
 // Tiles each inverse kernel needs per matrix with nb blocks per edge at a
 // given potrf step (trsm, syrk) or trtri level.  Shared by the host, which
 // sizes the grids, and the kernels, which decode their tile index.
-enum InvKind : int32_t { kInvPrepare = 0, kInvPanel = 1, kInvSyrk = 2, kInvTrtri = 3, kInvLauum = 4 };
+enum InvKind : int32_t { kInvPrepare = 0, kInvPanel = 1, kInvSyrk = 2, kInvTrtri = 3, kInvLauum = 4, kInvLauum2 = 5 };
 
 // Groups of 2^l blocks leave a last level that joins almost all blocks with
 // a handful when nb is just above a power of two (33 = 32 + 1): a few long
@@ -133,6 +133,10 @@ __host__ __device__ inline int64_t inv_tiles(int kind, int64_t nb, int64_t step)
         case kInvPrepare:
         case kInvLauum:
             return nb * (nb + 1) / 2;
+        case kInvLauum2: {  // 2 x 2 groups of blocks, upper triangle
+            const int64_t n2 = (nb + 1) / 2;
+            return n2 * (n2 + 1) / 2;
+        }
         case kInvPanel:  // one workgroup per block right of the diagonal, at least one
             return nb > step ? (nb - step - 1 > 1 ? nb - step - 1 : 1) : 0;
         case kInvSyrk: {  // step k applies step k-1's update to blocks (i, j), k < i <= j
@@ -165,5 +169,6 @@ hipError_t launch_inv_step(const InvLaunch& L, int64_t tiles, hipStream_t s);
 hipError_t launch_inv_trtri_a(const InvLaunch& L, int64_t tiles, hipStream_t s);
 hipError_t launch_inv_trtri_b(const InvLaunch& L, int64_t tiles, hipStream_t s);
 hipError_t launch_inv_lauum(const InvLaunch& L, int64_t tiles, hipStream_t s);
+hipError_t launch_inv_lauum2(const InvLaunch& L, int64_t tiles, hipStream_t s);
 
 }  // namespace kfac

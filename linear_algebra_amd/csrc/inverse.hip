@@ -215,6 +215,144 @@ __device__ __forceinline__ void block_gemm(doublex4 (&acc)[2][2], double* S, int
     }
 }
 
+// ---- 128 x 128 output tiles --------------------------------------------
+// A workgroup computes a 2 x 2 group of output blocks, wave (a, b) block
+// (a, b), from panels of two stacked 64 x 64 blocks.  Per flop this loads half
+// as many bytes from memory and writes half as many to LDS as 64 x 64 tiles.
+// The panels are staged in quarters of 16 k-columns, double buffered, which
+// keeps two workgroups on a CU.
+constexpr int KQ = 16;                // k-columns per staged quarter
+constexpr int LDQ = KQ + 1;           // LDS row stride of a staged quarter (doubles)
+constexpr int QB = 2 * B * LDQ;       // doubles per staged panel quarter (128 rows)
+constexpr int QPER = 2 * B * KQ / NT; // panel-quarter elements per thread (8)
+constexpr int STAGE2 = 4 * QB;        // LDS doubles of the staging area
+
+// Two 64 x 64 blocks stacked into a 128-row panel (in the [m][k] convention
+// of Blk); a block flagged zero is staged as zeros and not read.
+struct Panel {
+    Blk blk[2];
+    bool zero[2];
+};
+
+__device__ __forceinline__ void fetch_quarter(double (&v)[QPER], const Panel& P, int q) {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const Blk& b = P.blk[h];
+        if (P.zero[h]) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) v[4 * h + s] = 0.0;
+        } else if (!b.trans) {
+            const int c = KQ * q + (t & 15), r = t >> 4;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) v[4 * h + s] = b.p[(int64_t)(r + 16 * s) * b.ld + c];
+        } else {
+            const int c = t & 63, r = KQ * q + (t >> 6);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) v[4 * h + s] = b.p[(int64_t)(r + 4 * s) * b.ld + c];
+        }
+    }
+}
+__device__ __forceinline__ void put_quarter(double* S, const double (&v)[QPER], const Panel& P) {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        if (P.zero[h] || !P.blk[h].trans) {
+            const int k = t & 15, m = B * h + (t >> 4);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) S[(m + 16 * s) * LDQ + k] = v[4 * h + s];
+        } else {
+            const int m = B * h + (t & 63), k = t >> 6;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) S[m * LDQ + k + 4 * s] = v[4 * h + s];
+        }
+    }
+}
+
+// acc[i][j] += (neg ? -1 : 1) sum_k A[64a + 16i + .][k] B[64b + 16j + .][k]
+// over one staged quarter: wave (a, b) computes its whole 64 x 64 block as
+// 4 x 4 blocks of v_mfma_f64_16x16x4f64.
+__device__ __forceinline__ void mma_quarter(doublex4 (&acc)[4][4], const double* SA, const double* SB, int a, int b,
+                                            bool neg) {
+    const int lane = threadIdx.x & 63, li = lane & 15, lk = lane >> 4;
+    const double* ap = SA + (B * a + li) * LDQ + lk;
+    const double* bp = SB + (B * b + li) * LDQ + lk;
+#pragma unroll
+    for (int k0 = 0; k0 < KQ; k0 += 4) {
+        double av[4], bv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            av[i] = ap[16 * i * LDQ + k0];
+            if (neg) av[i] = -av[i];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bv[j] = bp[16 * j * LDQ + k0];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[i], bv[j], acc[i][j], 0, 0, 0);
+    }
+}
+
+// acc += (neg ? -1 : 1) sum_{t in [t0, t1)} PA_t PB_t^T restricted to wave
+// (a, b)'s block, PA_t = panelA(t) and PB_t = panelB(t); `same` reuses the A
+// panel for B; a wave with `active` false stages but skips its products.
+// Ends with a barrier.
+template <typename FA, typename FB>
+__device__ __forceinline__ void panel_gemm(doublex4 (&acc)[4][4], double* S, int t0, int t1, FA panelA, FB panelB,
+                                           bool neg, bool same, int a, int b, bool active) {
+    if (t0 >= t1) return;
+    double* A0 = S;
+    double* A1 = S + QB;
+    double* B0 = same ? A0 : S + 2 * QB;
+    double* B1 = same ? A1 : S + 3 * QB;
+    const int H = 4 * (t1 - t0);   // quarters, even
+    double ra0[QPER], rb0[QPER], ra1[QPER], rb1[QPER];
+    // quarter h of the run: step t0 + h / 4, k-quarter h % 4
+    fetch_quarter(ra0, panelA(t0), 0);
+    if (!same) fetch_quarter(rb0, panelB(t0), 0);
+    fetch_quarter(ra1, panelA(t0), 1);
+    if (!same) fetch_quarter(rb1, panelB(t0), 1);
+    __syncthreads();   // earlier users of S are done
+    put_quarter(A0, ra0, panelA(t0));
+    if (!same) put_quarter(B0, rb0, panelB(t0));
+    __syncthreads();
+    for (int h = 0; h < H; h += 2) {
+        const int t1q = t0 + ((h + 1) >> 2), t2 = t0 + ((h + 2) >> 2), t3 = t0 + ((h + 3) >> 2);
+        // quarter h + 1 into buffer 1; quarter h + 2 in flight
+        put_quarter(A1, ra1, panelA(t1q));
+        if (!same) put_quarter(B1, rb1, panelB(t1q));
+        if (h + 2 < H) {
+            fetch_quarter(ra0, panelA(t2), (h + 2) & 3);
+            if (!same) fetch_quarter(rb0, panelB(t2), (h + 2) & 3);
+        }
+        if (active) mma_quarter(acc, A0, B0, a, b, neg);
+        __syncthreads();
+        // quarter h + 2 into buffer 0; quarter h + 3 in flight
+        if (h + 2 < H) {
+            put_quarter(A0, ra0, panelA(t2));
+            if (!same) put_quarter(B0, rb0, panelB(t2));
+            fetch_quarter(ra1, panelA(t3), (h + 3) & 3);
+            if (!same) fetch_quarter(rb1, panelB(t3), (h + 3) & 3);
+        }
+        if (active) mma_quarter(acc, A1, B1, a, b, neg);
+        __syncthreads();
+    }
+}
+
+// 16 x 16 block (i, j) of a wave's 64 x 64 block: lane l holds column
+// 16 j + l % 16 and rows 16 i + l / 16 + 4 r.
+template <typename F>
+__device__ __forceinline__ void for_acc4(F&& f) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) f(i, j, r, 16 * i + (lane >> 4) + 4 * r, 16 * j + (lane & 15));
+}
+
 // Output layout of a 16 x 16 f64 MFMA block (checked on gfx950): lane l holds
 // column l % 16 and rows l/16 + 4*r for its four registers r.  (The f32
 // 16 x 16 blocks use rows 4*(l/16) + r instead.)
@@ -769,6 +907,63 @@ __global__ __launch_bounds__(NT) void inv_lauum_kernel(InvLaunch L, int64_t tile
     }
 }
 
+// Z = V V^T on 2 x 2 groups of blocks: group (I2, J2), I2 <= J2, holds the
+// blocks (2 I2 + a, 2 J2 + b); wave (a, b) owns one, summing over t >= 2 J2.
+// Blocks of V below the diagonal are zero (their storage holds trtri's
+// parked products) and are staged as zeros; in a diagonal group the wave of
+// the block below the diagonal computes nothing (its block is the mirror).
+// float32 out, both triangles, mirrored through LDS.
+__global__ __launch_bounds__(NT, 2) void inv_lauum2_kernel(InvLaunch L, int64_t tiles) {
+    __shared__ double S[STAGE2];
+    static_assert(STAGE2 * 2 >= 4 * B * (B + 1), "the four blocks are mirrored through the staging area");
+    int mi;
+    int64_t local;
+    const int64_t item = xcd_runs<kRun>(blockIdx.x);
+    if (item >= tiles || !locate(L, kInvLauum2, item, mi, local)) return;
+    const InvMat M = L.mats[mi];
+    int I2, J2;
+    column_decode(local, I2, J2);
+    const int nb = M.nb;
+    const int64_t D = (int64_t)nb * B, d = M.d;
+    const int w = threadIdx.x >> 6, a = w >> 1, b = w & 1;
+    const int I = 2 * I2 + a, J = 2 * J2 + b;
+    const bool active = I < nb && J < nb && !(I2 == J2 && a > b);
+    auto V = [&](int row, int t) {
+        if (row >= nb || t < row) return Blk{M.w, D, false};
+        return t == row ? Blk{M.dinv + (int64_t)row * BB, B, false}
+                        : Blk{M.w + (int64_t)row * B * D + (int64_t)t * B, D, false};
+    };
+    auto panel = [&](int r0, int t) {
+        return Panel{{V(r0, t), V(r0 + 1, t)}, {r0 >= nb || t < r0, r0 + 1 >= nb || t < r0 + 1}};
+    };
+    doublex4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = doublex4{0.0, 0.0, 0.0, 0.0};
+    panel_gemm(acc, S, 2 * J2, nb, [&](int t) { return panel(2 * I2, t); }, [&](int t) { return panel(2 * J2, t); },
+               false, I2 == J2, a, b, active);
+    // each wave's block as float32 in LDS, then written with coalesced rows
+    float* F = reinterpret_cast<float*>(S) + w * B * (B + 1);
+    for_acc4([&](int i, int j, int r, int row, int col) { F[row * (B + 1) + col] = (float)acc[i][j][r]; });
+    __syncthreads();
+    if (!active) return;
+    const int64_t r0 = (int64_t)I * B, c0 = (int64_t)J * B;
+    const int l = threadIdx.x & 63;
+    for (int r = 0; r < B; ++r) {
+        const int c = l;
+        const int64_t i = r0 + r, j = c0 + c;
+        if (i < d && j < d) M.z[i * d + j] = (I != J || c >= r) ? F[r * (B + 1) + c] : F[c * (B + 1) + r];
+    }
+    if (I != J) {
+        for (int c = 0; c < B; ++c) {
+            const int r = l;   // destination row c0 + c, column r0 + r
+            const int64_t i = c0 + c, j = r0 + r;
+            if (i < d && j < d) M.z[i * d + j] = F[r * (B + 1) + c];
+        }
+    }
+}
+
 template <typename K>
 hipError_t launch(K kernel, const InvLaunch& L, int64_t tiles, hipStream_t s, bool runs = false) {
     if (tiles <= 0) return hipSuccess;
@@ -784,5 +979,6 @@ hipError_t launch_inv_step(const InvLaunch& L, int64_t t, hipStream_t s) { retur
 hipError_t launch_inv_trtri_a(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_trtri_a_kernel, L, t, s, true); }
 hipError_t launch_inv_trtri_b(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_trtri_b_kernel, L, t, s, true); }
 hipError_t launch_inv_lauum(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_lauum_kernel, L, t, s, true); }
+hipError_t launch_inv_lauum2(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_lauum2_kernel, L, t, s, true); }
 
 }  // namespace kfac

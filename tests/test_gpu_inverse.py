@@ -240,3 +240,30 @@ def test_inverse_max_dimension_8192():
     for q in range(len(cols)):
         bound = 64 * 2.0 ** -24 * np.linalg.norm(xd, 1) * np.abs(z[:, cols[q]]).sum()
         assert np.abs(res[:, q]).max() <= bound
+
+
+def test_inverse_many_ragged_matrices():
+    """Seventy factors of ragged sizes (odd and even block counts, sizes one
+    off a multiple of 64) in one call: enough 2 x 2 groups of blocks
+    (sum over matrices of n2 (n2 + 1) / 2 with n2 = ceil(ceil(d / 64) / 2),
+    at least 1024) for the product V V^T to run on 128 x 128 tiles.  Every
+    matrix against the oracle in full."""
+    rng = np.random.default_rng(70)
+    edge = [1, 2, 63, 64, 65, 127, 128, 129, 191, 192, 193, 1023, 1025]
+    dims = edge + [int(x) for x in rng.integers(100, 1400, 70 - len(edge))]
+    groups = sum(((d + 127) // 128) * ((d + 127) // 128 + 1) // 2 for d in dims)
+    assert groups >= 1024, groups
+    gamma = np.float32(1e-3)
+    xs = [spd_f32(rng, d, max(1, d // 2)) for d in dims]
+    say("inverse 70 ragged matrices, groups", groups)
+    zs, info = gpu_inverse(xs, gamma)
+    assert np.all(info == 0), info
+    worst = 0.0
+    for x, z in zip(xs, zs):
+        ref, rinfo = oracle.damped_inverse(x, gamma)
+        assert rinfo == 0
+        err = rel_fro(z, ref)
+        worst = max(worst, err)
+        assert err <= TOL, (x.shape[0], err)
+        np.testing.assert_array_equal(z, z.T)
+    say(f"70 ragged matrices: worst rel err {worst:.3e}")
