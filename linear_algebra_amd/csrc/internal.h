@@ -117,7 +117,9 @@ struct InvLaunch {
 // Tiles each inverse kernel needs per matrix with nb blocks per edge at a
 // given potrf step (trsm, syrk) or trtri level.  Shared by the host, which
 // sizes the grids, and the kernels, which decode their tile index.
-enum InvKind : int32_t { kInvPrepare = 0, kInvPanel = 1, kInvSyrk = 2, kInvTrtri = 3, kInvLauum = 4, kInvLauum2 = 5 };
+enum InvKind : int32_t {
+    kInvPrepare = 0, kInvPanel = 1, kInvSyrk = 2, kInvTrtri = 3, kInvLauum = 4, kInvLauum2 = 5
+};
 
 // Groups of 2^l blocks leave a last level that joins almost all blocks with
 // a handful when nb is just above a power of two (33 = 32 + 1): a few long

@@ -234,6 +234,12 @@ struct Panel {
     bool zero[2];
 };
 
+// Loads go through buffer descriptors whose base moves with the quarter, so
+// a thread keeps one 32-bit offset per block instead of a 64-bit address per
+// element and quarter (which do not fit in registers next to the tile).
+__device__ __forceinline__ double load_f64(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
+    return __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0));
+}
 __device__ __forceinline__ void fetch_quarter(double (&v)[QPER], const Panel& P, int q) {
     const int t = threadIdx.x;
 #pragma unroll
@@ -242,14 +248,20 @@ __device__ __forceinline__ void fetch_quarter(double (&v)[QPER], const Panel& P,
         if (P.zero[h]) {
 #pragma unroll
             for (int s = 0; s < 4; ++s) v[4 * h + s] = 0.0;
-        } else if (!b.trans) {
-            const int c = KQ * q + (t & 15), r = t >> 4;
+            continue;
+        }
+        const int ld = __builtin_amdgcn_readfirstlane((int)b.ld);
+        const char* base = reinterpret_cast<const char*>(b.p) + (b.trans ? (int64_t)KQ * q * ld : (int64_t)KQ * q) * 8;
+        const __amdgpu_buffer_rsrc_t r =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, B * ld * 8, 0x00020000);
+        if (!b.trans) {   // rows (t >> 4) + 16 s, columns 16 q + (t & 15)
+            const uint32_t off = (uint32_t)(((t >> 4) * ld + (t & 15)) * 8);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) v[4 * h + s] = b.p[(int64_t)(r + 16 * s) * b.ld + c];
-        } else {
-            const int c = t & 63, r = KQ * q + (t >> 6);
+            for (int s = 0; s < 4; ++s) v[4 * h + s] = load_f64(r, off, (uint32_t)(16 * s * ld * 8));
+        } else {          // rows 16 q + (t >> 6) + 4 s, columns t & 63
+            const uint32_t off = (uint32_t)(((t >> 6) * ld + (t & 63)) * 8);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) v[4 * h + s] = b.p[(int64_t)(r + 4 * s) * b.ld + c];
+            for (int s = 0; s < 4; ++s) v[4 * h + s] = load_f64(r, off, (uint32_t)(4 * s * ld * 8));
         }
     }
 }
@@ -317,6 +329,7 @@ __device__ __forceinline__ void panel_gemm(doublex4 (&acc)[4][4], double* S, int
     put_quarter(A0, ra0, panelA(t0));
     if (!same) put_quarter(B0, rb0, panelB(t0));
     __syncthreads();
+#pragma unroll 1   // unrolled, the phases' loads overlap and the registers do not suffice
     for (int h = 0; h < H; h += 2) {
         const int t1q = t0 + ((h + 1) >> 2), t2 = t0 + ((h + 2) >> 2), t3 = t0 + ((h + 3) >> 2);
         // quarter h + 1 into buffer 1; quarter h + 2 in flight
