@@ -7,6 +7,9 @@
  *     kfac_damped_inverse  (X + gamma I)^-1 of every factor, batched
  *     kfac_precondition (G + gamma I)^-1 . gradW . (A + gamma I)^-1 per layer
  *
+ * and, to feed real layers, kfac_im2col / kfac_grad_rows (factor inputs from
+ * a layer's input and output gradient) and kfac_grad_matrix (a layer's
+ * weight and bias gradients as one matrix and back),
  * following "Accelerating Distributed K-FAC with Smart Parallelism of
  * Computing and Communication Tasks" (cited per entry point below).
  *
@@ -149,6 +152,72 @@ kfac_status_t kfac_precondition(int n, const float* const* ginv, const float* co
                                 const float* const* ainv, const int64_t* d_g, const int64_t* d_a,
                                 float* const* out, void* workspace, size_t workspace_bytes,
                                 hipStream_t stream);
+
+/* ----------------------------------------------------------------- layers --
+ * Factor inputs of real layers.  The page computes A_{l-1} from the layer's
+ * input in the forward pre-hook and G_l from the gradient with respect to the
+ * layer's output in the backward hook (pipelining paragraph; the optimizer
+ * paragraph that registers both hooks on every layer).  For a convolution the
+ * rows of a factor input are its patches, one row per sample and output
+ * position, so that A = (1/rows) a^T a with rows = batch * H_out * W_out.
+ * A fully connected layer is the 1 x 1 case: h = w = kh = kw = 1.
+ */
+typedef struct {
+    int64_t n, c, h, w; /* input [n, c, h, w] row-major; n, c, h, w >= 1 */
+    int32_t kh, kw;     /* kernel size >= 1 */
+    int32_t sh, sw;     /* stride >= 1 */
+    int32_t ph, pw;     /* zero padding >= 0 */
+    int32_t dh, dw;     /* dilation >= 1 */
+    int32_t ones;       /* 1: a trailing column of ones (the layer has a bias), else 0 */
+    int32_t reserved;   /* 0 */
+} kfac_conv_t;
+
+/* Patches of each layer input as the rows of its A-factor input:
+ *
+ *     oh = (h + 2 ph - dh (kh - 1) - 1) / sh + 1,  ow likewise (both >= 1)
+ *     a[l][(ni oh + y) ow + x][(ci kh + i) kw + j] = x[l][ni][ci][y sh - ph + i dh][x sw - pw + j dw]
+ *
+ * zero where the index falls outside the input, and 1 in the last column
+ * when ones = 1.  a[l] is [n oh ow, c kh kw + ones] row-major, in `dtype`
+ * like x[l]; values are copied bit for bit.  The column order matches a
+ * weight [c_out, c, kh, kw] read as [c_out, c kh kw].  a[l] must not
+ * overlap any x[j]; at most 2^31 - 1 elements per a[l].
+ */
+size_t kfac_im2col_workspace_size(int n);
+kfac_status_t kfac_im2col(int n, const void* const* x, const kfac_conv_t* shape, kfac_dtype_t dtype,
+                          void* const* a, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Output gradients as the rows of each G-factor input:
+ *
+ *     g[l][b hw + p][ci] = scale * gy[l][b][ci][p]
+ *
+ * gy[l] : [batch[l], c[l], hw[l]] (an output gradient [b, c, H, W] with the
+ *         positions flattened; a fully connected layer: hw = 1);
+ * g[l]  : [batch[l] hw[l], c[l]], the product formed in float32 and stored
+ *         in `dtype` like gy[l] (rounded to nearest even for bfloat16).
+ * `scale` multiplies every gradient (for a loss averaged over the batch,
+ * scale = batch gives per-sample gradients).  g[l] must not overlap gy[j].
+ */
+size_t kfac_grad_rows_workspace_size(int n);
+kfac_status_t kfac_grad_rows(int n, const void* const* gy, const int64_t* batch, const int64_t* c,
+                             const int64_t* hw, kfac_dtype_t dtype, float scale, void* const* g,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* A layer's weight and bias gradients as one [d_out, d_in + has_bias] matrix
+ * (the gradW of kfac_precondition, bias in the last column) and back:
+ *
+ *     KFAC_PACK    mat[l][r][k] = wgrad[l][r][k] (k < d_in), mat[l][r][d_in] = bgrad[l][r]
+ *     KFAC_UNPACK  the reverse
+ *
+ * wgrad[l] : [d_out, d_in] float32 (a convolution weight [c_out, c, kh, kw]
+ *            with d_in = c kh kw);  bgrad[l] : [d_out] float32 or NULL (no
+ *            bias, has_bias = 0).  Values are copied bit for bit; mat[l]
+ *            must not overlap wgrad[j] or bgrad[j].
+ */
+size_t kfac_grad_matrix_workspace_size(int n);
+kfac_status_t kfac_grad_matrix(int n, float* const* wgrad, float* const* bgrad, const int64_t* d_out,
+                               const int64_t* d_in, float* const* mat, kfac_pack_dir_t dir,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

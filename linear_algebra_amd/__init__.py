@@ -28,7 +28,19 @@ EXPORTS = (
     "kfac_packed_size", "kfac_pack_workspace_size", "kfac_pack_sym",
     "kfac_inverse_workspace_size", "kfac_damped_inverse",
     "kfac_precondition_workspace_size", "kfac_precondition",
+    "kfac_im2col_workspace_size", "kfac_im2col",
+    "kfac_grad_rows_workspace_size", "kfac_grad_rows",
+    "kfac_grad_matrix_workspace_size", "kfac_grad_matrix",
 )
+
+
+class KfacConv(ctypes.Structure):
+    """kfac_conv_t: shape of a layer input and its convolution (1 x 1 for a
+    fully connected layer)."""
+    _fields_ = [("n", ctypes.c_int64), ("c", ctypes.c_int64), ("h", ctypes.c_int64), ("w", ctypes.c_int64),
+                ("kh", ctypes.c_int32), ("kw", ctypes.c_int32), ("sh", ctypes.c_int32), ("sw", ctypes.c_int32),
+                ("ph", ctypes.c_int32), ("pw", ctypes.c_int32), ("dh", ctypes.c_int32), ("dw", ctypes.c_int32),
+                ("ones", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class KfacLibraryError(RuntimeError):
@@ -65,6 +77,12 @@ def load_library(path: str = LIB_PATH):
         "kfac_damped_inverse": (i32, [i32, vp, vp, f32, vp, vp, vp, sz, vp]),
         "kfac_precondition_workspace_size": (sz, [i32, vp, vp]),
         "kfac_precondition": (i32, [i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "kfac_im2col_workspace_size": (sz, [i32]),
+        "kfac_im2col": (i32, [i32, vp, vp, i32, vp, vp, sz, vp]),
+        "kfac_grad_rows_workspace_size": (sz, [i32]),
+        "kfac_grad_rows": (i32, [i32, vp, vp, vp, vp, i32, f32, vp, vp, sz, vp]),
+        "kfac_grad_matrix_workspace_size": (sz, [i32]),
+        "kfac_grad_matrix": (i32, [i32, vp, vp, vp, vp, vp, i32, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -236,3 +254,95 @@ __all__ = [
     "kfac_factors", "kfac_packed_size", "kfac_pack_sym", "kfac_damped_inverse", "kfac_precondition",
     "KFAC_F32", "KFAC_BF16", "KFAC_PACK", "KFAC_UNPACK", "EXPORTS",
 ]
+
+
+def conv_out_hw(h: int, w: int, kh: int, kw: int, stride=(1, 1), padding=(0, 0), dilation=(1, 1)):
+    """Output height and width of a convolution (the formula of kfac_im2col)."""
+    oh = (h + 2 * padding[0] - dilation[0] * (kh - 1) - 1) // stride[0] + 1
+    ow = (w + 2 * padding[1] - dilation[1] * (kw - 1) - 1) // stride[1] + 1
+    return oh, ow
+
+
+def kfac_im2col(xs: Sequence, shapes: Sequence[dict], outs: Sequence, stream=None) -> None:
+    """a = patches of x as rows (kfac_im2col).  xs[i]: [n, c, h, w] float32 or
+    bfloat16; shapes[i]: dict with kh, kw, stride, padding, dilation, ones;
+    outs[i]: [n*oh*ow, c*kh*kw + ones] of the same dtype."""
+    import torch
+    lib = load_library()
+    if len(xs) != len(shapes) or len(xs) != len(outs) or len(xs) == 0:
+        raise ValueError("kfac_im2col: need equally many inputs, shapes and outputs")
+    dt = xs[0].dtype
+    if dt not in (torch.float32, torch.bfloat16):
+        raise ValueError("kfac_im2col: inputs must be float32 or bfloat16")
+    dev = _check(list(xs) + list(outs), dt, "kfac_im2col")
+    n = len(xs)
+    arr = (KfacConv * n)()
+    for i, (x, sh, o) in enumerate(zip(xs, shapes, outs)):
+        if x.dim() != 4:
+            raise ValueError("kfac_im2col: inputs must be [n, c, h, w]")
+        kh, kw = sh.get("kernel", (1, 1))
+        st, pd, dl = sh.get("stride", (1, 1)), sh.get("padding", (0, 0)), sh.get("dilation", (1, 1))
+        ones = int(bool(sh.get("ones", False)))
+        oh, ow = conv_out_hw(x.shape[2], x.shape[3], kh, kw, st, pd, dl)
+        if o.dim() != 2 or o.shape != (x.shape[0] * oh * ow, x.shape[1] * kh * kw + ones):
+            raise ValueError("kfac_im2col: output has the wrong shape")
+        arr[i] = KfacConv(x.shape[0], x.shape[1], x.shape[2], x.shape[3], kh, kw, st[0], st[1], pd[0], pd[1],
+                          dl[0], dl[1], ones, 0)
+    ws = _workspace(lib.kfac_im2col_workspace_size(n), dev)
+    dtype = KFAC_BF16 if dt == torch.bfloat16 else KFAC_F32
+    _call(lib.kfac_im2col(n, _ptrs(xs), ctypes.cast(arr, ctypes.c_void_p), dtype, _ptrs(outs),
+                          ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(dev, stream)), "kfac_im2col")
+
+
+def kfac_grad_rows(gys: Sequence, scale: float, outs: Sequence, stream=None) -> None:
+    """g[b*hw + p][c] = scale * gy[b][c][p] (kfac_grad_rows).  gys[i]:
+    [b, c] or [b, c, H, W], float32 or bfloat16; outs[i]: [b*H*W, c]."""
+    import torch
+    lib = load_library()
+    if len(gys) != len(outs) or len(gys) == 0:
+        raise ValueError("kfac_grad_rows: need equally many gradients and outputs")
+    dt = gys[0].dtype
+    if dt not in (torch.float32, torch.bfloat16):
+        raise ValueError("kfac_grad_rows: gradients must be float32 or bfloat16")
+    dev = _check(list(gys) + list(outs), dt, "kfac_grad_rows")
+    b, c, hw = [], [], []
+    for gy, o in zip(gys, outs):
+        if gy.dim() < 2:
+            raise ValueError("kfac_grad_rows: gradients must be [b, c, ...]")
+        p = 1
+        for s_ in gy.shape[2:]:
+            p *= s_
+        if o.shape != (gy.shape[0] * p, gy.shape[1]):
+            raise ValueError("kfac_grad_rows: output has the wrong shape")
+        b.append(gy.shape[0]); c.append(gy.shape[1]); hw.append(p)
+    n = len(gys)
+    ws = _workspace(lib.kfac_grad_rows_workspace_size(n), dev)
+    dtype = KFAC_BF16 if dt == torch.bfloat16 else KFAC_F32
+    _call(lib.kfac_grad_rows(n, _ptrs(gys), _i64(b), _i64(c), _i64(hw), dtype, ctypes.c_float(scale), _ptrs(outs),
+                             ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(dev, stream)), "kfac_grad_rows")
+
+
+def kfac_grad_matrix(wgrads: Sequence, bgrads: Sequence, mats: Sequence, direction: int, stream=None) -> None:
+    """KFAC_PACK: mats[i] = [wgrad | bgrad]; KFAC_UNPACK: the reverse.
+    wgrads[i]: float32 with d_out = shape[0] and d_in = the rest flattened;
+    bgrads[i]: [d_out] or None; mats[i]: [d_out, d_in + has_bias]."""
+    import torch
+    lib = load_library()
+    if len(wgrads) != len(bgrads) or len(wgrads) != len(mats) or len(wgrads) == 0:
+        raise ValueError("kfac_grad_matrix: need equally many weights, biases and matrices")
+    dev = _check(list(wgrads) + [b for b in bgrads if b is not None] + list(mats), torch.float32, "kfac_grad_matrix")
+    d_out, d_in = [], []
+    for w, b, m in zip(wgrads, bgrads, mats):
+        do = w.shape[0]
+        di = w.numel() // do
+        if b is not None and b.numel() != do:
+            raise ValueError("kfac_grad_matrix: bias gradient has the wrong length")
+        if m.shape != (do, di + (b is not None)):
+            raise ValueError("kfac_grad_matrix: matrix has the wrong shape")
+        d_out.append(do); d_in.append(di)
+    n = len(wgrads)
+    bptr = (ctypes.c_void_p * n)(*[b.data_ptr() if b is not None else None for b in bgrads])
+    ws = _workspace(lib.kfac_grad_matrix_workspace_size(n), dev)
+    _call(lib.kfac_grad_matrix(n, _ptrs(wgrads), ctypes.cast(bptr, ctypes.c_void_p), _i64(d_out), _i64(d_in),
+                               _ptrs(mats), int(direction), ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+                               _stream(dev, stream)), "kfac_grad_matrix")

@@ -65,6 +65,47 @@ struct GemmLaunch {
 hipError_t launch_gemm(const GemmLaunch& L, int64_t items, hipStream_t stream, bool bf16);
 hipError_t launch_gemm_reduce(const GemmLaunch& L, int64_t tiles, hipStream_t stream);
 
+// ----------------------------------------------------------------- layers --
+constexpr int kLayerTile = 64;       // im2col and gradient-row tiles are 64 x 64
+constexpr int kGradMatChunk = 4096;  // elements per workgroup in kfac_grad_matrix
+
+struct Im2colLayer {
+    const void* x;
+    void* a;
+    int64_t c, h, w;
+    int64_t rows;         // n * oh * ow
+    int64_t tile_begin;   // first work item of this layer
+    int32_t kh, kw, sh, sw, ph, pw, dh, dw;
+    int32_t oh, ow;
+    int32_t cols;         // c * kh * kw + ones
+    int32_t ones;
+    int32_t tiles_c;      // column tiles
+    int32_t pad_;
+};
+
+struct GradRowsLayer {
+    const void* gy;
+    void* g;
+    int64_t batch, c, hw;
+    int64_t tile_begin;
+    int32_t tiles_c;      // channel tiles
+    int32_t tiles_p;      // position tiles per sample (hw > 1) or batch tiles (hw == 1)
+};
+
+struct GradMatLayer {
+    float* w;
+    float* b;
+    float* mat;
+    int64_t d_out, d_in;
+    int64_t chunk_begin;
+    int64_t cols;         // d_in + (b != nullptr)
+};
+
+hipError_t launch_im2col(const Im2colLayer* layers, int n, int64_t tiles, bool bf16, hipStream_t stream);
+hipError_t launch_grad_rows(const GradRowsLayer* layers, int n, int64_t tiles, bool bf16, float scale,
+                            hipStream_t stream);
+hipError_t launch_grad_matrix(const GradMatLayer* layers, int n, int64_t chunks, bool pack, hipStream_t stream);
+
 // ------------------------------------------------------------------- pack --
 struct PackLayer {
     float* m;             // [d][d] matrix

@@ -488,4 +488,116 @@ kfac_status_t kfac_precondition(int n, const float* const* ginv, const float* co
     return hip_status(e);
 }
 
+// ----------------------------------------------------------------- layers --
+
+size_t kfac_im2col_workspace_size(int n) {
+    if (n < 1 || n > KFAC_MAX_COUNT) return 0;
+    Carver c(nullptr);
+    c.take(sizeof(Im2colLayer) * n);
+    return c.used;
+}
+
+kfac_status_t kfac_im2col(int n, const void* const* x, const kfac_conv_t* shape, kfac_dtype_t dtype,
+                          void* const* a, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (n < 1 || n > KFAC_MAX_COUNT || x == nullptr || shape == nullptr || a == nullptr) return KFAC_ERR_INVALID_VALUE;
+    if (dtype != KFAC_F32 && dtype != KFAC_BF16) return KFAC_ERR_INVALID_VALUE;
+    const size_t esz = dtype == KFAC_BF16 ? 2 : 4;
+    std::vector<Im2colLayer> layers(n);
+    int64_t tiles = 0;
+    for (int i = 0; i < n; ++i) {
+        const kfac_conv_t& s = shape[i];
+        if (x[i] == nullptr || a[i] == nullptr || !aligned(x[i], esz) || !aligned(a[i], esz)) return KFAC_ERR_INVALID_VALUE;
+        if (s.n < 1 || s.c < 1 || s.h < 1 || s.w < 1 || s.kh < 1 || s.kw < 1 || s.sh < 1 || s.sw < 1 || s.ph < 0 ||
+            s.pw < 0 || s.dh < 1 || s.dw < 1 || (s.ones != 0 && s.ones != 1) || s.reserved != 0)
+            return KFAC_ERR_INVALID_VALUE;
+        const int64_t eh = s.h + 2 * (int64_t)s.ph - (int64_t)s.dh * (s.kh - 1) - 1;
+        const int64_t ew = s.w + 2 * (int64_t)s.pw - (int64_t)s.dw * (s.kw - 1) - 1;
+        if (eh < 0 || ew < 0) return KFAC_ERR_INVALID_VALUE;
+        const int64_t oh = eh / s.sh + 1, ow = ew / s.sw + 1;
+        const int64_t cols = s.c * s.kh * s.kw + s.ones;
+        const int64_t rows = s.n * oh * ow;
+        if (oh > INT32_MAX || ow > INT32_MAX || cols > INT32_MAX || rows > INT32_MAX / cols) return KFAC_ERR_INVALID_VALUE;
+        Im2colLayer& L = layers[i];
+        L = Im2colLayer{x[i], a[i], s.c, s.h, s.w, rows, tiles, s.kh, s.kw, s.sh, s.sw, s.ph, s.pw, s.dh, s.dw,
+                        (int32_t)oh, (int32_t)ow, (int32_t)cols, s.ones, (int32_t)ceil_div(cols, kLayerTile), 0};
+        tiles += ceil_div(rows, kLayerTile) * L.tiles_c;
+    }
+    const size_t need = kfac_im2col_workspace_size(n);
+    if (workspace == nullptr || !aligned(workspace, kAlign) || workspace_bytes < need) return KFAC_ERR_WORKSPACE;
+    Carver c(workspace);
+    Im2colLayer* dev = static_cast<Im2colLayer*>(c.take(sizeof(Im2colLayer) * n));
+    hipError_t e = upload_table(dev, layers.data(), sizeof(Im2colLayer) * n, stream);
+    if (e != hipSuccess) return KFAC_ERR_HIP;
+    return hip_status(launch_im2col(dev, n, tiles, dtype == KFAC_BF16, stream));
+}
+
+size_t kfac_grad_rows_workspace_size(int n) {
+    if (n < 1 || n > KFAC_MAX_COUNT) return 0;
+    Carver c(nullptr);
+    c.take(sizeof(GradRowsLayer) * n);
+    return c.used;
+}
+
+kfac_status_t kfac_grad_rows(int n, const void* const* gy, const int64_t* batch, const int64_t* ch,
+                             const int64_t* hw, kfac_dtype_t dtype, float scale, void* const* g,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (n < 1 || n > KFAC_MAX_COUNT || gy == nullptr || batch == nullptr || ch == nullptr || hw == nullptr ||
+        g == nullptr || !std::isfinite(scale))
+        return KFAC_ERR_INVALID_VALUE;
+    if (dtype != KFAC_F32 && dtype != KFAC_BF16) return KFAC_ERR_INVALID_VALUE;
+    const size_t esz = dtype == KFAC_BF16 ? 2 : 4;
+    std::vector<GradRowsLayer> layers(n);
+    int64_t tiles = 0;
+    for (int i = 0; i < n; ++i) {
+        if (gy[i] == nullptr || g[i] == nullptr || !aligned(gy[i], esz) || !aligned(g[i], esz)) return KFAC_ERR_INVALID_VALUE;
+        if (batch[i] < 1 || ch[i] < 1 || hw[i] < 1) return KFAC_ERR_INVALID_VALUE;
+        const int64_t tc = ceil_div(ch[i], kLayerTile);
+        const int64_t tp = hw[i] == 1 ? ceil_div(batch[i], kLayerTile) : ceil_div(hw[i], kLayerTile);
+        if (tc > INT32_MAX || tp > INT32_MAX) return KFAC_ERR_INVALID_VALUE;
+        layers[i] = GradRowsLayer{gy[i], g[i], batch[i], ch[i], hw[i], tiles, (int32_t)tc, (int32_t)tp};
+        tiles += hw[i] == 1 ? tp * tc : batch[i] * tc * tp;
+    }
+    const size_t need = kfac_grad_rows_workspace_size(n);
+    if (workspace == nullptr || !aligned(workspace, kAlign) || workspace_bytes < need) return KFAC_ERR_WORKSPACE;
+    Carver c(workspace);
+    GradRowsLayer* dev = static_cast<GradRowsLayer*>(c.take(sizeof(GradRowsLayer) * n));
+    hipError_t e = upload_table(dev, layers.data(), sizeof(GradRowsLayer) * n, stream);
+    if (e != hipSuccess) return KFAC_ERR_HIP;
+    return hip_status(launch_grad_rows(dev, n, tiles, dtype == KFAC_BF16, scale, stream));
+}
+
+size_t kfac_grad_matrix_workspace_size(int n) {
+    if (n < 1 || n > KFAC_MAX_COUNT) return 0;
+    Carver c(nullptr);
+    c.take(sizeof(GradMatLayer) * n);
+    return c.used;
+}
+
+kfac_status_t kfac_grad_matrix(int n, float* const* wgrad, float* const* bgrad, const int64_t* d_out,
+                               const int64_t* d_in, float* const* mat, kfac_pack_dir_t dir,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (n < 1 || n > KFAC_MAX_COUNT || wgrad == nullptr || d_out == nullptr || d_in == nullptr || mat == nullptr)
+        return KFAC_ERR_INVALID_VALUE;
+    if (dir != KFAC_PACK && dir != KFAC_UNPACK) return KFAC_ERR_INVALID_VALUE;
+    std::vector<GradMatLayer> layers(n);
+    int64_t chunks = 0;
+    for (int i = 0; i < n; ++i) {
+        float* b = bgrad ? bgrad[i] : nullptr;
+        if (wgrad[i] == nullptr || mat[i] == nullptr || !aligned(wgrad[i], 4) || !aligned(mat[i], 4) ||
+            (b != nullptr && !aligned(b, 4)))
+            return KFAC_ERR_INVALID_VALUE;
+        if (d_out[i] < 1 || d_in[i] < 1) return KFAC_ERR_INVALID_VALUE;
+        const int64_t cols = d_in[i] + (b ? 1 : 0);
+        layers[i] = GradMatLayer{wgrad[i], b, mat[i], d_out[i], d_in[i], chunks, cols};
+        chunks += ceil_div(d_out[i] * cols, kGradMatChunk);
+    }
+    const size_t need = kfac_grad_matrix_workspace_size(n);
+    if (workspace == nullptr || !aligned(workspace, kAlign) || workspace_bytes < need) return KFAC_ERR_WORKSPACE;
+    Carver c(workspace);
+    GradMatLayer* dev = static_cast<GradMatLayer*>(c.take(sizeof(GradMatLayer) * n));
+    hipError_t e = upload_table(dev, layers.data(), sizeof(GradMatLayer) * n, stream);
+    if (e != hipSuccess) return KFAC_ERR_HIP;
+    return hip_status(launch_grad_matrix(dev, n, chunks, dir == KFAC_PACK, stream));
+}
+
 }  // extern "C"

@@ -26,6 +26,14 @@ plain reading is used and listed in the design notes:
 * precondition P = (G+gamma I)^-1 grad (A+gamma I)^-1 (the damped update rule
               after the Kronecker inverse property, Eq. (4) onwards); computed
               as two fp64 matrix products of the given inverses.
+* layers      the factor inputs of real layers, taken in the forward
+              pre-hook (layer input) and the backward hook (gradient of the
+              layer output) of the pipelining paragraph: the patches of a
+              convolution input as rows (one per sample and output position,
+              a column of ones for a bias), the output gradient as rows
+              [b*H*W, c] times a scale, and a layer's weight and bias
+              gradients as one matrix.  Written as index loops over the
+              kernel taps.
 
 Inputs are the exact values given to the GPU (float32 and bf16 upcast to
 float64 exactly).  gamma and eps are float32 in the GPU library; callers pass
@@ -215,3 +223,76 @@ __all__ = [
     "cholesky_upper", "damped_inverse", "damped_inverse_columns", "precondition",
     "precondition_entries", "rel_fro", "rel_fro_upper",
 ]
+
+
+# ----------------------------------------------------------------- layers --
+
+def conv_out_hw(h, w, kh, kw, stride=(1, 1), padding=(0, 0), dilation=(1, 1)):
+    """Output size of a convolution: (h + 2p - d (k - 1) - 1) // s + 1."""
+    oh = (h + 2 * padding[0] - dilation[0] * (kh - 1) - 1) // stride[0] + 1
+    ow = (w + 2 * padding[1] - dilation[1] * (kw - 1) - 1) // stride[1] + 1
+    return oh, ow
+
+
+def im2col(x, kernel=(1, 1), stride=(1, 1), padding=(0, 0), dilation=(1, 1), ones=False) -> np.ndarray:
+    """Patches of x [n, c, h, w] as rows: row (ni*oh + y)*ow + xo, column
+    (ci*kh + i)*kw + j holds x[ni, ci, y*sh - ph + i*dh, xo*sw - pw + j*dw]
+    (zero outside the input), then a column of ones if `ones`.  Same dtype
+    as x (values are copied)."""
+    x = np.asarray(x)
+    n, c, h, w = x.shape
+    kh, kw = kernel
+    oh, ow = conv_out_hw(h, w, kh, kw, stride, padding, dilation)
+    out = np.zeros((n, oh, ow, c, kh, kw), dtype=x.dtype)
+    for i in range(kh):
+        for j in range(kw):
+            for y in range(oh):
+                yy = y * stride[0] - padding[0] + i * dilation[0]
+                if yy < 0 or yy >= h:
+                    continue
+                for xo in range(ow):
+                    xx = xo * stride[1] - padding[1] + j * dilation[1]
+                    if 0 <= xx < w:
+                        out[:, y, xo, :, i, j] = x[:, :, yy, xx]
+    a = out.reshape(n * oh * ow, c * kh * kw)
+    if ones:
+        a = np.concatenate([a, np.ones((a.shape[0], 1), dtype=x.dtype)], axis=1)
+    return a
+
+
+def bf16_round(x32) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round to nearest, ties to
+    even; NaN stays NaN."""
+    u = np.asarray(x32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    nan = (u & 0x7FFFFFFF) > 0x7F800000
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    r[nan] = ((u[nan] >> 16) | 0x40).astype(np.uint16)
+    return r
+
+
+def grad_rows(gy, scale: float, bf16: bool = False) -> np.ndarray:
+    """g[b*hw + p][ci] = scale * gy[b][ci][p] for gy [b, c, ...] (positions
+    flattened), the product in float32; bfloat16 inputs are given as their
+    uint16 bit patterns and the result is rounded back to bfloat16."""
+    gy = np.asarray(gy)
+    b, c = gy.shape[0], gy.shape[1]
+    v = gy.reshape(b, c, -1)
+    if bf16:
+        v = (v.astype(np.uint32) << 16).view(np.float32)
+    g = np.empty((b * v.shape[2], c), dtype=np.float32)
+    s = np.float32(scale)
+    for bi in range(b):
+        for p in range(v.shape[2]):
+            g[bi * v.shape[2] + p, :] = s * v[bi, :, p]
+    return bf16_round(g) if bf16 else g
+
+
+def grad_matrix(wgrad, bgrad=None) -> np.ndarray:
+    """[wgrad | bgrad]: wgrad [d_out, ...] read as [d_out, d_in], the bias
+    gradient as the last column."""
+    w = np.asarray(wgrad)
+    w = w.reshape(w.shape[0], -1)
+    if bgrad is None:
+        return w.copy()
+    return np.concatenate([w, np.asarray(bgrad).reshape(-1, 1)], axis=1)
+

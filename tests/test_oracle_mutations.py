@@ -39,6 +39,12 @@ PIN_CASES = [
     (pins.test_precondition_kronecker_brute_force, dict(da=16, dg=16)),
     (pins.test_precondition_kronecker_brute_force, dict(da=9, dg=2)),
     (pins.test_precondition_closed_forms, {}),
+    (pins.test_im2col_matches_torch_unfold, {}),
+    (pins.test_im2col_hand_example, {}),
+    (pins.test_conv_weight_gradient_is_g_rows_times_patches, {}),
+    (pins.test_grad_rows_layout_and_scale, {}),
+    (pins.test_grad_rows_bf16_rounding, {}),
+    (pins.test_grad_matrix_concatenates_bias, {}),
 ]
 
 
@@ -101,7 +107,33 @@ PY_MUTATIONS = {
                                         lambda m, f, eps, first: _f64(f).copy() if first else (1 - eps) * _f64(m) + eps * _f64(f)),
     "precondition_missing_right_inverse": ("precondition", lambda zg, g, za: _f64(zg) @ _f64(g)),
     "precondition_swapped_inverses": ("precondition", lambda zg, g, za: _f64(za) @ _f64(g) @ _f64(zg)),
+    "im2col_taps_transposed": ("im2col", lambda x, kernel=(1, 1), stride=(1, 1), padding=(0, 0), dilation=(1, 1),
+                               ones=False: _im2col_taps_transposed(x, kernel, stride, padding, dilation, ones)),
+    "im2col_padding_dropped": ("im2col", lambda x, kernel=(1, 1), stride=(1, 1), padding=(0, 0), dilation=(1, 1),
+                               ones=False: _REAL_IM2COL(x, kernel, stride, (0, 0), dilation, ones)),
+    "grad_rows_no_transpose": ("grad_rows", lambda gy, scale, bf16=False: _grad_rows_no_transpose(gy, scale, bf16)),
+    "grad_rows_scale_dropped": ("grad_rows", lambda gy, scale, bf16=False: _REAL_GRAD_ROWS(gy, 1.0, bf16)),
 }
+
+_REAL_IM2COL = oracle.im2col
+_REAL_GRAD_ROWS = oracle.grad_rows
+
+
+def _im2col_taps_transposed(x, kernel, stride, padding, dilation, ones):
+    # columns in (c, j, i) order instead of (c, i, j)
+    a = _REAL_IM2COL(x, kernel, stride, padding, dilation, False)
+    n, c = a.shape[0], np.asarray(x).shape[1]
+    a = a.reshape(n, c, kernel[0], kernel[1]).transpose(0, 1, 3, 2).reshape(n, -1)
+    if ones:
+        a = np.concatenate([a, np.ones((n, 1), dtype=a.dtype)], axis=1)
+    return a
+
+
+def _grad_rows_no_transpose(gy, scale, bf16):
+    # rows read as [b*c] blocks of positions, i.e. the NCHW order kept
+    g = _REAL_GRAD_ROWS(gy, scale, bf16)
+    gy = np.asarray(gy)
+    return g.reshape(gy.shape[0], -1, gy.shape[1]).transpose(0, 2, 1).reshape(g.shape)
 
 
 @pytest.mark.parametrize("name", sorted(PY_MUTATIONS))

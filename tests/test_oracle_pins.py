@@ -397,3 +397,97 @@ def test_bf16_rounding_matches_torch():
     ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     np.testing.assert_array_equal(f32_to_bf16_bits(x), ref)
     np.testing.assert_array_equal(bf16_bits_to_f32(ref), torch.from_numpy(ref.view(np.int16)).view(torch.bfloat16).float().numpy())
+
+
+# ----------------------------------------------------------------- layers --
+
+CONV_CASES = [
+    dict(shape=(2, 3, 7, 6), kernel=(3, 3), stride=(1, 1), padding=(1, 1), dilation=(1, 1)),
+    dict(shape=(1, 4, 9, 8), kernel=(3, 2), stride=(2, 1), padding=(1, 0), dilation=(1, 2)),
+    dict(shape=(3, 2, 5, 5), kernel=(1, 1), stride=(2, 2), padding=(0, 0), dilation=(1, 1)),
+    dict(shape=(2, 3, 8, 8), kernel=(7, 7), stride=(2, 2), padding=(3, 3), dilation=(1, 1)),
+]
+
+
+def test_im2col_matches_torch_unfold():
+    """Patch matrix against torch's CPU unfold (a different implementation):
+    unfold gives [n, c*kh*kw, oh*ow] with the same column order."""
+    import torch
+    rng = np.random.default_rng(41)
+    for case in CONV_CASES:
+        x = rng.standard_normal(case["shape"])
+        a = oracle.im2col(x, case["kernel"], case["stride"], case["padding"], case["dilation"], ones=True)
+        u = torch.nn.functional.unfold(torch.from_numpy(x), case["kernel"], dilation=case["dilation"],
+                                       padding=case["padding"], stride=case["stride"])
+        ref = u.permute(0, 2, 1).reshape(-1, u.shape[1]).numpy()
+        np.testing.assert_array_equal(a[:, :-1], ref)
+        assert np.all(a[:, -1] == 1.0)
+
+
+def test_im2col_hand_example():
+    """3 x 3 image 1..9, 2 x 2 kernel: the four patches written out."""
+    x = np.arange(1.0, 10.0).reshape(1, 1, 3, 3)
+    a = oracle.im2col(x, (2, 2))
+    np.testing.assert_array_equal(a, [[1, 2, 4, 5], [2, 3, 5, 6], [4, 5, 7, 8], [5, 6, 8, 9]])
+    # padding 1 puts zeros around: the first patch is [0, 0, 0, 1]
+    b = oracle.im2col(x, (2, 2), padding=(1, 1))
+    assert b.shape == (16, 4)
+    np.testing.assert_array_equal(b[0], [0, 0, 0, 1])
+    np.testing.assert_array_equal(b[-1], [9, 0, 0, 0])
+
+
+def test_conv_weight_gradient_is_g_rows_times_patches():
+    """For a convolution, autograd's weight gradient equals g^T a with
+    g = grad_rows(dL/dy, 1) and a = im2col(x): this ties the row order of
+    both factor inputs and the column order of the patches to the weight
+    layout [c_out, c, kh, kw].  The bias gradient is g^T 1."""
+    import torch
+    rng = np.random.default_rng(42)
+    for case in CONV_CASES:
+        n, c, h, w = case["shape"]
+        x = torch.from_numpy(rng.standard_normal(case["shape"]))
+        conv = torch.nn.Conv2d(c, 5, case["kernel"], stride=case["stride"], padding=case["padding"],
+                               dilation=case["dilation"], bias=True).double()
+        y = conv(x)
+        gy = torch.from_numpy(rng.standard_normal(tuple(y.shape)))
+        y.backward(gy)
+        a = oracle.im2col(x.numpy(), case["kernel"], case["stride"], case["padding"], case["dilation"], ones=True)
+        g = oracle.grad_rows(gy.numpy().astype(np.float32), 1.0).astype(np.float64)
+        gw = g.T @ a
+        np.testing.assert_allclose(gw[:, :-1], conv.weight.grad.reshape(5, -1).numpy(), rtol=1e-6, atol=1e-6)
+        np.testing.assert_allclose(gw[:, -1], conv.bias.grad.numpy(), rtol=1e-6, atol=1e-6)
+
+
+def test_grad_rows_layout_and_scale():
+    gy = np.arange(2 * 3 * 4, dtype=np.float32).reshape(2, 3, 2, 2)
+    g = oracle.grad_rows(gy, 0.5)
+    assert g.shape == (8, 3)
+    for b in range(2):
+        for ci in range(3):
+            for p in range(4):
+                assert g[b * 4 + p, ci] == np.float32(0.5) * gy[b, ci, p // 2, p % 2]
+    # a fully connected layer: [b, c] scaled, no reordering
+    np.testing.assert_array_equal(oracle.grad_rows(gy[:, :, 0, 0], 4.0), 4.0 * gy[:, :, 0, 0])
+
+
+def test_grad_rows_bf16_rounding():
+    """bfloat16 gradients: the scaled float32 value rounded to nearest even,
+    checked against torch's conversion, including exact ties."""
+    import torch
+    rng = np.random.default_rng(43)
+    x32 = (rng.standard_normal((4, 5, 3)) * 0.02).astype(np.float32)
+    bits = torch.from_numpy(x32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = oracle.grad_rows(bits, 3.0, bf16=True)
+    vals = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).float() * 3.0
+    ref = vals.permute(0, 2, 1).reshape(12, 5).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(got, ref)
+    ties = np.array([0x3F808000, 0x3F818000, 0xBF808000], dtype=np.uint32).view(np.float32)
+    np.testing.assert_array_equal(oracle.bf16_round(ties), [0x3F80, 0x3F82, 0xBF80])
+
+
+def test_grad_matrix_concatenates_bias():
+    w = np.arange(12, dtype=np.float32).reshape(2, 3, 2)
+    b = np.array([100.0, 200.0], dtype=np.float32)
+    m = oracle.grad_matrix(w, b)
+    np.testing.assert_array_equal(m, [[0, 1, 2, 3, 4, 5, 100], [6, 7, 8, 9, 10, 11, 200]])
+    np.testing.assert_array_equal(oracle.grad_matrix(w), w.reshape(2, 6))
