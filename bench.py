@@ -192,6 +192,102 @@ def sweep_inverse(dims=(64, 128, 256, 512, 768, 1024, 1536, 2048, 3072, 4096, 61
     }
 
 
+def resnet50_conv_geometry(batch=32):
+    """Input shape, kernel, stride and padding of each ResNet-50 convolution,
+    read back from the factor workload's layer list (d_A = c_in k^2,
+    rows = batch H_out W_out; stride 2 on the stem and on the 3x3 and
+    shortcut convolutions of each down-sampling block)."""
+    import math
+    from workloads import CONFIGS
+    out = []
+    for l in CONFIGS[3].layers:
+        if l.name == "fc":
+            continue
+        k = 7 if l.name == "conv1" else (3 if l.name.endswith("conv2") else 1)
+        parts = l.name.split(".")
+        s = 2 if l.name == "conv1" or (parts[0] in ("layer2", "layer3", "layer4") and parts[1] == "0"
+                                       and parts[2] in ("conv2", "downsample")) else 1
+        ho = int(round(math.sqrt(l.rows / batch)))
+        out.append(dict(name=l.name, c_in=l.d_a // (k * k), c_out=l.d_g, h_in=ho * s, h_out=ho, k=k, s=s, p=k // 2,
+                        rows=l.rows, d_a=l.d_a))
+    return out
+
+
+def bench_layers(steps=10, warmup=3):
+    """Factor inputs of real layers: kfac_im2col over the 53 ResNet-50
+    convolution inputs and kfac_grad_rows over their output gradients (batch
+    32, one call each, HBM-bound: bytes = the input elements the patches
+    touch, read once, + the output written once),
+    and one KFACPreconditioner step on the four-layer MLP built from
+    torch.nn.Linear layers (batch 128, inverses every step)."""
+    import numpy as np
+    import torch
+
+    import linear_algebra_amd as la
+    from linear_algebra_amd.kfac_preconditioner import KFACPreconditioner
+
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    geo = resnet50_conv_geometry()
+    xs, shapes, outs, gys, gouts = [], [], [], [], []
+    bytes_im2col = bytes_rows = 0
+    for g in geo:
+        x = torch.randn(32, g["c_in"], g["h_in"], g["h_in"], device=dev, generator=gen)
+        sh = dict(kernel=(g["k"], g["k"]), stride=(g["s"], g["s"]), padding=(g["p"], g["p"]), dilation=(1, 1),
+                  ones=False)
+        assert la.conv_out_hw(g["h_in"], g["h_in"], g["k"], g["k"], sh["stride"], sh["padding"]) == (g["h_out"], g["h_out"])
+        xs.append(x)
+        shapes.append(sh)
+        outs.append(torch.empty(g["rows"], g["d_a"], device=dev))
+        gy = torch.randn(32, g["c_out"], g["h_out"], g["h_out"], device=dev, generator=gen)
+        gys.append(gy)
+        gouts.append(torch.empty(g["rows"], g["c_out"], device=dev))
+        # input elements some patch reads (all of them, except the skipped
+        # rows and columns of a 1x1 stride-2 shortcut), read once, + a written
+        ref = len({y * g["s"] - g["p"] + i for y in range(g["h_out"]) for i in range(g["k"])} & set(range(g["h_in"])))
+        bytes_im2col += 4 * (32 * g["c_in"] * ref * ref + g["rows"] * g["d_a"])
+        bytes_rows += 8 * gy.numel()
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ms_im2col = timed(lambda: la.kfac_im2col(xs, shapes, outs))
+    ms_rows = timed(lambda: la.kfac_grad_rows(gys, 32.0, gouts))
+    del xs, outs, gys, gouts
+    torch.cuda.empty_cache()
+
+    torch.manual_seed(1)
+    model = torch.nn.Sequential(torch.nn.Linear(1024, 2048), torch.nn.ReLU(), torch.nn.Linear(2048, 2048),
+                                torch.nn.ReLU(), torch.nn.Linear(2048, 1024), torch.nn.ReLU(),
+                                torch.nn.Linear(1024, 10)).to(dev)
+    pre = KFACPreconditioner(model, damping=1e-3, factor_decay=0.95, inv_update_freq=1)
+    x = torch.randn(128, 1024, device=dev, generator=gen)
+    y = torch.randint(0, 10, (128,), device=dev, generator=gen)
+    torch.nn.functional.cross_entropy(model(x), y).backward()
+    ms_pre = timed(pre.step)
+    return {
+        "metric": "factor inputs of real layers and one preconditioner step",
+        "im2col": {"workload": "ResNet-50, 53 convolutions, batch 32, fp32", "ms": round(ms_im2col, 4),
+                   "bytes": bytes_im2col, "achieved_GBps": round(bytes_im2col / ms_im2col / 1e6, 1),
+                   "peak_GBps": PEAK_HBM / 1e9, "frac": round(bytes_im2col / (ms_im2col * 1e-3) / PEAK_HBM, 4)},
+        "grad_rows": {"workload": "ResNet-50 output gradients, batch 32, fp32", "ms": round(ms_rows, 4),
+                      "bytes": bytes_rows, "achieved_GBps": round(bytes_rows / ms_rows / 1e6, 1),
+                      "frac": round(bytes_rows / (ms_rows * 1e-3) / PEAK_HBM, 4)},
+        "preconditioner_step": {"workload": "MLP 1024-2048-2048-1024-10 as nn.Linear, batch 128, inverses every step",
+                                "ms": round(ms_pre, 4)},
+    }
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -200,6 +296,8 @@ def main(argv=None):
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=25.0)
+    ap.add_argument("--layers", action="store_true",
+                    help="time the layer factor inputs (im2col, gradient rows) and a preconditioner step")
     ap.add_argument("--sweep-inverse", action="store_true",
                     help="time kfac_damped_inverse on single matrices of d in [64, 8192] and fit time models")
     args = ap.parse_args(argv)
@@ -218,6 +316,9 @@ def main(argv=None):
     la.load_library()
     if args.sweep_inverse:
         print(json.dumps(sweep_inverse()), flush=True)
+        return 0
+    if args.layers:
+        print(json.dumps(bench_layers()), flush=True)
         return 0
     dev = torch.device("cuda:0")
     cfg = CONFIGS[args.config]

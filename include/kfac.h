@@ -181,7 +181,8 @@ typedef struct {
  * when ones = 1.  a[l] is [n oh ow, c kh kw + ones] row-major, in `dtype`
  * like x[l]; values are copied bit for bit.  The column order matches a
  * weight [c_out, c, kh, kw] read as [c_out, c kh kw].  a[l] must not
- * overlap any x[j]; at most 2^31 - 1 elements per a[l].
+ * overlap any x[j]; at most 2^31 - 1 elements per a[l] and per sample of
+ * x[l] (c h w), else KFAC_ERR_INVALID_VALUE.
  */
 size_t kfac_im2col_workspace_size(int n);
 kfac_status_t kfac_im2col(int n, const void* const* x, const kfac_conv_t* shape, kfac_dtype_t dtype,

@@ -80,8 +80,14 @@ struct Im2colLayer {
     int32_t cols;         // c * kh * kw + ones
     int32_t ones;
     int32_t tiles_c;      // column tiles
-    int32_t pad_;
+    int32_t vec;          // kVecIn | kVecOut
 };
+
+// Four-element accesses of the layer kernels: kVecIn when every group of
+// four consecutive rows of a tile is four consecutive, aligned elements of
+// the input, kVecOut when the rows of the output hold a multiple of four
+// elements and start aligned.
+constexpr int32_t kVecIn = 1, kVecOut = 2;
 
 struct GradRowsLayer {
     const void* gy;
@@ -90,6 +96,8 @@ struct GradRowsLayer {
     int64_t tile_begin;
     int32_t tiles_c;      // channel tiles
     int32_t tiles_p;      // position tiles per sample (hw > 1) or batch tiles (hw == 1)
+    int32_t vec;          // kVecIn | kVecOut
+    int32_t pad_;
 };
 
 struct GradMatLayer {

@@ -516,10 +516,16 @@ kfac_status_t kfac_im2col(int n, const void* const* x, const kfac_conv_t* shape,
         const int64_t oh = eh / s.sh + 1, ow = ew / s.sw + 1;
         const int64_t cols = s.c * s.kh * s.kw + s.ones;
         const int64_t rows = s.n * oh * ow;
-        if (oh > INT32_MAX || ow > INT32_MAX || cols > INT32_MAX || rows > INT32_MAX / cols) return KFAC_ERR_INVALID_VALUE;
+        if (oh > INT32_MAX || ow > INT32_MAX || cols > INT32_MAX || rows > INT32_MAX / cols ||
+            s.c > INT32_MAX / s.h / s.w)
+            return KFAC_ERR_INVALID_VALUE;
         Im2colLayer& L = layers[i];
         L = Im2colLayer{x[i], a[i], s.c, s.h, s.w, rows, tiles, s.kh, s.kw, s.sh, s.sw, s.ph, s.pw, s.dh, s.dw,
                         (int32_t)oh, (int32_t)ow, (int32_t)cols, s.ones, (int32_t)ceil_div(cols, kLayerTile), 0};
+        if (s.kh == 1 && s.kw == 1 && s.sh == 1 && s.sw == 1 && s.ph == 0 && s.pw == 0 && (s.h * s.w) % 4 == 0 &&
+            aligned(x[i], 4 * esz))
+            L.vec |= kVecIn;
+        if (cols % 4 == 0 && aligned(a[i], 4 * esz)) L.vec |= kVecOut;
         tiles += ceil_div(rows, kLayerTile) * L.tiles_c;
     }
     const size_t need = kfac_im2col_workspace_size(n);
@@ -554,7 +560,9 @@ kfac_status_t kfac_grad_rows(int n, const void* const* gy, const int64_t* batch,
         const int64_t tc = ceil_div(ch[i], kLayerTile);
         const int64_t tp = hw[i] == 1 ? ceil_div(batch[i], kLayerTile) : ceil_div(hw[i], kLayerTile);
         if (tc > INT32_MAX || tp > INT32_MAX) return KFAC_ERR_INVALID_VALUE;
-        layers[i] = GradRowsLayer{gy[i], g[i], batch[i], ch[i], hw[i], tiles, (int32_t)tc, (int32_t)tp};
+        layers[i] = GradRowsLayer{gy[i], g[i], batch[i], ch[i], hw[i], tiles, (int32_t)tc, (int32_t)tp, 0, 0};
+        if (hw[i] % 4 == 0 && aligned(gy[i], 4 * esz)) layers[i].vec |= kVecIn;
+        if (ch[i] % 4 == 0 && aligned(g[i], 4 * esz)) layers[i].vec |= kVecOut;
         tiles += hw[i] == 1 ? tp * tc : batch[i] * tc * tp;
     }
     const size_t need = kfac_grad_rows_workspace_size(n);

@@ -21,6 +21,12 @@ CASES = [  # (n, c, h, w), kernel, stride, padding, dilation, ones
     ((2, 3, 56, 56), (7, 7), (2, 2), (3, 3), (1, 1), False),
     ((5, 130, 9, 11), (3, 3), (2, 2), (1, 1), (1, 1), True),
     ((37, 1025, 1, 1), (1, 1), (1, 1), (0, 0), (1, 1), True),   # a fully connected layer with bias
+    # four-element gathers (1 x 1, stride 1, h w % 4 == 0) and writes (columns % 4 == 0)
+    ((3, 64, 14, 14), (1, 1), (1, 1), (0, 0), (1, 1), False),   # both; 588 rows, a ragged row tile
+    ((2, 130, 6, 6), (1, 1), (1, 1), (0, 0), (1, 1), True),     # gather only: 131 columns
+    ((2, 68, 5, 5), (3, 3), (1, 1), (1, 1), (1, 1), False),     # write only: 612 columns
+    ((3, 72, 7, 7), (1, 1), (1, 1), (0, 0), (1, 1), False),     # write only: h w = 49
+    ((32, 1024, 1, 1), (1, 1), (1, 1), (0, 0), (1, 1), False),  # fully connected, no bias: both
 ]
 
 
@@ -88,11 +94,30 @@ def test_im2col_resnet50_conv1_full_size():
         np.testing.assert_array_equal(got[ni * per:(ni + 1) * per], oracle.im2col(x[ni:ni + 1], *s.values()))
 
 
+@pytest.mark.parametrize("shp,k,st,pd", [((32, 64, 56, 56), (1, 1), (1, 1), (0, 0)),
+                                         ((32, 128, 28, 28), (3, 3), (1, 1), (1, 1)),
+                                         ((32, 256, 56, 56), (1, 1), (2, 2), (0, 0))])
+def test_im2col_resnet50_layers_full_size(shp, k, st, pd):
+    """ResNet-50 bottleneck convolutions at batch 32 (a 1 x 1, a 3 x 3 and a
+    stride-2 shortcut): the rows of three samples against the oracle."""
+    rng = np.random.default_rng(55)
+    say("im2col full size", shp, k, st, pd)
+    x = rng.standard_normal(shp).astype(np.float32)
+    s = shape_dict(k, st, pd, (1, 1), False)
+    (got,) = gpu_im2col([to_dev(x)], [s])
+    oh, ow = la.conv_out_hw(shp[2], shp[3], *k, st, pd)
+    per = oh * ow
+    assert got.shape == (shp[0] * per, shp[1] * k[0] * k[1])
+    for ni in (0, 13, 31):
+        np.testing.assert_array_equal(got[ni * per:(ni + 1) * per], oracle.im2col(x[ni:ni + 1], *s.values()))
+
+
 @pytest.mark.parametrize("bf16", [False, True])
 def test_grad_rows(bf16):
     import torch
     rng = np.random.default_rng(54)
-    shapes = [(4, 64, 28, 28), (8, 10), (3, 130, 7, 9), (130, 70), (2, 5, 1, 1), (1, 3, 65, 3)]
+    shapes = [(4, 64, 28, 28), (8, 10), (3, 130, 7, 9), (130, 70), (2, 5, 1, 1), (1, 3, 65, 3),
+              (2, 132, 10, 10), (3, 66, 8, 8), (2, 12, 7, 7)]
     gys = [inputs(rng, s, bf16) for s in shapes]
     scale = 37.0
     outs = []
