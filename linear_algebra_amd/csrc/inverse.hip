@@ -415,26 +415,25 @@ __device__ __forceinline__ double rsqrt_refined(double x) {
 constexpr int SB = 16;          // strip height and leaf block edge
 constexpr int NS = B / SB;      // strips per diagonal block
 
-// LDS scratch of factor_diagonal: 1 / U_cc of every pivot, one failure
-// slot per strip.
+// LDS scratch of factor_diagonal: the pivot row being broadcast, one
+// failure slot per strip.
 struct PanelScratch {
-    double row[B];      // the current pivot row of the strip being factored
-    double ydiag[B];
+    alignas(16) double row[B];   // the current pivot row of the strip being factored
     int fail[NS];
 };
 
 // acc += (neg ? -1 : 1) A B over K = 16 for 16 x 16 blocks in LDS (row
 // stride LD): A[i][k] = X[xr + i][xc + k], or X[xr + k][xc + i] when `at`;
-// B[k][j] = Y[yr + k][yc + j].  Lane l feeds A[l % 16][4c + l / 16] and
+// B[k][j] = Y[yr + k][yc + j], or Y[yr + j][yc + k] when `bt`.  Lane l feeds A[l % 16][4c + l / 16] and
 // B[4c + l / 16][l % 16] to k-chunk c of v_mfma_f64_16x16x4f64.
 __device__ __forceinline__ void mm16(doublex4& acc, const double* X, int xr, int xc, bool at, const double* Y,
-                                     int yr, int yc, bool neg) {
+                                     int yr, int yc, bool neg, bool bt = false) {
     const int l = threadIdx.x & 63, li = l & 15, lk = l >> 4;
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
         const int k = 4 * kc + lk;
         double a = at ? X[(xr + k) * LD + xc + li] : X[(xr + li) * LD + xc + k];
-        const double b = Y[(yr + k) * LD + yc + li];
+        const double b = bt ? Y[(yr + li) * LD + yc + k] : Y[(yr + k) * LD + yc + li];
         if (neg) a = -a;
         acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc, 0, 0, 0);
     }
@@ -461,28 +460,47 @@ __device__ __forceinline__ doublex4 zero4() {
 // u[0..15], so the strip's own diagonal block sits in lanes 0..15; the
 // wrapped lanes (columns left of the strip) carry values nobody reads.
 // Pivot c takes the diagonal entry from lane c, scales row c by its inverse
-// square root (stored as ydiag = 1 / U_cc) and subtracts the rank-one update
-// from the rows below.  Row c + 1 gets its update first, through a
-// cross-lane read, so that pivot c + 1's square-root chain runs beside the
-// other rows' updates, which read row c back from LDS (same address in
-// every lane).  Returns the 1-based column of the first pivot that is not
-// positive or not finite, or 0.
-__device__ __forceinline__ int strip_factor(double (&u)[SB], PanelScratch& S, int s, int j) {
+// square root and subtracts the rank-one update from the rows below.  Row
+// c + 1 gets its update first, through a cross-lane read, so that pivot
+// c + 1's square-root chain runs beside the other rows' updates, which read
+// row c back from LDS (same address in every lane, all reads in flight at
+// once).
+//
+// The same rows of U give the inverse of the strip's diagonal block,
+// V = U_ss^-1, by forward elimination on V U = I: lane i keeps row i % 16 of
+// V in x[0..15] (starting as that row of the identity); after pivot c,
+// x[c] *= 1 / U_cc and x[t] -= x[c] U_ct for t > c.  This rides on the
+// pivot loop's reads of row c and fills the issue slots the square-root
+// chain leaves idle.  Returns the 1-based column of the first pivot that is
+// not positive or not finite, or 0.
+__device__ __forceinline__ int strip_factor(double (&u)[SB], double (&x)[SB], PanelScratch& S, int s, int j) {
     int failed = 0;
     double piv = readlane_f64(u[0], 0);
     double yc = rsqrt_refined(piv);
 #pragma unroll
+    for (int c = 0; c < SB; ++c) x[c] = ((j & (SB - 1)) == c) ? 1.0 : 0.0;
+#pragma unroll
     for (int c = 0; c < SB; ++c) {
         failed = (failed == 0 && !(piv > 0.0 && piv <= DBL_MAX)) ? SB * s + c + 1 : failed;
-        S.ydiag[SB * s + c] = yc;   // every lane, same value: no branch per pivot
         u[c] *= yc;   // lane c holds the pivot itself: U_cc = piv / sqrt(piv)
+        x[c] *= yc;
         if (c + 1 < SB) {
             if (c + 2 < SB) S.row[j] = u[c];
-            u[c + 1] = fma(-readlane_f64(u[c], c + 1), u[c], u[c + 1]);
+            const double r1 = readlane_f64(u[c], c + 1);   // U_c,c+1
+            u[c + 1] = fma(-r1, u[c], u[c + 1]);
+            x[c + 1] = fma(-r1, x[c], x[c + 1]);
+            // row c in pairs, every read in flight at once
+            double2 rp[SB / 2];
+#pragma unroll
+            for (int p = (c + 2) / 2; p < SB / 2; ++p) rp[p] = reinterpret_cast<const double2*>(S.row)[p];
             const double pn = readlane_f64(u[c + 1], c + 1);
             const double yn = rsqrt_refined(pn);
 #pragma unroll
-            for (int t = c + 2; t < SB; ++t) u[t] = fma(-S.row[t], u[c], u[t]);
+            for (int t = c + 2; t < SB; ++t) {
+                const double rt = (t & 1) ? rp[t / 2].y : rp[t / 2].x;   // U_ct
+                u[t] = fma(-rt, u[c], u[t]);
+                x[t] = fma(-rt, x[c], x[t]);
+            }
             piv = pn;
             yc = yn;
         }
@@ -493,33 +511,19 @@ __device__ __forceinline__ int strip_factor(double (&u)[SB], PanelScratch& S, in
     return failed;
 }
 
-// V_qq = U_qq^-1 of strip q's 16 x 16 diagonal block, lane j < 16 computing
-// column SB*q + j: solves U V = I from the last row up; row t is scaled by
-// 1 / U_tt and then eliminated from the rows above.  U_qq is read from P
-// (same address in every lane); V_qq is written into the diagonal block
-// (q, q) of Q.
-__device__ __forceinline__ void leaf_inverse(const double* P, const double* ydiag, int q, int j, double* Q) {
-    const double* yq = ydiag + SB * q;
-    double v[SB];
+// Block (i, c) of V = U^-1 from the blocks of V to its left and the
+// diagonal block V_cc (V U = I):  V_ic = -(sum_{i <= m < c} V_im U_mc) V_cc.
+// The sum is formed transposed, sum U_mc^T V_im^T, whose accumulator holds
+// the sum itself in the A-operand layout of the final product with V_cc.
+__device__ __forceinline__ void v_block(const double* P, double* Q, int i, int c) {
+    const int l = threadIdx.x & 63, li = l & 15, lk = l >> 4;
+    doublex4 t = zero4();
+    for (int m = i; m < c; ++m) mm16(t, P, SB * m, SB * c, true, Q, SB * i, SB * m, false, true);
+    doublex4 v = zero4();
 #pragma unroll
-    for (int k = 0; k < SB; ++k) v[k] = (j == k) ? 1.0 : 0.0;
-#pragma unroll
-    for (int t = SB - 1; t >= 0; --t) {
-        // U_qq[k][t] = P[off + k * LD + t]; the offset is tied to the
-        // previous step's result so that the reads of a step cannot be
-        // hoisted further than one step ahead (all 120 of them live at once
-        // would not fit in registers)
-        int off = SB * q * (LD + 1);
-        if (t + 1 < SB) asm volatile("" : "+s"(off) : "v"(v[t + 1]));
-        v[t] *= yq[t];
-#pragma unroll
-        for (int k = 0; k < t; ++k) v[k] = fma(-P[off + k * LD + t], v[t], v[k]);
-    }
-    if (j < SB) {
-        double* V = Q + SB * q * (LD + 1);
-#pragma unroll
-        for (int k = 0; k < SB; ++k) V[k * LD + j] = v[k];
-    }
+    for (int kc = 0; kc < 4; ++kc)
+        v = __builtin_amdgcn_mfma_f64_16x16x4f64(-t[kc], Q[(SB * c + 4 * kc + lk) * LD + SB * c + li], v, 0, 0, 0);
+    store16(v, Q, SB * i, SB * c);
 }
 
 // Cholesky P = U^T U and V = U^-1 of the 64 x 64 diagonal block in LDS
@@ -527,10 +531,10 @@ __device__ __forceinline__ void leaf_inverse(const double* P, const double* ydia
 // P is left holding U in its upper blocks and scratch below).  Recursive in
 // 16-row strips: wave s factors strip s in registers (no block barrier per
 // pivot), then all waves subtract the strip's product from the trailing
-// 16 x 16 blocks on the matrix cores.  While wave s + 1 factors its strip,
-// wave s inverts its own 16 x 16 leaf.  The leaves are joined by two levels
-// of doubling, V_12 = -V_11 (U_12 V_22), as 16 x 16 block products; the
-// inner products are parked in P's lower blocks.  Returns the 1-based column
+// 16 x 16 blocks on the matrix cores.  Each strip's wave also inverts its
+// 16 x 16 diagonal block as it factors it; while strip s is factored, the
+// other waves form block column s - 1 of V from the columns before it, and
+// the last column follows the last strip.  Returns the 1-based column
 // of the first pivot that is not positive or not finite, or 0 (in every
 // thread).
 __device__ int factor_diagonal(double* P, double* Q, PanelScratch& S) {
@@ -551,12 +555,19 @@ __device__ int factor_diagonal(double* P, double* Q, PanelScratch& S) {
             const int col = (SB * s + j) & (B - 1);
 #pragma unroll
             for (int c = 0; c < SB; ++c) u[c] = P[(SB * s + c) * LD + col];
-            const int f = strip_factor(u, S, s, j);
+            double x[SB];
+            const int f = strip_factor(u, x, S, s, j);
 #pragma unroll
             for (int c = 0; c < SB; ++c) P[(SB * s + c) * LD + col] = u[c];
+            // row j % 16 of V_ss into the diagonal block (s, s) of Q; the four
+            // lanes of a row store the same values (no branch: behind one,
+            // the compiler would defer the eliminations to the store and
+            // keep every pivot row live until then)
+#pragma unroll
+            for (int c = 0; c < SB; ++c) Q[(SB * s + (j & (SB - 1))) * LD + SB * s + c] = x[c];
             if (j == 0) S.fail[s] = f;
-        } else if (w == s - 1) {
-            leaf_inverse(P, S.ydiag, w, j, Q);
+        } else if (w + 1 < s) {
+            v_block(P, Q, w, s - 1);   // column s - 1 of V, beside strip s
         }
         __syncthreads();
         if (s + 1 < NS) {
@@ -577,57 +588,8 @@ __device__ int factor_diagonal(double* P, double* Q, PanelScratch& S) {
             __syncthreads();
         }
     }
-    if (w == NS - 1) leaf_inverse(P, S.ydiag, w, j, Q);
-    __syncthreads();
-    // doubling, 16 -> 32: V_01, V_23; and T_02 = U_02 V_22, T_12 = U_12 V_22
-    // parked in P's blocks (2, 0), (2, 1)
-    {
-        doublex4 t = zero4(), v = zero4();
-        if (w == 0 || w == 1) {
-            const int o = 32 * w;   // pair (0, 1) or (2, 3)
-            mm16(t, P, o, o + 16, false, Q, o + 16, o + 16, false);          // T = U_ab V_bb
-            const int l = threadIdx.x & 63, li = l & 15, lk = l >> 4;
-#pragma unroll
-            for (int kc = 0; kc < 4; ++kc)                                      // V_ab = -V_aa T
-                v = __builtin_amdgcn_mfma_f64_16x16x4f64(-Q[(o + li) * LD + o + 4 * kc + lk], t[kc], v, 0, 0, 0);
-            store16(v, Q, o, o + 16);
-        } else {
-            const int a = w - 2;    // T_a2 = U_a2 V_22
-            mm16(t, P, 16 * a, 32, false, Q, 32, 32, false);
-            store16(t, P, 32, 16 * a);
-        }
-    }
-    __syncthreads();
-    // 32 -> 64, first half: T_03, T_13 parked in (3, 0), (3, 1); V_12, V_02
-    {
-        doublex4 t = zero4();
-        if (w <= 1) {
-            const int a = w;        // T_a3 = U_a2 V_23 + U_a3 V_33
-            mm16(t, P, 16 * a, 32, false, Q, 32, 48, false);
-            mm16(t, P, 16 * a, 48, false, Q, 48, 48, false);
-            store16(t, P, 48, 16 * a);
-        } else if (w == 2) {        // V_12 = -V_11 T_12
-            mm16(t, Q, 16, 16, false, P, 32, 16, true);
-            store16(t, Q, 16, 32);
-        } else {                    // V_02 = -(V_00 T_02 + V_01 T_12)
-            mm16(t, Q, 0, 0, false, P, 32, 0, true);
-            mm16(t, Q, 0, 16, false, P, 32, 16, true);
-            store16(t, Q, 0, 32);
-        }
-    }
-    __syncthreads();
-    // second half: V_03 = -(V_00 T_03 + V_01 T_13), V_13 = -V_11 T_13
-    {
-        doublex4 t = zero4();
-        if (w == 0) {
-            mm16(t, Q, 0, 0, false, P, 48, 0, true);
-            mm16(t, Q, 0, 16, false, P, 48, 16, true);
-            store16(t, Q, 0, 48);
-        } else if (w == 1) {
-            mm16(t, Q, 16, 16, false, P, 48, 16, true);
-            store16(t, Q, 16, 48);
-        }
-    }
+    // the last column of V
+    if (w + 1 < NS) v_block(P, Q, w, NS - 1);
     __syncthreads();
     // strips are factored in order, so the first failure is the smallest code
     int f = 0;
