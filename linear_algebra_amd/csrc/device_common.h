@@ -6,6 +6,15 @@
 
 namespace kfac {
 
+// A pointer into global memory as such, so that its accesses are global
+// (not flat) instructions: they count only against the vector-memory wait
+// counter, and a wait for LDS or scalar loads does not also wait for them.
+template <typename T>
+__device__ __forceinline__ __attribute__((address_space(1))) T* as_global(T* p) {
+    return (__attribute__((address_space(1))) T*)p;
+}
+
+
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef double doublex4 __attribute__((ext_vector_type(4)));
 

@@ -7,7 +7,7 @@
 //
 // Tile 128 x 128 per workgroup of 4 waves (2 x 2, 64 x 64 each, four
 // v_mfma_f32_32x32x2f32 accumulators per wave).  K is staged through two LDS
-// buffers of 16 rows per operand; the next slab is fetched into registers
+// buffers of kGemmBK rows per operand; the next slab is fetched into registers
 // while the current one feeds the matrix cores.  Products are summed in
 // float32 over sub-chunks of kGemmSubK rows and then folded into a second
 // float32 sum, which keeps the rounding error of long reductions (hundreds of
@@ -16,8 +16,8 @@
 // Operands are read with buffer loads whose descriptor covers one K-slab:
 // rows past the end of the input read as zero without a branch, and the
 // per-thread offsets inside a slab are computed once.  LDS holds each slab
-// as [m][k] with k contiguous, so a lane fetches its eight k-values of a
-// block with two 128-bit reads and the slab's 32 MFMAs issue back to back.
+// as [m][k] with k contiguous, so a lane fetches its k-values of a block
+// with 128-bit reads and the slab's MFMAs issue back to back.
 #include "device_common.h"
 #include "internal.h"
 
@@ -29,7 +29,9 @@ constexpr int BK = kGemmBK;
 constexpr int NT = kGemmThreads;
 constexpr int kGemmRun = 16;        // items per XCD run in large launches
 constexpr int64_t kGemmRunsMin = 2048;
-constexpr int LOADS = BK * BM / NT;  // elements of one operand slab per thread (8)
+constexpr int LOADS = BK * BM / NT;  // elements of one operand slab per thread
+constexpr int KPL = BK / 2;          // slab rows each lane feeds to the matrix cores
+static_assert(LOADS % 4 == 0 && KPL % 4 == 0, "slabs move in float4 pieces");
 constexpr int SUB_STAGES = kGemmSubK / BK;
 
 template <bool BF16>
@@ -164,8 +166,8 @@ __global__ __launch_bounds__(NT, 2) void gemm_tn_kernel(GemmLaunch L, int64_t it
     const int wm = wave >> 1, wn = wave & 1;
     const bool active = W.active;
 
-    // Thread t loads column lc of the tile, slab rows lr8 .. lr8+7; the byte
-    // offsets inside a slab are the same for every slab.
+    // Thread t loads column lc of the tile, slab rows lr8 .. lr8 + LOADS - 1;
+    // the byte offsets inside a slab are the same for every slab.
     const int lc = tid & (BM - 1);
     const int lr8 = (tid >> 7) * LOADS;
     uint32_t offa[LOADS], offb[LOADS];
@@ -189,12 +191,12 @@ __global__ __launch_bounds__(NT, 2) void gemm_tn_kernel(GemmLaunch L, int64_t it
     };
     auto sstore = [&](int buf) {
         float4* da = reinterpret_cast<float4*>(&As[buf][lc * LDK + lr8]);
-        da[0] = make_float4(ra[0], ra[1], ra[2], ra[3]);
-        da[1] = make_float4(ra[4], ra[5], ra[6], ra[7]);
+#pragma unroll
+        for (int q = 0; q < LOADS / 4; ++q) da[q] = make_float4(ra[4 * q], ra[4 * q + 1], ra[4 * q + 2], ra[4 * q + 3]);
         if (!same) {
             float4* db = reinterpret_cast<float4*>(&Bs[buf][lc * LDK + lr8]);
-            db[0] = make_float4(rb[0], rb[1], rb[2], rb[3]);
-            db[1] = make_float4(rb[4], rb[5], rb[6], rb[7]);
+#pragma unroll
+            for (int q = 0; q < LOADS / 4; ++q) db[q] = make_float4(rb[4 * q], rb[4 * q + 1], rb[4 * q + 2], rb[4 * q + 3]);
         }
     };
 
@@ -214,10 +216,10 @@ __global__ __launch_bounds__(NT, 2) void gemm_tn_kernel(GemmLaunch L, int64_t it
     __syncthreads();
 
     // MFMA fragments: lane l supplies rows/columns (l % 32) of its 32-wide
-    // blocks and, over the 8 steps s of a slab, the slab rows 8*(l/32) + s
+    // blocks and, over the KPL steps s of a slab, the slab rows KPL*(l/32) + s
     // (the sum over the slab does not depend on how its rows are paired).
     const int fr = lane & 31;
-    const int fk = (lane >> 5) * 8;
+    const int fk = (lane >> 5) * KPL;
 
     for (int st = 0; st < nstages; ++st) {
         const int buf = st & 1;
@@ -225,18 +227,19 @@ __global__ __launch_bounds__(NT, 2) void gemm_tn_kernel(GemmLaunch L, int64_t it
         if (active) {
             const float* Ab = As[buf];
             const float* Bb = same ? As[buf] : Bs[buf];
-            float4 fa[2][2], fb[2][2];
+            float4 fa[2][KPL / 4], fb[2][KPL / 4];
 #pragma unroll
             for (int a = 0; a < 2; ++a) {
                 const float4* pa = reinterpret_cast<const float4*>(&Ab[(wm * 64 + a * 32 + fr) * LDK + fk]);
-                fa[a][0] = pa[0];
-                fa[a][1] = pa[1];
                 const float4* pb = reinterpret_cast<const float4*>(&Bb[(wn * 64 + a * 32 + fr) * LDK + fk]);
-                fb[a][0] = pb[0];
-                fb[a][1] = pb[1];
+#pragma unroll
+                for (int q = 0; q < KPL / 4; ++q) {
+                    fa[a][q] = pa[q];
+                    fb[a][q] = pb[q];
+                }
             }
 #pragma unroll
-            for (int s = 0; s < BK / 2; ++s) {
+            for (int s = 0; s < KPL; ++s) {
                 const float a0 = fa[0][s >> 2][s & 3], a1 = fa[1][s >> 2][s & 3];
                 const float b0 = fb[0][s >> 2][s & 3], b1 = fb[1][s >> 2][s & 3];
                 acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);

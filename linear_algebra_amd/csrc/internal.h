@@ -29,7 +29,7 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 //   precondition:   S^T = grad^T Z_G  (Aop = grad, Bop = Z_G)  and
 //                   P   = (S^T)^T Z_A (Aop = S^T,  Bop = Z_A).
 constexpr int kGemmTile = 128;     // output tile edge (BM = BN)
-constexpr int kGemmBK = 16;        // rows of each operand staged per LDS buffer
+constexpr int kGemmBK = 32;        // rows of each operand staged per LDS buffer
 constexpr int kGemmThreads = 256;  // 4 waves, 2 x 2 over the tile, 64 x 64 each
 constexpr int kGemmSubK = 512;     // rows accumulated before folding into the running sum
 

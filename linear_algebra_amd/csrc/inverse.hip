@@ -74,7 +74,7 @@ struct Blk {
 __device__ __forceinline__ void fetch(double (&v)[PER], const Blk& b) {
     const int r0 = threadIdx.x >> 6, c = threadIdx.x & 63;
 #pragma unroll
-    for (int s = 0; s < PER; ++s) v[s] = b.p[(int64_t)(r0 + 4 * s) * b.ld + c];
+    for (int s = 0; s < PER; ++s) v[s] = as_global(b.p)[(int64_t)(r0 + 4 * s) * b.ld + c];
 }
 __device__ __forceinline__ void put(double* S, const double (&v)[PER], bool trans) {
     const int r0 = threadIdx.x >> 6, c = threadIdx.x & 63;
@@ -128,11 +128,11 @@ __device__ __forceinline__ void fetch_half(double (&v)[HPER], const Blk& b, int 
     if (!b.trans) {
         const int c = KH * h + (t & 31), r = t >> 5;
 #pragma unroll
-        for (int s = 0; s < HPER; ++s) v[s] = b.p[(int64_t)(r + 8 * s) * b.ld + c];
+        for (int s = 0; s < HPER; ++s) v[s] = as_global(b.p)[(int64_t)(r + 8 * s) * b.ld + c];
     } else {
         const int c = t & 63, r = KH * h + (t >> 6);
 #pragma unroll
-        for (int s = 0; s < HPER; ++s) v[s] = b.p[(int64_t)(r + 4 * s) * b.ld + c];
+        for (int s = 0; s < HPER; ++s) v[s] = as_global(b.p)[(int64_t)(r + 4 * s) * b.ld + c];
     }
 }
 __device__ __forceinline__ void put_half(double* S, const double (&v)[HPER], bool trans) {
@@ -386,10 +386,10 @@ __device__ __forceinline__ void acc_zero(doublex4 (&acc)[2][2]) {
     for_acc([&](int a, int b, int r, int, int) { acc[a][b][r] = 0.0; });
 }
 __device__ __forceinline__ void acc_load(doublex4 (&acc)[2][2], const double* G, int64_t ld) {
-    for_acc([&](int a, int b, int r, int row, int col) { acc[a][b][r] = G[(int64_t)row * ld + col]; });
+    for_acc([&](int a, int b, int r, int row, int col) { acc[a][b][r] = as_global(G)[(int64_t)row * ld + col]; });
 }
 __device__ __forceinline__ void acc_store(const doublex4 (&acc)[2][2], double* G, int64_t ld) {
-    for_acc([&](int a, int b, int r, int row, int col) { G[(int64_t)row * ld + col] = acc[a][b][r]; });
+    for_acc([&](int a, int b, int r, int row, int col) { as_global(G)[(int64_t)row * ld + col] = acc[a][b][r]; });
 }
 __device__ __forceinline__ void acc_to_lds(const doublex4 (&acc)[2][2], double* S) {
     for_acc([&](int a, int b, int r, int row, int col) { S[row * LD + col] = acc[a][b][r]; });
@@ -604,9 +604,9 @@ __device__ int factor_diagonal(double* P, double* Q, PanelScratch& S) {
 __device__ __forceinline__ void record_info(const InvMat& M, int k, int f) {
     if (threadIdx.x != 0) return;
     if (k == 0) {
-        *M.info = f;
-    } else if (f && *M.info == 0) {
-        *M.info = k * B + f;
+        *as_global(M.info) = f;
+    } else if (f && *as_global(M.info) == 0) {
+        *as_global(M.info) = k * B + f;
     }
 }
 
@@ -626,7 +626,7 @@ __global__ __launch_bounds__(NT) void inv_prepare_kernel(InvLaunch L, int64_t ti
 #pragma unroll
     for (int s = 0; s < PER; ++s) {
         const int64_t i = (int64_t)bi * B + r0 + 4 * s, j = (int64_t)bj * B + c;
-        xv[s] = (i < d && j < d && j >= i) ? M.x[i * d + j] : 0.0f;
+        xv[s] = (i < d && j < d && j >= i) ? as_global(M.x)[i * d + j] : 0.0f;
     }
 #pragma unroll
     for (int s = 0; s < PER; ++s) {
@@ -638,7 +638,7 @@ __global__ __launch_bounds__(NT) void inv_prepare_kernel(InvLaunch L, int64_t ti
         } else {
             v = (i == j) ? 1.0 : 0.0;  // identity padding
         }
-        M.w[i * D + j] = v;
+        as_global(M.w)[i * D + j] = v;
     }
 }
 
@@ -658,14 +658,20 @@ __device__ __forceinline__ void potrf_row_block(const InvLaunch& L, const InvMat
     const int J = k + 1 + (int)local;
     double* Wkk = M.w + (int64_t)k * B * D + (int64_t)k * B;
     double* Wkj = M.w + (int64_t)k * B * D + (int64_t)J * B;
+    // Every block this workgroup reads is requested before the first wait,
+    // the panel blocks of step k - 1 first.  The requests are unconditional
+    // (a branch around them would end in a wait for all of them): without
+    // a block right of the diagonal, or at step 0, they read blocks of the
+    // matrix that are then not used.
+    const int Jr = has_right ? J : k;
+    const double* prev = M.w + (int64_t)(k > 0 ? k - 1 : 0) * B * D;
+    double ra[PER], rb[PER];
+    fetch(ra, Blk{prev + (int64_t)k * B, D, true});
+    fetch(rb, Blk{prev + (int64_t)Jr * B, D, true});
     doublex4 dk[2][2], wj[2][2];
     acc_load(dk, Wkk, D);
-    if (has_right) acc_load(wj, Wkj, D);
+    acc_load(wj, M.w + (int64_t)k * B * D + (int64_t)Jr * B, D);
     if (k > 0) {
-        const double* prev = M.w + (int64_t)(k - 1) * B * D;
-        double ra[PER], rb[PER];
-        fetch(ra, Blk{prev + (int64_t)k * B, D, true});
-        if (has_right) fetch(rb, Blk{prev + (int64_t)J * B, D, true});
         put(As, ra, true);
         if (has_right) put(Bs, rb, true);
         __syncthreads();
@@ -680,7 +686,7 @@ __device__ __forceinline__ void potrf_row_block(const InvLaunch& L, const InvMat
 #pragma unroll
         for (int s = 0; s < PER; ++s) {
             const int r = r0 + 4 * s;
-            M.dinv[(int64_t)k * BB + r * B + c] = As[r * LD + c];
+            as_global(M.dinv)[(int64_t)k * BB + r * B + c] = As[r * LD + c];
         }
         record_info(M, k, f);
     }
@@ -747,8 +753,11 @@ __global__ __launch_bounds__(NT, 2) void inv_step_kernel(InvLaunch L, int64_t ti
 // above a power of two): depth d = D - 1 - step, node n covers
 // [n nb / 2^d, (n + 1) nb / 2^d) and joins its children G1 = [lo, mid),
 // G2 = [mid, hi) in s2 x s2 slots, of which those beyond |G1| x |G2| have
-// no work.  The slot is block (I, J), I in G1, J in G2.
-__device__ __forceinline__ bool trtri_decode(int64_t local, int nb, int step, int& I, int& J, int& g1_end) {
+// no work.  The slot is block (I, J), I in G1, J in G2, in row-major order,
+// or with `desc_j` column by column from the last column of G2 (the longest
+// products of the first trtri launch first).
+__device__ __forceinline__ bool trtri_decode(int64_t local, int nb, int step, int& I, int& J, int& g1_end,
+                                             bool desc_j) {
     if (trtri_balanced(nb)) {
         int D = 0;
         while ((1 << D) < nb) ++D;
@@ -756,7 +765,8 @@ __device__ __forceinline__ bool trtri_decode(int64_t local, int nb, int step, in
         const int s2 = (nb + (1 << (d + 1)) - 1) >> (d + 1);
         const int n = (int)(local / ((int64_t)s2 * s2));
         const int r = (int)(local % ((int64_t)s2 * s2));
-        const int bi = r / s2, bj = r % s2;
+        const int bi = desc_j ? r % s2 : r / s2;
+        const int bj = desc_j ? s2 - 1 - r / s2 : r % s2;
         const int lo = (int)(((int64_t)n * nb) >> d);
         const int mid = (int)(((int64_t)(2 * n + 1) * nb) >> (d + 1));
         const int hi = (int)(((int64_t)(n + 1) * nb) >> d);
@@ -773,14 +783,14 @@ __device__ __forceinline__ bool trtri_decode(int64_t local, int nb, int step, in
     if (local / hh < full) {
         m = (int)(local / hh);
         const int r = (int)(local % hh);
-        bi = r / h;
-        bj = r % h;
+        bi = desc_j ? r % h : r / h;
+        bj = desc_j ? h - 1 - r / h : r % h;
     } else {
         m = full;
         const int r = (int)(local - (int64_t)full * hh);
         const int w2 = nb % g - h;
-        bi = r / w2;
-        bj = r % w2;
+        bi = desc_j ? r % h : r / w2;
+        bj = desc_j ? w2 - 1 - r / h : r % w2;
     }
     I = m * g + bi;
     J = m * g + h + bj;
@@ -797,7 +807,7 @@ __global__ __launch_bounds__(NT) void inv_trtri_a_kernel(InvLaunch L, int64_t ti
     if (item >= tiles || !locate(L, kInvTrtri, item, mi, local)) return;
     const InvMat M = L.mats[mi];
     int I, J, g1_end;
-    if (!trtri_decode(local, M.nb, L.step, I, J, g1_end)) return;
+    if (!trtri_decode(local, M.nb, L.step, I, J, g1_end, true)) return;
     const int64_t D = (int64_t)M.nb * B;
     doublex4 acc[2][2];
     acc_zero(acc);
@@ -820,7 +830,7 @@ __global__ __launch_bounds__(NT) void inv_trtri_b_kernel(InvLaunch L, int64_t ti
     if (item >= tiles || !locate(L, kInvTrtri, item, mi, local)) return;
     const InvMat M = L.mats[mi];
     int I, J, g1_end;
-    if (!trtri_decode(local, M.nb, L.step, I, J, g1_end)) return;
+    if (!trtri_decode(local, M.nb, L.step, I, J, g1_end, false)) return;
     const int64_t D = (int64_t)M.nb * B;
     doublex4 acc[2][2];
     acc_zero(acc);
@@ -869,7 +879,7 @@ __global__ __launch_bounds__(NT) void inv_lauum_kernel(InvLaunch L, int64_t tile
         const int64_t i = r0 + r, j = c0 + c;
         if (i < d && j < d) {
             const double v = (I != J || c >= r) ? As[r * LD + c] : As[c * LD + r];
-            M.z[i * d + j] = (float)v;
+            as_global(M.z)[i * d + j] = (float)v;
         }
     }
     if (I != J) {
@@ -877,7 +887,7 @@ __global__ __launch_bounds__(NT) void inv_lauum_kernel(InvLaunch L, int64_t tile
         for (int s = 0; s < PER; ++s) {
             const int c = q0 + 4 * s, r = l;      // destination row c0+c, column r0+r
             const int64_t i = c0 + c, j = r0 + r;
-            if (i < d && j < d) M.z[i * d + j] = (float)As[r * LD + c];
+            if (i < d && j < d) as_global(M.z)[i * d + j] = (float)As[r * LD + c];
         }
     }
 }
@@ -928,13 +938,13 @@ __global__ __launch_bounds__(NT, 2) void inv_lauum2_kernel(InvLaunch L, int64_t 
     for (int r = 0; r < B; ++r) {
         const int c = l;
         const int64_t i = r0 + r, j = c0 + c;
-        if (i < d && j < d) M.z[i * d + j] = (I != J || c >= r) ? F[r * (B + 1) + c] : F[c * (B + 1) + r];
+        if (i < d && j < d) as_global(M.z)[i * d + j] = (I != J || c >= r) ? F[r * (B + 1) + c] : F[c * (B + 1) + r];
     }
     if (I != J) {
         for (int c = 0; c < B; ++c) {
             const int r = l;   // destination row c0 + c, column r0 + r
             const int64_t i = c0 + c, j = r0 + r;
-            if (i < d && j < d) M.z[i * d + j] = F[r * (B + 1) + c];
+            if (i < d && j < d) as_global(M.z)[i * d + j] = F[r * (B + 1) + c];
         }
     }
 }
