@@ -53,17 +53,25 @@ __device__ __forceinline__ int find_prob(const GemmProb* probs, int nprob, int64
     return lo;
 }
 
-// Epilogue for one output element (row i, column j of the problem).
-__device__ __forceinline__ void store_elem(const GemmProb& P, int i, int j, float v, float eps, int first) {
-    if (i >= P.M || j >= P.N) return;
-    if (P.mode == kModeFactor) {
-        if (j < i) return;
-        const float f = v * P.alpha;
-        float* dst = P.c + (int64_t)i * P.ldc + j;
-        *dst = first ? f : eps * (*dst) + (1.0f - eps) * f;
-    } else {
-        P.c[(int64_t)i * P.ldc + j] = v * P.alpha;
-    }
+// Epilogue of one output element (row i, column j of the problem): kept
+// when inside the problem (and on or above the diagonal for a factor), with
+// `prev` the element's value before the call.
+__device__ __forceinline__ bool elem_kept(const GemmProb& P, int i, int j) {
+    return i < P.M && j < P.N && (P.mode != kModeFactor || j >= i);
+}
+__device__ __forceinline__ float elem_value(const GemmProb& P, float v, float prev, float eps, int first) {
+    if (P.mode != kModeFactor) return v * P.alpha;
+    const float f = v * P.alpha;
+    return first ? f : eps * prev + (1.0f - eps) * f;
+}
+// The old value for the running average, read from element 0 when (i, j)
+// is not kept, so the read needs no branch.
+__device__ __forceinline__ float elem_prev(const GemmProb& P, int i, int j) {
+    const int64_t off = elem_kept(P, i, j) ? (int64_t)i * P.ldc + j : 0;
+    return as_global(P.c)[off];
+}
+__device__ __forceinline__ void elem_store(const GemmProb& P, int i, int j, float r) {
+    if (elem_kept(P, i, j)) as_global(P.c)[(int64_t)i * P.ldc + j] = r;
 }
 
 constexpr int LDK = BK + 4;        // LDS row stride (floats): [m][k], k contiguous
@@ -94,24 +102,46 @@ __device__ __forceinline__ float slab_load(__amdgpu_buffer_rsrc_t r, uint32_t of
 // Writes a finished 128 x 128 tile: to the split-K partial buffer when K is
 // split, else through the epilogue.  Output layout of a 32 x 32 MFMA block:
 // lane l holds column (l % 32); register r holds row 8*(r/4) + 4*(l/32) + (r%4).
+// The running average reads every old value of the thread's 64 elements,
+// then forms every result, then writes: with the reads, or the stores'
+// inputs, behind per-element branches, each store would wait for the
+// memory operations before it.
 __device__ __forceinline__ void store_tile(const GemmProb& P, const GemmLaunch& L, const floatx16 (&sum)[2][2],
                                            int kc, int t, int m0, int n0, int wm, int wn, int lane) {
     const int khalf = lane >> 5;
-    float* part = (P.ksplit > 1) ? P.part + ((int64_t)kc * P.ntiles + t) * (BM * BM) : nullptr;
+    auto row_of = [&](int a, int r) { return wm * 64 + a * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3); };
+    auto col_of = [&](int b) { return wn * 64 + b * 32 + (lane & 31); };
+    if (P.ksplit > 1) {
+        float* part = P.part + ((int64_t)kc * P.ntiles + t) * (BM * BM);
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) as_global(part)[row_of(a, r) * BM + col_of(b)] = sum[a][b][r];
+        return;
+    }
+    floatx16 res[2][2];
+    if (P.mode == kModeFactor && !L.first_step) {
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) res[a][b][r] = elem_prev(P, m0 + row_of(a, r), n0 + col_of(b));
+    }
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = wm * 64 + a * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
-                const int col = wn * 64 + b * 32 + (lane & 31);
-                if (part) {
-                    part[row * BM + col] = sum[a][b][r];
-                } else {
-                    store_elem(P, m0 + row, n0 + col, sum[a][b][r], L.eps, L.first_step);
-                }
-            }
+            for (int r = 0; r < 16; ++r) res[a][b][r] = elem_value(P, sum[a][b][r], res[a][b][r], L.eps, L.first_step);
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) elem_store(P, m0 + row_of(a, r), n0 + col_of(b), res[a][b][r]);
 }
 
 // Tile and K-chunk of a work item.
@@ -426,11 +456,15 @@ __global__ __launch_bounds__(NT) void gemm_reduce_kernel(GemmLaunch L, int64_t s
         s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
     }
     const float sv[4] = {s.x, s.y, s.z, s.w};
+    float res[4] = {0.f, 0.f, 0.f, 0.f};
+    if (P.mode == kModeFactor && !L.first_step) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int e = e0 + q;
-        store_elem(P, ti * BM + e / BM, tj * BM + e % BM, sv[q], L.eps, L.first_step);
+        for (int q = 0; q < 4; ++q) res[q] = elem_prev(P, ti * BM + (e0 + q) / BM, tj * BM + (e0 + q) % BM);
     }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) res[q] = elem_value(P, sv[q], res[q], L.eps, L.first_step);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) elem_store(P, ti * BM + (e0 + q) / BM, tj * BM + (e0 + q) % BM, res[q]);
 }
 
 }  // namespace

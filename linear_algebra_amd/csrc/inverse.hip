@@ -739,11 +739,18 @@ __global__ __launch_bounds__(NT, 2) void inv_step_kernel(InvLaunch L, int64_t ti
     const int64_t D = (int64_t)M.nb * B;
     double* Wij = M.w + (int64_t)I * B * D + (int64_t)J * B;
     const double* prev = M.w + (int64_t)(k - 1) * B * D;
+    // one 64-deep product: both panel blocks and the block being updated
+    // are requested at once (a single memory round trip), then multiplied
+    // from LDS
+    double ra[PER], rb[PER];
+    fetch(ra, Blk{prev + (int64_t)I * B, D, true});
+    if (I != J) fetch(rb, Blk{prev + (int64_t)J * B, D, true});
     doublex4 acc[2][2];
     acc_load(acc, Wij, D);
-    block_gemm(acc, S, 0, 1,
-               [&](int) { return Blk{prev + (int64_t)I * B, D, true}; },
-               [&](int) { return Blk{prev + (int64_t)J * B, D, true}; }, true, I == J);
+    put(As, ra, true);
+    if (I != J) put(Bs, rb, true);
+    __syncthreads();
+    mma_block(acc, As, I == J ? As : Bs, true);
     acc_store(acc, Wij, D);
 }
 
