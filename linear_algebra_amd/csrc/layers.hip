@@ -184,14 +184,21 @@ __global__ __launch_bounds__(NT) void grad_rows_kernel(const GradRowsLayer* laye
     const int64_t t = item - L.tile_begin;
     const int lx = threadIdx.x & 63, ly = threadIdx.x >> 6;
     const int q4 = threadIdx.x & 15, g16 = threadIdx.x >> 4;
-    if (L.hw == 1) {
+    if (L.hw == 1) {   // all loads first (from element 0 past the edges), then the stores
         const int64_t b0 = (t / L.tiles_c) * T;
         const int64_t c0 = (t % L.tiles_c) * T;
         const int64_t ci = c0 + lx;
-        if (ci >= L.c) return;
+        float v[T / 4];
+#pragma unroll
         for (int s = 0; s < T / 4; ++s) {
             const int64_t b = b0 + ly + 4 * s;
-            if (b < L.batch) store_val<BF16>(L.g, b * L.c + ci, scale * load_val<BF16>(L.gy, b * L.c + ci));
+            v[s] = load_val<BF16>(L.gy, (b < L.batch && ci < L.c) ? b * L.c + ci : 0);
+        }
+        if (ci >= L.c) return;
+#pragma unroll
+        for (int s = 0; s < T / 4; ++s) {
+            const int64_t b = b0 + ly + 4 * s;
+            if (b < L.batch) store_val<BF16>(L.g, b * L.c + ci, scale * v[s]);
         }
         return;
     }
@@ -262,13 +269,26 @@ __global__ __launch_bounds__(NT) void grad_matrix_kernel(const GradMatLayer* lay
     const GradMatLayer L = layers[find_layer(layers, n, item, &GradMatLayer::chunk_begin)];
     const int64_t total = L.d_out * L.cols;
     const int64_t e0 = (item - L.chunk_begin) * kGradMatChunk;
-    for (int s = 0; s < kGradMatChunk / NT; ++s) {
+    // every element read before any is written (a read after a write to a
+    // buffer that might alias would wait for it); reads past the end take
+    // element 0 of the source
+    constexpr int PER = kGradMatChunk / NT;
+    float* src[PER];
+    float v[PER];
+#pragma unroll
+    for (int s = 0; s < PER; ++s) {
+        const int64_t e = e0 + threadIdx.x + (int64_t)s * NT;
+        const int64_t ec = e < total ? e : 0;
+        const int64_t r = ec / L.cols, k = ec % L.cols;
+        src[s] = k < L.d_in ? L.w + r * L.d_in + k : L.b + r;
+        v[s] = pack ? *as_global(src[s]) : as_global(L.mat)[ec];
+    }
+#pragma unroll
+    for (int s = 0; s < PER; ++s) {
         const int64_t e = e0 + threadIdx.x + (int64_t)s * NT;
         if (e >= total) break;
-        const int64_t r = e / L.cols, k = e % L.cols;
-        float* src = k < L.d_in ? L.w + r * L.d_in + k : L.b + r;
-        if (pack) L.mat[e] = *src;
-        else *src = L.mat[e];
+        if (pack) as_global(L.mat)[e] = v[s];
+        else *as_global(src[s]) = v[s];
     }
 }
 
