@@ -137,3 +137,60 @@ def test_python_binding_refuses_cpu_tensors():
     m = torch.zeros(3, 3)
     with pytest.raises((ValueError, la.KfacLibraryError)):
         la.kfac_factors([x], [m], 0.95, True)
+
+
+def conv_shape(**kw):
+    """A valid kfac_conv_t (2 x 3 x 8 x 8 input, 3 x 3 kernel, padding 1)
+    with the given fields changed."""
+    c = la.KfacConv(2, 3, 8, 8, 3, 3, 1, 1, 1, 1, 1, 1, 0, 0)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_layer_entry_points_reject_bad_arguments(lib):
+    ws = ctypes.c_void_p(FAKE)
+    out = vps([FAKE])
+
+    def im2col(shape, n=1, dtype=0, wsb=1 << 20, x=None):
+        arr = (la.KfacConv * 1)(shape)
+        return lib.kfac_im2col(n, x if x is not None else vps([FAKE]), ctypes.cast(arr, ctypes.c_void_p), dtype,
+                               out, ws, wsb, None)
+
+    bad = la.KFAC_ERR_INVALID_VALUE
+    assert im2col(conv_shape(), n=0) == bad
+    assert im2col(conv_shape(), dtype=7) == bad
+    assert im2col(conv_shape(), x=vps([0])) == bad
+    assert im2col(conv_shape(), x=vps([FAKE + 2])) == bad           # not 4-byte aligned for float32
+    for field, value in [("n", 0), ("c", 0), ("kh", 0), ("sw", 0), ("ph", -1), ("dw", 0), ("ones", 2),
+                         ("reserved", 1)]:
+        assert im2col(conv_shape(**{field: value})) == bad, field
+    assert im2col(conv_shape(kh=11)) == bad                         # kernel wider than the padded input
+    assert im2col(conv_shape(c=1 << 20, h=1 << 11, w=1 << 11, kh=1, kw=1, ph=0, pw=0)) == bad   # c h w >= 2^31
+    assert im2col(conv_shape(n=1 << 20, c=64, h=64, w=64)) == bad   # more than 2^31 - 1 patch elements
+    assert im2col(conv_shape(), wsb=0) == la.KFAC_ERR_WORKSPACE
+
+    def grad_rows(batch=4, c=8, hw=9, dtype=0, scale=1.0, gy=None, wsb=1 << 20):
+        return lib.kfac_grad_rows(1, gy if gy is not None else vps([FAKE]), i64([batch]), i64([c]), i64([hw]),
+                                  dtype, ctypes.c_float(scale), out, ws, wsb, None)
+
+    assert grad_rows(batch=0) == bad
+    assert grad_rows(c=0) == bad
+    assert grad_rows(hw=0) == bad
+    assert grad_rows(dtype=3) == bad
+    assert grad_rows(scale=float("nan")) == bad
+    assert grad_rows(gy=vps([0])) == bad
+    assert grad_rows(wsb=0) == la.KFAC_ERR_WORKSPACE
+
+    def grad_matrix(d_out=4, d_in=6, direction=0, mat=None, wsb=1 << 20):
+        return lib.kfac_grad_matrix(1, vps([FAKE]), None, i64([d_out]), i64([d_in]),
+                                    mat if mat is not None else vps([FAKE]), direction, ws, wsb, None)
+
+    assert grad_matrix(d_out=0) == bad
+    assert grad_matrix(d_in=0) == bad
+    assert grad_matrix(direction=2) == bad
+    assert grad_matrix(mat=vps([0])) == bad
+    assert grad_matrix(mat=vps([FAKE + 1])) == bad
+    assert grad_matrix(wsb=0) == la.KFAC_ERR_WORKSPACE
+    assert lib.kfac_im2col_workspace_size(0) == 0
+    assert lib.kfac_grad_rows_workspace_size(1) > 0

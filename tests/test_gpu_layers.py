@@ -27,6 +27,10 @@ CASES = [  # (n, c, h, w), kernel, stride, padding, dilation, ones
     ((2, 68, 5, 5), (3, 3), (1, 1), (1, 1), (1, 1), False),     # write only: 612 columns
     ((3, 72, 7, 7), (1, 1), (1, 1), (0, 0), (1, 1), False),     # write only: h w = 49
     ((32, 1024, 1, 1), (1, 1), (1, 1), (0, 0), (1, 1), False),  # fully connected, no bias: both
+    # degenerate shapes: a 1 x 1 output, a stride wider than the kernel, one channel with dilation 2
+    ((2, 3, 5, 5), (7, 7), (1, 1), (1, 1), (1, 1), True),
+    ((1, 2, 9, 9), (2, 2), (3, 3), (0, 0), (1, 1), False),
+    ((3, 1, 6, 6), (3, 3), (1, 1), (0, 0), (2, 2), False),
 ]
 
 
