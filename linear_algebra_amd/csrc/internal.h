@@ -142,6 +142,7 @@ struct InvMat {
     double* w;            // workspace [D][D] float64: U, then V = U^-1 above the diagonal
     double* dinv;         // workspace [NB][64][64]: inverses of the diagonal blocks of U
     int32_t* info;        // &info[original index]
+    double* part;         // workspace: partial blocks of V, 2 x vpart_slots(nb - 1) blocks (by column parity)
     int32_t d;
     int32_t nb;           // blocks per edge
 };
@@ -161,14 +162,36 @@ struct InvLaunch {
     double gamma;
     int64_t split;        // potrf step launch: blocks [0, split) are row-k blocks
     int64_t tail_first;   // potrf step launch: first block of the trailing update
+    int64_t fin_end;      // potrf step launch: [split, fin_end) finish a column of V
+    int64_t part_end;     // potrf step launch: [fin_end, part_end) partial sums of the next column
+    int32_t vlow;         // V is kept transposed below the diagonal (formed beside potrf), not above it
+    int32_t pad_;
 };
 
 // Tiles each inverse kernel needs per matrix with nb blocks per edge at a
 // given potrf step (trsm, syrk) or trtri level.  Shared by the host, which
 // sizes the grids, and the kernels, which decode their tile index.
 enum InvKind : int32_t {
-    kInvPrepare = 0, kInvPanel = 1, kInvSyrk = 2, kInvTrtri = 3, kInvLauum = 4, kInvLauum2 = 5
+    kInvPrepare = 0, kInvPanel = 1, kInvSyrk = 2, kInvTrtri = 3, kInvLauum = 4, kInvLauum2 = 5,
+    kInvVPart = 6, kInvVFin = 7
 };
+
+// V = U^-1 formed column by column beside the potrf steps (V U = I):
+//   V_ic = -(sum_{i <= m < c} V_im U_mc) V_cc,  i < c.
+// Step launch k sums, for column c = k - 1, the terms m <= c - 2 in chunks of
+// kVChunk blocks (one partial block per chunk and row i), and finishes column
+// c = k - 2: its partial blocks, the term m = c - 1, and the product with V_cc.
+// Partial slots of a column: chunk q covers rows i <= c - 2 - q kVChunk, so
+// chunk q holds c - 1 - q kVChunk slots, chunk by chunk.
+constexpr int kVChunk = 4;
+__host__ __device__ inline int64_t vpart_slot0(int64_t c, int64_t q) {   // first slot of chunk q
+    return q * (c - 1) - (int64_t)kVChunk * q * (q - 1) / 2;
+}
+__host__ __device__ inline int64_t vpart_slots(int64_t c) {
+    if (c < 2) return 0;
+    const int64_t nq = (c - 1 + kVChunk - 1) / kVChunk;
+    return vpart_slot0(c, nq);
+}
 
 // Groups of 2^l blocks leave a last level that joins almost all blocks with
 // a handful when nb is just above a power of two (33 = 32 + 1): a few long
@@ -187,6 +210,14 @@ __host__ __device__ inline int64_t inv_tiles(int kind, int64_t nb, int64_t step)
         case kInvLauum2: {  // 2 x 2 groups of blocks, upper triangle
             const int64_t n2 = (nb + 1) / 2;
             return n2 * (n2 + 1) / 2;
+        }
+        case kInvVPart: {  // partial sums of column step - 1
+            const int64_t c = step - 1;
+            return c >= 2 && c < nb ? vpart_slots(c) : 0;
+        }
+        case kInvVFin: {   // rows 0 .. c - 1 of column c = step - 2
+            const int64_t c = step - 2;
+            return c >= 1 && c < nb ? c : 0;
         }
         case kInvPanel:  // one workgroup per block right of the diagonal, at least one
             return nb > step ? (nb - step - 1 > 1 ? nb - step - 1 : 1) : 0;

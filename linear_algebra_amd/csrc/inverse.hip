@@ -707,6 +707,73 @@ __device__ __forceinline__ void potrf_row_block(const InvLaunch& L, const InvMat
     acc_store(acc, Wkj, D);
 }
 
+// Block V_im of V = U^-1 (m >= i) staged as [row][k]: the inverted diagonal
+// block, or block (m, i) below the diagonal of W, which holds V_im^T.
+__device__ __forceinline__ Blk v_low(const InvMat& M, int64_t D, int i, int m) {
+    return m == i ? Blk{M.dinv + (int64_t)i * BB, B, false} : Blk{M.w + (int64_t)m * B * D + (int64_t)i * B, D, true};
+}
+
+// Partial sum of column c = step - 1 of V, slot `local`: chunk q of row i,
+// sum_{m in chunk} V_im U_mc over m in [i + q kVChunk, min(i + (q + 1) kVChunk, c - 1)).
+__device__ __forceinline__ void v_partial(const InvLaunch& L, const InvMat& M, int64_t local, double* S) {
+    const int c = L.step - 1;
+    const int64_t D = (int64_t)M.nb * B;
+    int q = 0;
+    int64_t r = local;
+    while (r >= c - 1 - (int64_t)q * kVChunk) {
+        r -= c - 1 - (int64_t)q * kVChunk;
+        ++q;
+    }
+    const int i = (int)r;
+    const int m0 = i + q * kVChunk, m1 = min(m0 + kVChunk, c - 1);
+    doublex4 acc[2][2];
+    acc_zero(acc);
+    block_gemm(acc, S, m0, m1, [&](int m) { return v_low(M, D, i, m); },
+               [&](int m) { return Blk{M.w + (int64_t)m * B * D + (int64_t)c * B, D, true}; }, false, false);
+    double* dst = M.part + ((int64_t)(c & 1) * vpart_slots(M.nb - 1) + local) * BB;
+    acc_store(acc, dst, B);
+}
+
+// Block (i, c) of V, c = step - 2: T = (its partial blocks) + V_i,c-1 U_c-1,c,
+// then V_ic = -T V_cc, stored transposed into block (c, i) of W.
+__device__ __forceinline__ void v_finalize(const InvLaunch& L, const InvMat& M, int64_t local, double* S) {
+    const int c = L.step - 2, i = (int)local;
+    const int64_t D = (int64_t)M.nb * B;
+    double* As = S;
+    double* Bs = S + B * LD;
+    doublex4 acc[2][2];
+    acc_zero(acc);
+    const int nq = i <= c - 2 ? (c - 1 - i + kVChunk - 1) / kVChunk : 0;
+    const double* part = M.part + (int64_t)(c & 1) * vpart_slots(M.nb - 1) * BB;
+    for (int q = 0; q < nq; ++q) {
+        doublex4 t[2][2];
+        acc_load(t, part + (vpart_slot0(c, q) + i) * BB, B);
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int b = 0; b < 2; ++b) acc[a][b] += t[a][b];
+    }
+    block_gemm(acc, S, c - 1, c, [&](int m) { return v_low(M, D, i, m); },
+               [&](int m) { return Blk{M.w + (int64_t)m * B * D + (int64_t)c * B, D, true}; }, false, false);
+    // -T V_cc: T staged as [m][k], V_cc as [n][k] = V_cc[k][n]
+    double vc[PER];
+    fetch(vc, Blk{M.dinv + (int64_t)c * BB, B, false});
+    acc_to_lds(acc, As);
+    put(Bs, vc, true);
+    __syncthreads();
+    doublex4 out[2][2];
+    acc_zero(out);
+    mma_block(out, As, Bs, true);
+    __syncthreads();
+    // V_ic^T through LDS, so that block (c, i) is written in whole rows
+    for_acc([&](int a, int b, int r, int row, int col) { As[col * LD + row] = out[a][b][r]; });
+    __syncthreads();
+    double* dst = M.w + (int64_t)c * B * D + (int64_t)i * B;
+    const int r0 = threadIdx.x >> 6, cl = threadIdx.x & 63;
+#pragma unroll
+    for (int s = 0; s < PER; ++s) as_global(dst)[(int64_t)(r0 + 4 * s) * D + cl] = As[(r0 + 4 * s) * LD + cl];
+}
+
 // Step k of potrf with a look-ahead of one step.  Workgroups [0, split) are
 // the row-k blocks of every matrix, the critical path: they come first in
 // the dispatch and keep its order, so the hardware spreads them over the
@@ -725,6 +792,16 @@ __global__ __launch_bounds__(NT, 2) void inv_step_kernel(InvLaunch L, int64_t ti
     if (b < L.split) {
         if (!locate(L, kInvPanel, b, mi, local)) return;
         potrf_row_block(L, L.mats[mi], local, As, Bs, R);
+        return;
+    }
+    if (b < L.fin_end) {
+        if (!locate(L, kInvVFin, b - L.split, mi, local)) return;
+        v_finalize(L, L.mats[mi], local, S);
+        return;
+    }
+    if (b < L.part_end) {
+        if (!locate(L, kInvVPart, b - L.fin_end, mi, local)) return;
+        v_partial(L, L.mats[mi], local, S);
         return;
     }
     if (b < L.tail_first) return;
@@ -870,6 +947,7 @@ __global__ __launch_bounds__(NT) void inv_lauum_kernel(InvLaunch L, int64_t tile
     doublex4 acc[2][2];
     acc_zero(acc);
     auto V = [&](int row, int t) {
+        if (L.vlow) return v_low(M, D, row, t);
         return t == row ? Blk{M.dinv + (int64_t)row * BB, B, false}
                         : Blk{M.w + (int64_t)row * B * D + (int64_t)t * B, D, false};
     };
@@ -922,6 +1000,7 @@ __global__ __launch_bounds__(NT, 2) void inv_lauum2_kernel(InvLaunch L, int64_t 
     const bool active = I < nb && J < nb && !(I2 == J2 && a > b);
     auto V = [&](int row, int t) {
         if (row >= nb || t < row) return Blk{M.w, D, false};
+        if (L.vlow) return v_low(M, D, row, t);
         return t == row ? Blk{M.dinv + (int64_t)row * BB, B, false}
                         : Blk{M.w + (int64_t)row * B * D + (int64_t)t * B, D, false};
     };

@@ -206,14 +206,32 @@ InvPlan plan_inverse(int n, const int64_t* d) {
     return p;
 }
 
+// V = U^-1 is formed beside the potrf steps (two extra step launches at the
+// end, no triangular-inverse launches) when those steps leave most of the
+// chip idle: on average fewer than kFuseTilesPerStep trailing-update tiles
+// per step (four per resident workgroup slot).  Otherwise the potrf steps
+// are busy with the trailing update and V is formed afterwards by recursive
+// doubling, in launches of its own.
+constexpr int64_t kFuseTilesPerStep = 2048;
+
+int64_t bucket_tiles(const InvPlan& p, int kind, int step);
+
+bool fuse_v(const InvPlan& p) {
+    int64_t tiles = 0;
+    for (int k = 0; k < p.nbmax; ++k) tiles += bucket_tiles(p, kInvSyrk, k);
+    return tiles < kFuseTilesPerStep * (int64_t)p.nbmax;
+}
+
 size_t inverse_ws(int n, const int64_t* d) {
+    const bool fused = fuse_v(plan_inverse(n, d));
     Carver c(nullptr);
     c.take(sizeof(InvMat) * n);
     c.take(sizeof(InvBucket) * n);
     for (int i = 0; i < n; ++i) {
-        const int64_t D = ceil_div(d[i], kInvNB) * kInvNB;
+        const int64_t nb = ceil_div(d[i], kInvNB), D = nb * kInvNB;
         c.take(sizeof(double) * (size_t)(D * D));
         c.take(sizeof(double) * (size_t)(D * kInvNB));
+        if (fused) c.take(sizeof(double) * (size_t)(2 * vpart_slots(nb - 1) * kInvNB * kInvNB));
     }
     return c.used;
 }
@@ -377,37 +395,46 @@ kfac_status_t kfac_damped_inverse(int n, const float* const* x, const int64_t* d
     if (workspace == nullptr || !aligned(workspace, kAlign) || workspace_bytes < need) return KFAC_ERR_WORKSPACE;
 
     InvPlan p = plan_inverse(n, d);
+    const bool fused = fuse_v(p);
     Carver c(workspace);
     InvMat* mats_dev = static_cast<InvMat*>(c.take(sizeof(InvMat) * n));
     InvBucket* buckets_dev = static_cast<InvBucket*>(c.take(sizeof(InvBucket) * n));
     // per-matrix scratch in original order
-    std::vector<double*> w(n), dinv(n);
+    std::vector<double*> w(n), dinv(n), part(n);
     for (int i = 0; i < n; ++i) {
-        const int64_t D = ceil_div(d[i], kInvNB) * kInvNB;
+        const int64_t nb = ceil_div(d[i], kInvNB), D = nb * kInvNB;
         w[i] = static_cast<double*>(c.take(sizeof(double) * (size_t)(D * D)));
         dinv[i] = static_cast<double*>(c.take(sizeof(double) * (size_t)(D * kInvNB)));
+        part[i] = fused ? static_cast<double*>(c.take(sizeof(double) * (size_t)(2 * vpart_slots(nb - 1) * kInvNB * kInvNB)))
+                          : nullptr;
     }
     std::vector<InvMat> mats(n);
     for (int s = 0; s < n; ++s) {
         const int i = p.order[s];
-        mats[s] = InvMat{x[i], xinv[i], w[i], dinv[i], info + i, (int32_t)d[i], (int32_t)ceil_div(d[i], kInvNB)};
+        mats[s] = InvMat{x[i], xinv[i], w[i], dinv[i], info + i, part[i], (int32_t)d[i],
+                         (int32_t)ceil_div(d[i], kInvNB)};
     }
     hipError_t e = upload_table(mats_dev, mats.data(), sizeof(InvMat) * n, stream);
     if (e == hipSuccess) e = upload_table(buckets_dev, p.buckets.data(), sizeof(InvBucket) * p.buckets.size(), stream);
     if (e != hipSuccess) return KFAC_ERR_HIP;
 
-    InvLaunch L{mats_dev, buckets_dev, (int32_t)p.buckets.size(), 0, (double)gamma, 0, 0};
+    InvLaunch L{mats_dev, buckets_dev, (int32_t)p.buckets.size(), 0, (double)gamma, 0, 0, 0, 0, fused ? 1 : 0, 0};
     e = launch_inv_prepare(L, bucket_tiles(p, kInvPrepare, 0), stream);
-    for (int k = 0; e == hipSuccess && k < p.nbmax; ++k) {
+    // with V formed beside potrf, two more launches finish its last columns
+    const int nsteps = fused ? p.nbmax + 2 : p.nbmax;
+    for (int k = 0; e == hipSuccess && k < nsteps; ++k) {
         // row-k blocks of every matrix in the first workgroups (spread over the
-        // XCDs as dispatched), then the trailing update from a multiple of 8
+        // XCDs as dispatched), then the columns of V, then the trailing update
+        // from a multiple of 8
         L.step = k;
         L.split = bucket_tiles(p, kInvPanel, k);
+        L.fin_end = L.split + (fused ? bucket_tiles(p, kInvVFin, k) : 0);
+        L.part_end = L.fin_end + (fused ? bucket_tiles(p, kInvVPart, k) : 0);
         const int64_t trail = bucket_tiles(p, kInvSyrk, k);
-        L.tail_first = trail > 0 ? (L.split + 7) / 8 * 8 : L.split;
-        e = launch_inv_step(L, L.tail_first + trail, stream);
+        L.tail_first = trail > 0 ? (L.part_end + 7) / 8 * 8 : L.part_end;
+        if (L.tail_first + trail > 0) e = launch_inv_step(L, L.tail_first + trail, stream);
     }
-    for (int lvl = 0; e == hipSuccess && (1 << lvl) < p.nbmax; ++lvl) {   // bottom level first
+    for (int lvl = 0; !fused && e == hipSuccess && (1 << lvl) < p.nbmax; ++lvl) {   // bottom level first
         L.step = lvl;
         const int64_t t = bucket_tiles(p, kInvTrtri, lvl);
         e = launch_inv_trtri_a(L, t, stream);
