@@ -183,7 +183,7 @@ enum InvKind : int32_t {
 // c = k - 2: its partial blocks, the term m = c - 1, and the product with V_cc.
 // Partial slots of a column: chunk q covers rows i <= c - 2 - q kVChunk, so
 // chunk q holds c - 1 - q kVChunk slots, chunk by chunk.
-constexpr int kVChunk = 4;
+constexpr int kVChunk = 2;
 __host__ __device__ inline int64_t vpart_slot0(int64_t c, int64_t q) {   // first slot of chunk q
     return q * (c - 1) - (int64_t)kVChunk * q * (q - 1) / 2;
 }
