@@ -745,13 +745,19 @@ __device__ __forceinline__ void v_finalize(const InvLaunch& L, const InvMat& M, 
     acc_zero(acc);
     const int nq = i <= c - 2 ? (c - 1 - i + kVChunk - 1) / kVChunk : 0;
     const double* part = M.part + (int64_t)(c & 1) * vpart_slots(M.nb - 1) * BB;
-    for (int q = 0; q < nq; ++q) {
-        doublex4 t[2][2];
-        acc_load(t, part + (vpart_slot0(c, q) + i) * BB, B);
+    // four partial blocks in flight per round trip (in chunk order, so the
+    // sum is the same on every run); past nq, block 0 is read and not used
+    for (int q = 0; q < nq; q += 4) {
+        doublex4 t[4][2][2];
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
+        for (int u = 0; u < 4; ++u) acc_load(t[u], part + (vpart_slot0(c, q + u < nq ? q + u : 0) + i) * BB, B);
 #pragma unroll
-            for (int b = 0; b < 2; ++b) acc[a][b] += t[a][b];
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+                    if (q + u < nq) acc[a][b] += t[u][a][b];
     }
     block_gemm(acc, S, c - 1, c, [&](int m) { return v_low(M, D, i, m); },
                [&](int m) { return Blk{M.w + (int64_t)m * B * D + (int64_t)c * B, D, true}; }, false, false);
