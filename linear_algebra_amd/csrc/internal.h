@@ -164,7 +164,7 @@ struct InvLaunch {
     int64_t tail_first;   // potrf step launch: first block of the trailing update
     int64_t fin_end;      // potrf step launch: [split, fin_end) finish a column of V
     int64_t part_end;     // potrf step launch: [fin_end, part_end) partial sums of the next column
-    int32_t vlow;         // V is kept transposed below the diagonal (formed beside potrf), not above it
+    int32_t vlow;         // V_ic is kept in block (c, i) below the diagonal (formed beside potrf), not in (i, c)
     int32_t pad_;
 };
 

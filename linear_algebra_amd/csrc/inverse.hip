@@ -708,9 +708,9 @@ __device__ __forceinline__ void potrf_row_block(const InvLaunch& L, const InvMat
 }
 
 // Block V_im of V = U^-1 (m >= i) staged as [row][k]: the inverted diagonal
-// block, or block (m, i) below the diagonal of W, which holds V_im^T.
+// block, or block (m, i) below the diagonal of W, which holds V_im.
 __device__ __forceinline__ Blk v_low(const InvMat& M, int64_t D, int i, int m) {
-    return m == i ? Blk{M.dinv + (int64_t)i * BB, B, false} : Blk{M.w + (int64_t)m * B * D + (int64_t)i * B, D, true};
+    return m == i ? Blk{M.dinv + (int64_t)i * BB, B, false} : Blk{M.w + (int64_t)m * B * D + (int64_t)i * B, D, false};
 }
 
 // Partial sum of column c = step - 1 of V, slot `local`: chunk q of row i,
@@ -735,7 +735,7 @@ __device__ __forceinline__ void v_partial(const InvLaunch& L, const InvMat& M, i
 }
 
 // Block (i, c) of V, c = step - 2: T = (its partial blocks) + V_i,c-1 U_c-1,c,
-// then V_ic = -T V_cc, stored transposed into block (c, i) of W.
+// then V_ic = -T V_cc, stored into block (c, i) of W (below the diagonal).
 __device__ __forceinline__ void v_finalize(const InvLaunch& L, const InvMat& M, int64_t local, double* S) {
     const int c = L.step - 2, i = (int)local;
     const int64_t D = (int64_t)M.nb * B;
@@ -770,14 +770,7 @@ __device__ __forceinline__ void v_finalize(const InvLaunch& L, const InvMat& M, 
     doublex4 out[2][2];
     acc_zero(out);
     mma_block(out, As, Bs, true);
-    __syncthreads();
-    // V_ic^T through LDS, so that block (c, i) is written in whole rows
-    for_acc([&](int a, int b, int r, int row, int col) { As[col * LD + row] = out[a][b][r]; });
-    __syncthreads();
-    double* dst = M.w + (int64_t)c * B * D + (int64_t)i * B;
-    const int r0 = threadIdx.x >> 6, cl = threadIdx.x & 63;
-#pragma unroll
-    for (int s = 0; s < PER; ++s) as_global(dst)[(int64_t)(r0 + 4 * s) * D + cl] = As[(r0 + 4 * s) * LD + cl];
+    acc_store(out, M.w + (int64_t)c * B * D + (int64_t)i * B, D);
 }
 
 // Step k of potrf with a look-ahead of one step.  Workgroups [0, split) are
