@@ -165,7 +165,7 @@ struct InvLaunch {
     int64_t fin_end;      // potrf step launch: [split, fin_end) finish a column of V
     int64_t part_end;     // potrf step launch: [fin_end, part_end) partial sums of the next column
     int32_t vlow;         // V_ic is kept in block (c, i) below the diagonal (formed beside potrf), not in (i, c)
-    int32_t pad_;
+    int32_t plo;          // potrf step launch: row k and the trailing update apply panels [plo, k)
 };
 
 // Tiles each inverse kernel needs per matrix with nb blocks per edge at a

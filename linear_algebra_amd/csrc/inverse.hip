@@ -658,26 +658,34 @@ __device__ __forceinline__ void potrf_row_block(const InvLaunch& L, const InvMat
     const int J = k + 1 + (int)local;
     double* Wkk = M.w + (int64_t)k * B * D + (int64_t)k * B;
     double* Wkj = M.w + (int64_t)k * B * D + (int64_t)J * B;
-    // Every block this workgroup reads is requested before the first wait,
-    // the panel blocks of step k - 1 first.  The requests are unconditional
-    // (a branch around them would end in a wait for all of them): without
-    // a block right of the diagonal, or at step 0, they read blocks of the
-    // matrix that are then not used.
+    // Row k still lacks the updates of panels [plo, k) (one, or two where
+    // the trailing update runs every other step).  Every block this
+    // workgroup reads first is requested before the first wait, the first
+    // panel's blocks first.  The requests are unconditional (a branch around
+    // them would end in a wait for all of them): without a block right of
+    // the diagonal, or at step 0, they read blocks of the matrix that are
+    // then not used.
     const int Jr = has_right ? J : k;
-    const double* prev = M.w + (int64_t)(k > 0 ? k - 1 : 0) * B * D;
+    const int p0 = L.plo < k ? L.plo : 0;
     double ra[PER], rb[PER];
-    fetch(ra, Blk{prev + (int64_t)k * B, D, true});
-    fetch(rb, Blk{prev + (int64_t)Jr * B, D, true});
+    fetch(ra, Blk{M.w + (int64_t)p0 * B * D + (int64_t)k * B, D, true});
+    fetch(rb, Blk{M.w + (int64_t)p0 * B * D + (int64_t)Jr * B, D, true});
     doublex4 dk[2][2], wj[2][2];
     acc_load(dk, Wkk, D);
     acc_load(wj, M.w + (int64_t)k * B * D + (int64_t)Jr * B, D);
-    if (k > 0) {
+    auto update = [&]() {
         put(As, ra, true);
         if (has_right) put(Bs, rb, true);
         __syncthreads();
         mma_block(dk, As, As, true);
         if (has_right) mma_block(wj, As, Bs, true);
         __syncthreads();
+    };
+    if (p0 < k) update();
+    if (p0 + 1 < k) {   // at most two panels: the host keeps k - plo <= 2
+        fetch(ra, Blk{M.w + (int64_t)(p0 + 1) * B * D + (int64_t)k * B, D, true});
+        fetch(rb, Blk{M.w + (int64_t)(p0 + 1) * B * D + (int64_t)Jr * B, D, true});
+        update();
     }
     acc_to_lds(dk, Bs);
     const int f = factor_diagonal(Bs, As, R);   // As: U_kk^-1
@@ -814,19 +822,26 @@ __global__ __launch_bounds__(NT, 2) void inv_step_kernel(InvLaunch L, int64_t ti
     const int I = k + 1 + a, J = k + 1 + c;
     const int64_t D = (int64_t)M.nb * B;
     double* Wij = M.w + (int64_t)I * B * D + (int64_t)J * B;
-    const double* prev = M.w + (int64_t)(k - 1) * B * D;
-    // one 64-deep product: both panel blocks and the block being updated
-    // are requested at once (a single memory round trip), then multiplied
-    // from LDS
-    double ra[PER], rb[PER];
-    fetch(ra, Blk{prev + (int64_t)I * B, D, true});
-    if (I != J) fetch(rb, Blk{prev + (int64_t)J * B, D, true});
     doublex4 acc[2][2];
-    acc_load(acc, Wij, D);
-    put(As, ra, true);
-    if (I != J) put(Bs, rb, true);
-    __syncthreads();
-    mma_block(acc, As, I == J ? As : Bs, true);
+    if (L.plo == k - 1) {
+        // one 64-deep product: both panel blocks and the block being updated
+        // are requested at once (a single memory round trip), then
+        // multiplied from LDS
+        const double* prev = M.w + (int64_t)(k - 1) * B * D;
+        double ra[PER], rb[PER];
+        fetch(ra, Blk{prev + (int64_t)I * B, D, true});
+        if (I != J) fetch(rb, Blk{prev + (int64_t)J * B, D, true});
+        acc_load(acc, Wij, D);
+        put(As, ra, true);
+        if (I != J) put(Bs, rb, true);
+        __syncthreads();
+        mma_block(acc, As, I == J ? As : Bs, true);
+    } else {
+        // panels [plo, k) at once: the block is read and written once for all
+        acc_load(acc, Wij, D);
+        block_gemm(acc, S, L.plo, k, [&](int t) { return Blk{M.w + (int64_t)t * B * D + (int64_t)I * B, D, true}; },
+                   [&](int t) { return Blk{M.w + (int64_t)t * B * D + (int64_t)J * B, D, true}; }, true, I == J);
+    }
     acc_store(acc, Wij, D);
 }
 

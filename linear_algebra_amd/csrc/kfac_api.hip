@@ -213,6 +213,8 @@ InvPlan plan_inverse(int n, const int64_t* d) {
 // are busy with the trailing update and V is formed afterwards by recursive
 // doubling, in launches of its own.
 constexpr int64_t kFuseTilesPerStep = 2048;
+// Trailing updates of at least this many blocks run every other step.
+constexpr int64_t kPass2Tiles = 1024;
 
 int64_t bucket_tiles(const InvPlan& p, int kind, int step);
 
@@ -419,6 +421,7 @@ kfac_status_t kfac_damped_inverse(int n, const float* const* x, const int64_t* d
     if (e != hipSuccess) return KFAC_ERR_HIP;
 
     InvLaunch L{mats_dev, buckets_dev, (int32_t)p.buckets.size(), 0, (double)gamma, 0, 0, 0, 0, fused ? 1 : 0, 0};
+    int last_pass = 0;   // rows below the last trailing update hold the updates of panels [0, last_pass)
     e = launch_inv_prepare(L, bucket_tiles(p, kInvPrepare, 0), stream);
     // with V formed beside potrf, two more launches finish its last columns
     const int nsteps = fused ? p.nbmax + 2 : p.nbmax;
@@ -427,10 +430,16 @@ kfac_status_t kfac_damped_inverse(int n, const float* const* x, const int64_t* d
         // XCDs as dispatched), then the columns of V, then the trailing update
         // from a multiple of 8
         L.step = k;
+        L.plo = last_pass;
         L.split = bucket_tiles(p, kInvPanel, k);
         L.fin_end = L.split + (fused ? bucket_tiles(p, kInvVFin, k) : 0);
         L.part_end = L.fin_end + (fused ? bucket_tiles(p, kInvVPart, k) : 0);
-        const int64_t trail = bucket_tiles(p, kInvSyrk, k);
+        // a heavy trailing update (it rewrites its blocks in full) runs every
+        // other step, two panels deep; the rows in between take the skipped
+        // panel themselves
+        int64_t trail = bucket_tiles(p, kInvSyrk, k);
+        if (trail >= kPass2Tiles && k - last_pass < 2) trail = 0;
+        if (trail > 0) last_pass = k;
         L.tail_first = trail > 0 ? (L.part_end + 7) / 8 * 8 : L.part_end;
         if (L.tail_first + trail > 0) e = launch_inv_step(L, L.tail_first + trail, stream);
     }
