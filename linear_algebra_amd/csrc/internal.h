@@ -167,6 +167,8 @@ struct InvLaunch {
     int32_t vlow;         // V_ic is kept in block (c, i) below the diagonal (formed beside potrf), not in (i, c)
     int32_t plo;          // potrf step launch: row k and the trailing update apply panels [plo, k)
 };
+// At most this many panels per trailing update (k - plo).
+constexpr int kMaxPassDepth = 3;
 
 // Tiles each inverse kernel needs per matrix with nb blocks per edge at a
 // given potrf step (trsm, syrk) or trtri level.  Shared by the host, which

@@ -682,10 +682,13 @@ __device__ __forceinline__ void potrf_row_block(const InvLaunch& L, const InvMat
         __syncthreads();
     };
     if (p0 < k) update();
-    if (p0 + 1 < k) {   // at most two panels: the host keeps k - plo <= 2
-        fetch(ra, Blk{M.w + (int64_t)(p0 + 1) * B * D + (int64_t)k * B, D, true});
-        fetch(rb, Blk{M.w + (int64_t)(p0 + 1) * B * D + (int64_t)Jr * B, D, true});
-        update();
+#pragma unroll
+    for (int u = 1; u < kMaxPassDepth; ++u) {   // the host keeps k - plo <= kMaxPassDepth
+        if (p0 + u < k) {
+            fetch(ra, Blk{M.w + (int64_t)(p0 + u) * B * D + (int64_t)k * B, D, true});
+            fetch(rb, Blk{M.w + (int64_t)(p0 + u) * B * D + (int64_t)Jr * B, D, true});
+            update();
+        }
     }
     acc_to_lds(dk, Bs);
     const int f = factor_diagonal(Bs, As, R);   // As: U_kk^-1

@@ -213,8 +213,10 @@ InvPlan plan_inverse(int n, const int64_t* d) {
 // are busy with the trailing update and V is formed afterwards by recursive
 // doubling, in launches of its own.
 constexpr int64_t kFuseTilesPerStep = 2048;
-// Trailing updates of at least this many blocks run every other step.
+// Trailing updates of at least this many blocks run every other step, two
+// panels deep, and of at least kPass3Tiles every third step.
 constexpr int64_t kPass2Tiles = 1024;
+constexpr int64_t kPass3Tiles = 8192;
 
 int64_t bucket_tiles(const InvPlan& p, int kind, int step);
 
@@ -434,12 +436,15 @@ kfac_status_t kfac_damped_inverse(int n, const float* const* x, const int64_t* d
         L.split = bucket_tiles(p, kInvPanel, k);
         L.fin_end = L.split + (fused ? bucket_tiles(p, kInvVFin, k) : 0);
         L.part_end = L.fin_end + (fused ? bucket_tiles(p, kInvVPart, k) : 0);
-        // a heavy trailing update (it rewrites its blocks in full) runs every
-        // other step, two panels deep; the rows in between take the skipped
-        // panel themselves
+        // A heavy trailing update (it rewrites its blocks in full) runs only
+        // every second or third step, two or three panels deep; the rows in
+        // between take the skipped panels themselves.  A step with no
+        // trailing blocks at all (no rows below it) counts as an update.
         int64_t trail = bucket_tiles(p, kInvSyrk, k);
-        if (trail >= kPass2Tiles && k - last_pass < 2) trail = 0;
-        if (trail > 0) last_pass = k;
+        const int depth = trail >= kPass3Tiles ? 3 : trail >= kPass2Tiles ? 2 : 1;
+        static_assert(kMaxPassDepth >= 3, "three-panel updates");
+        if (k - last_pass >= depth || trail == 0) last_pass = k;
+        else trail = 0;
         L.tail_first = trail > 0 ? (L.part_end + 7) / 8 * 8 : L.part_end;
         if (L.tail_first + trail > 0) e = launch_inv_step(L, L.tail_first + trail, stream);
     }
