@@ -48,15 +48,22 @@ def algorithmic_work(cfg):
 
 
 def kernel_source_sha256():
-    """Hash of the library's kernel sources, the key of stored counter data."""
+    """Hash of the library's kernel sources, the key of stored counter data.
+    Comments and blank lines are left out, so that the key changes only
+    with the code."""
     import glob
     import hashlib
+    import re
     h = hashlib.sha256()
     for p in sorted(glob.glob(os.path.join(ROOT, "linear_algebra_amd", "csrc", "*"))):
         if p.endswith((".hip", ".h", ".cpp")):
             h.update(os.path.basename(p).encode())
-            with open(p, "rb") as f:
-                h.update(f.read())
+            with open(p, encoding="utf-8") as f:
+                text = f.read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            text = re.sub(r"//[^\n]*", "", text)
+            lines = [ln.rstrip() for ln in text.splitlines()]
+            h.update("\n".join(ln for ln in lines if ln).encode())
     return h.hexdigest()
 
 

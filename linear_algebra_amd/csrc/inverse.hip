@@ -7,20 +7,33 @@
 //   prepare   W = sym(X) + gamma I (upper blocks), identity in the padding;
 //   potrf     right-looking, upper (Y = U^T U), one launch per step k with
 //             a look-ahead of one step:
-//               row k     W_kj -= U_{k-1,k}^T U_{k-1,j}   (j >= k); then
-//                         every row-k workgroup factors the diagonal block
-//                         and inverts its triangle (16-row strips, see
+//               row k     W_kj -= sum_p U_pk^T U_pj  (j >= k, p in [plo, k));
+//                         then every row-k workgroup factors the diagonal
+//                         block and inverts its triangle (16-row strips, see
 //                         factor_diagonal) and solves one block of the row:
 //                         U_kj = U_kk^-T W_kj           (j > k)
-//               trailing  W_ij -= U_{k-1,i}^T U_{k-1,j} (k < i <= j), in
-//                         the same launch, beside the row-k workgroups;
-//   trtri     V = U^-1 by recursive doubling over groups of blocks, from the
-//             leaves up: for sibling groups G1, G2 (G1 before G2)
-//               V_12 = -V_11 . (U_12 . V_22)
-//             two launches per level, ceil(log2(nb)) levels; the groups are
-//             runs of 2^l blocks, or a balanced binary tree when nb is just
-//             above a power of two; the inner product is parked in the
-//             unused lower triangle of W;
+//               trailing  W_ij -= sum_p U_pi^T U_pj  (k < i <= j, p in
+//                         [plo, k)), in the same launch, beside the row-k
+//                         workgroups; where the trailing matrix is large the
+//                         host runs it only every second or third step, so
+//                         that one read and write of a block takes two or
+//                         three panels (plo is the first panel not applied);
+//   V = U^-1  formed one of two ways, chosen by the host from the trailing
+//             work per step:
+//             fused     beside potrf: at step k the blocks of column k-1
+//                         above the diagonal get partial sums
+//                         sum_m V_im U_m,k-1 over chunks of two panels, and
+//                         column k-2 is finished as
+//                         V_ic = -(sum of its partials) V_cc; V_ic is kept
+//                         in the lower block (c, i), two extra launches
+//                         finish the last columns;
+//             trtri     after potrf, by recursive doubling over groups of
+//                         blocks, from the leaves up: for sibling groups G1,
+//                         G2 (G1 before G2)  V_12 = -V_11 . (U_12 . V_22),
+//                         two launches per level, ceil(log2(nb)) levels; the
+//                         groups are runs of 2^l blocks, or a balanced binary
+//                         tree when nb is just above a power of two; the
+//                         inner product is parked in the lower triangle of W;
 //   lauum     Z = V V^T (upper blocks), written as float32 to both triangles.
 //
 // Diagonal blocks of V are the inverses of the diagonal blocks of U, kept in
