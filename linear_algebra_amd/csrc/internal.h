@@ -143,9 +143,34 @@ struct InvMat {
     double* dinv;         // workspace [NB][64][64]: inverses of the diagonal blocks of U
     int32_t* info;        // &info[original index]
     double* part;         // workspace: partial blocks of V, 2 x vpart_slots(nb - 1) blocks (by column parity)
-    int32_t d;
-    int32_t nb;           // blocks per edge
+    double* bvec;         // bordered matrices (n < d): border_doubles(nb), see there
+    int32_t d;            // order of the matrix and row stride of x and z
+    int32_t n;            // order of the part factored in blocks: d, or d - 1 when the last row and
+                          // column are attached afterwards as a border
+    int32_t nb;           // blocks per edge, ceil(n / 64)
+    int32_t pad_;
 };
+
+// Order of the part of a d x d matrix that is factored in 64 x 64 blocks.
+// A matrix one larger than a multiple of 64 (the factor A of a layer with a
+// bias) would waste a whole block row and column on its last index, so that
+// index is attached after the inverse of the leading part, through its Schur
+// complement (a bordered Cholesky step).
+__host__ __device__ inline int64_t inv_extent(int64_t d) { return (d > kInvNB && d % kInvNB == 1) ? d - 1 : d; }
+
+// Workspace of a bordered matrix, in doubles: the border column v of V
+// (n = 64 nb), the partial sums of w^T w (one per run of columns, padded to
+// 64), then the partial sums of w (per column block and run of row blocks)
+// and of u = V w (per row block and run of column blocks), 64 each.  A run
+// is kBorderRun blocks, the share of one workgroup.
+constexpr int kBorderRun = 4;
+__host__ __device__ inline int64_t border_runs(int64_t nb) { return (nb + kBorderRun - 1) / kBorderRun; }
+__host__ __device__ inline int64_t border_ss_off(int64_t nb) { return nb * kInvNB; }
+__host__ __device__ inline int64_t border_w_off(int64_t nb) {
+    return border_ss_off(nb) + (border_runs(nb) + kInvNB - 1) / kInvNB * kInvNB;
+}
+__host__ __device__ inline int64_t border_u_off(int64_t nb) { return border_w_off(nb) + nb * border_runs(nb) * kInvNB; }
+__host__ __device__ inline int64_t border_doubles(int64_t nb) { return border_u_off(nb) + nb * border_runs(nb) * kInvNB; }
 
 struct InvBucket {
     int32_t nb;           // blocks per edge of every matrix in the bucket
@@ -175,7 +200,7 @@ constexpr int kMaxPassDepth = 3;
 // sizes the grids, and the kernels, which decode their tile index.
 enum InvKind : int32_t {
     kInvPrepare = 0, kInvPanel = 1, kInvSyrk = 2, kInvTrtri = 3, kInvLauum = 4, kInvLauum2 = 5,
-    kInvVPart = 6, kInvVFin = 7
+    kInvVPart = 6, kInvVFin = 7, kInvBorder = 8, kInvBorderRun = 9
 };
 
 // V = U^-1 formed column by column beside the potrf steps (V U = I):
@@ -221,6 +246,10 @@ __host__ __device__ inline int64_t inv_tiles(int kind, int64_t nb, int64_t step)
             const int64_t c = step - 2;
             return c >= 1 && c < nb ? c : 0;
         }
+        case kInvBorder:  // one workgroup per block row of the leading part
+            return nb;
+        case kInvBorderRun:  // one workgroup per block row (or column) and run of blocks
+            return nb * border_runs(nb);
         case kInvPanel:  // one workgroup per block right of the diagonal, at least one
             return nb > step ? (nb - step - 1 > 1 ? nb - step - 1 : 1) : 0;
         case kInvSyrk: {  // step k applies step k-1's update to blocks (i, j), k < i <= j
@@ -254,5 +283,8 @@ hipError_t launch_inv_trtri_a(const InvLaunch& L, int64_t tiles, hipStream_t s);
 hipError_t launch_inv_trtri_b(const InvLaunch& L, int64_t tiles, hipStream_t s);
 hipError_t launch_inv_lauum(const InvLaunch& L, int64_t tiles, hipStream_t s);
 hipError_t launch_inv_lauum2(const InvLaunch& L, int64_t tiles, hipStream_t s);
+hipError_t launch_inv_border_w(const InvLaunch& L, int64_t tiles, hipStream_t s);
+hipError_t launch_inv_border_u(const InvLaunch& L, int64_t tiles, hipStream_t s);
+hipError_t launch_inv_border_v(const InvLaunch& L, int64_t tiles, hipStream_t s);
 
 }  // namespace kfac

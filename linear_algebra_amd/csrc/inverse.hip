@@ -34,6 +34,10 @@
 //                         groups are runs of 2^l blocks, or a balanced binary
 //                         tree when nb is just above a power of two; the
 //                         inner product is parked in the lower triangle of W;
+//   border    for an order d = 64m + 1 (d > 64), only the leading 64m x 64m
+//             part goes through the steps above; its last row and column are
+//             attached afterwards as one more (bordered) Cholesky step, by two
+//             matrix-vector launches, and lauum adds the border column of V;
 //   lauum     Z = V V^T (upper blocks), written as float32 to both triangles.
 //
 // Diagonal blocks of V are the inverses of the diagonal blocks of U, kept in
@@ -625,7 +629,8 @@ __device__ __forceinline__ void record_info(const InvMat& M, int k, int f) {
 
 // -------------------------------------------------------------- kernels --
 
-// W = sym(X) + gamma I on the upper blocks, identity in the padding.
+// W = sym(X) + gamma I on the upper blocks of the leading n x n part,
+// identity in the padding.
 __global__ __launch_bounds__(NT) void inv_prepare_kernel(InvLaunch L, int64_t tiles) {
     int mi;
     int64_t local;
@@ -633,19 +638,19 @@ __global__ __launch_bounds__(NT) void inv_prepare_kernel(InvLaunch L, int64_t ti
     const InvMat M = L.mats[mi];
     int bi, bj;
     upper_decode(local, M.nb, bi, bj);
-    const int64_t D = (int64_t)M.nb * B, d = M.d;
+    const int64_t D = (int64_t)M.nb * B, d = M.d, n = M.n;
     const int r0 = threadIdx.x >> 6, c = threadIdx.x & 63;
     float xv[PER];
 #pragma unroll
     for (int s = 0; s < PER; ++s) {
         const int64_t i = (int64_t)bi * B + r0 + 4 * s, j = (int64_t)bj * B + c;
-        xv[s] = (i < d && j < d && j >= i) ? as_global(M.x)[i * d + j] : 0.0f;
+        xv[s] = (i < n && j < n && j >= i) ? as_global(M.x)[i * d + j] : 0.0f;
     }
 #pragma unroll
     for (int s = 0; s < PER; ++s) {
         const int64_t i = (int64_t)bi * B + r0 + 4 * s, j = (int64_t)bj * B + c;
         double v;
-        if (i < d && j < d) {
+        if (i < n && j < n) {
             v = (double)xv[s];
             if (i == j) v += L.gamma;
         } else {
@@ -959,6 +964,7 @@ __global__ __launch_bounds__(NT) void inv_trtri_b_kernel(InvLaunch L, int64_t ti
 }
 
 // Z_IJ = sum_{t >= J} V_It V_Jt^T for I <= J; float32 out, both triangles.
+// For a bordered matrix V has one more column, v, and Z_IJ gains v_I v_J^T.
 __global__ __launch_bounds__(NT) void inv_lauum_kernel(InvLaunch L, int64_t tiles) {
     __shared__ double S[STAGE];
     static_assert(STAGE >= B * LD, "the output is transposed through the staging area");
@@ -973,7 +979,13 @@ __global__ __launch_bounds__(NT) void inv_lauum_kernel(InvLaunch L, int64_t tile
     // share the blocks of V row J
     int I, J;
     column_decode(local, I, J);
-    const int64_t D = (int64_t)M.nb * B, d = M.d;
+    const int64_t D = (int64_t)M.nb * B, d = M.d, n = M.n;
+    const bool bord = n < d;
+    // the border column of V at rows I (vb[0, 64)) and J (vb[64, 128)),
+    // visible after the first barrier of the block product
+    __shared__ double vb[2 * B];
+    if (bord && threadIdx.x < 2 * B)
+        vb[threadIdx.x] = as_global(M.bvec)[(int64_t)(threadIdx.x < B ? I : J) * B + (threadIdx.x & 63)];
     doublex4 acc[2][2];
     acc_zero(acc);
     auto V = [&](int row, int t) {
@@ -992,8 +1004,9 @@ __global__ __launch_bounds__(NT) void inv_lauum_kernel(InvLaunch L, int64_t tile
     for (int s = 0; s < PER; ++s) {
         const int r = q0 + 4 * s, c = l;
         const int64_t i = r0 + r, j = c0 + c;
-        if (i < d && j < d) {
-            const double v = (I != J || c >= r) ? As[r * LD + c] : As[c * LD + r];
+        if (i < n && j < n) {
+            double v = (I != J || c >= r) ? As[r * LD + c] : As[c * LD + r];
+            if (bord) v += vb[r] * vb[B + c];
             as_global(M.z)[i * d + j] = (float)v;
         }
     }
@@ -1002,7 +1015,11 @@ __global__ __launch_bounds__(NT) void inv_lauum_kernel(InvLaunch L, int64_t tile
         for (int s = 0; s < PER; ++s) {
             const int c = q0 + 4 * s, r = l;      // destination row c0+c, column r0+r
             const int64_t i = c0 + c, j = r0 + r;
-            if (i < d && j < d) as_global(M.z)[i * d + j] = (float)As[r * LD + c];
+            if (i < n && j < n) {
+                double v = As[r * LD + c];
+                if (bord) v += vb[B + c] * vb[r];
+                as_global(M.z)[i * d + j] = (float)v;
+            }
         }
     }
 }
@@ -1024,7 +1041,7 @@ __global__ __launch_bounds__(NT, 2) void inv_lauum2_kernel(InvLaunch L, int64_t 
     int I2, J2;
     column_decode(local, I2, J2);
     const int nb = M.nb;
-    const int64_t D = (int64_t)nb * B, d = M.d;
+    const int64_t D = (int64_t)nb * B, d = M.d, n = M.n;
     const int w = threadIdx.x >> 6, a = w >> 1, b = w & 1;
     const int I = 2 * I2 + a, J = 2 * J2 + b;
     const bool active = I < nb && J < nb && !(I2 == J2 && a > b);
@@ -1037,6 +1054,15 @@ __global__ __launch_bounds__(NT, 2) void inv_lauum2_kernel(InvLaunch L, int64_t 
     auto panel = [&](int r0, int t) {
         return Panel{{V(r0, t), V(r0 + 1, t)}, {r0 >= nb || t < r0, r0 + 1 >= nb || t < r0 + 1}};
     };
+    // the border column of V at the rows of block rows 2 I2, 2 I2 + 1
+    // (vb[0, 128)) and 2 J2, 2 J2 + 1 (vb[128, 256)), visible after the first
+    // barrier of the panel product
+    const bool bord = n < d;
+    __shared__ double vb[4 * B];
+    if (bord) {
+        const int64_t row = (threadIdx.x < 2 * B ? 2 * I2 * B : 2 * J2 * B - 2 * B) + threadIdx.x;
+        vb[threadIdx.x] = row < n ? as_global(M.bvec)[row] : 0.0;
+    }
     doublex4 acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -1046,7 +1072,11 @@ __global__ __launch_bounds__(NT, 2) void inv_lauum2_kernel(InvLaunch L, int64_t 
                false, I2 == J2, a, b, active);
     // each wave's block as float32 in LDS, then written with coalesced rows
     float* F = reinterpret_cast<float*>(S) + w * B * (B + 1);
-    for_acc4([&](int i, int j, int r, int row, int col) { F[row * (B + 1) + col] = (float)acc[i][j][r]; });
+    for_acc4([&](int i, int j, int r, int row, int col) {
+        double v = acc[i][j][r];
+        if (bord) v += vb[a * B + row] * vb[2 * B + b * B + col];
+        F[row * (B + 1) + col] = (float)v;
+    });
     __syncthreads();
     if (!active) return;
     const int64_t r0 = (int64_t)I * B, c0 = (int64_t)J * B;
@@ -1054,14 +1084,163 @@ __global__ __launch_bounds__(NT, 2) void inv_lauum2_kernel(InvLaunch L, int64_t 
     for (int r = 0; r < B; ++r) {
         const int c = l;
         const int64_t i = r0 + r, j = c0 + c;
-        if (i < d && j < d) as_global(M.z)[i * d + j] = (I != J || c >= r) ? F[r * (B + 1) + c] : F[c * (B + 1) + r];
+        if (i < n && j < n) as_global(M.z)[i * d + j] = (I != J || c >= r) ? F[r * (B + 1) + c] : F[c * (B + 1) + r];
     }
     if (I != J) {
         for (int c = 0; c < B; ++c) {
             const int r = l;   // destination row c0 + c, column r0 + r
             const int64_t i = c0 + c, j = r0 + r;
-            if (i < d && j < d) as_global(M.z)[i * d + j] = F[r * (B + 1) + c];
+            if (i < n && j < n) as_global(M.z)[i * d + j] = F[r * (B + 1) + c];
         }
+    }
+}
+
+// Block (row, t) of V = U^-1 in whichever place it is kept: above the
+// diagonal, or in block (t, row) below it when formed beside potrf; the
+// diagonal blocks in dinv.
+__device__ __forceinline__ Blk v_blk(const InvLaunch& L, const InvMat& M, int64_t D, int row, int t) {
+    if (L.vlow) return v_low(M, D, row, t);
+    return t == row ? Blk{M.dinv + (int64_t)row * BB, B, false}
+                    : Blk{M.w + (int64_t)row * B * D + (int64_t)t * B, D, false};
+}
+
+// The last row and column of a bordered matrix (order d = n + 1, leading
+// n x n part already factored, Y_11 = U^T U, V = U^-1), as one more step of
+// the Cholesky factorisation: with x the last column above the diagonal and
+// xi = x_nn + gamma, the factor of the whole matrix has the column
+// w = U^-T x = V^T x and the pivot mu = sqrt(xi - w^T w), and its inverse
+// the column v = -V w / mu and the pivot 1 / mu.  Three launches, each
+// workgroup summing a run of kBorderRun blocks, partial sums kept in the
+// matrix's border workspace and added in a fixed order.
+//
+// w: workgroup (matrix, c, q) sums V_ic^T x_i over i in run q of
+// [0, c], i = q kBorderRun + u.
+__global__ __launch_bounds__(NT) void inv_border_w_kernel(InvLaunch L, int64_t tiles) {
+    static_assert(NT == 4 * B && kBorderRun == 4, "four row groups of a block, one x value per thread and run");
+    __shared__ double xs[kBorderRun * B];
+    __shared__ double red[4][B];
+    int mi;
+    int64_t local;
+    if (blockIdx.x >= tiles || !locate(L, kInvBorderRun, blockIdx.x, mi, local)) return;
+    const InvMat M = L.mats[mi];
+    const int64_t runs = border_runs(M.nb);
+    const int c = (int)(local / runs), q = (int)(local % runs);
+    const int i0 = q * kBorderRun;
+    if (M.n == M.d || i0 > c) return;
+    const int64_t D = (int64_t)M.nb * B, d = M.d, n = M.n;
+    const int j = threadIdx.x & 63, g = threadIdx.x >> 6;
+    {
+        const int64_t row = (int64_t)i0 * B + threadIdx.x;   // < (c + 1) B <= n when kept
+        xs[threadIdx.x] = row < (int64_t)(c + 1) * B ? (double)as_global(M.x)[row * d + n] : 0.0;
+    }
+    double vv[kBorderRun][PER];
+#pragma unroll
+    for (int u = 0; u < kBorderRun; ++u) {
+        const int i = i0 + u <= c ? i0 + u : c;
+        const Blk b = v_blk(L, M, D, i, c);
+#pragma unroll
+        for (int s = 0; s < PER; ++s) vv[u][s] = as_global(b.p)[(int64_t)(g + 4 * s) * b.ld + j];
+    }
+    __syncthreads();
+    double acc = 0.0;
+#pragma unroll
+    for (int u = 0; u < kBorderRun; ++u) {
+        double t = 0.0;
+#pragma unroll
+        for (int s = 0; s < PER; ++s) t += vv[u][s] * xs[u * B + g + 4 * s];
+        acc += i0 + u <= c ? t : 0.0;
+    }
+    red[g][j] = acc;
+    __syncthreads();
+    if (g == 0)
+        as_global(M.bvec)[border_w_off(M.nb) + ((int64_t)c * runs + q) * B + j] =
+            red[0][j] + red[1][j] + red[2][j] + red[3][j];
+}
+
+// u = V w: workgroup (matrix, i, q) first completes w_c (its partials, in
+// run order) for c in run q of [i, nb), c = i + q kBorderRun + u, then sums
+// V_ic w_c.  The workgroups of row 0 cover every c once and also sum w^T w
+// over their run.
+__global__ __launch_bounds__(NT) void inv_border_u_kernel(InvLaunch L, int64_t tiles) {
+    __shared__ double red[B][B + 1];
+    int mi;
+    int64_t local;
+    if (blockIdx.x >= tiles || !locate(L, kInvBorderRun, blockIdx.x, mi, local)) return;
+    const InvMat M = L.mats[mi];
+    const int64_t runs = border_runs(M.nb);
+    const int i = (int)(local / runs), q = (int)(local % runs);
+    const int c0 = i + q * kBorderRun;
+    if (M.n == M.d || c0 >= M.nb) return;
+    const int64_t D = (int64_t)M.nb * B;
+    const double* wp = M.bvec + border_w_off(M.nb);
+    const int lane = threadIdx.x & 63, g = threadIdx.x >> 6;
+    double vv[kBorderRun][PER], wc[kBorderRun];
+#pragma unroll
+    for (int u = 0; u < kBorderRun; ++u) {
+        const int c = c0 + u < M.nb ? c0 + u : M.nb - 1;
+        const Blk b = v_blk(L, M, D, i, c);
+#pragma unroll
+        for (int s = 0; s < PER; ++s) vv[u][s] = as_global(b.p)[(int64_t)(g + 4 * s) * b.ld + lane];
+        double w = 0.0;
+        const int nq = (int)border_runs(c + 1);
+        for (int qq = 0; qq < nq; ++qq) w += as_global(wp)[((int64_t)c * runs + qq) * B + lane];
+        wc[u] = c0 + u < M.nb ? w : 0.0;
+    }
+    double acc[PER];
+#pragma unroll
+    for (int s = 0; s < PER; ++s) {
+        acc[s] = 0.0;
+#pragma unroll
+        for (int u = 0; u < kBorderRun; ++u) acc[s] += vv[u][s] * wc[u];
+    }
+#pragma unroll
+    for (int s = 0; s < PER; ++s) red[g + 4 * s][lane] = acc[s];
+    if (i == 0 && g == 0) {
+        double ss = 0.0;
+#pragma unroll
+        for (int u = 0; u < kBorderRun; ++u) ss += wc[u] * wc[u];
+        for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+        if (lane == 0) as_global(M.bvec)[border_ss_off(M.nb) + q] = ss;
+    }
+    __syncthreads();
+    if (threadIdx.x < B) {
+        const int r = threadIdx.x;
+        double u = 0.0;
+        for (int j = 0; j < B; ++j) u += red[r][j];
+        as_global(M.bvec)[border_u_off(M.nb) + ((int64_t)i * runs + q) * B + r] = u;
+    }
+}
+
+// v: workgroup (matrix, i) completes u_i (its partials, in run order) and
+// w^T w, stores v_i = -u_i / mu for the product V V^T, and writes the border
+// of the inverse, z_rn = z_nr = v_r / mu and z_nn = 1 / mu^2.  A pivot mu^2
+// that is not positive and finite is reported as info = d, unless the
+// leading part has failed already.
+__global__ __launch_bounds__(NT) void inv_border_v_kernel(InvLaunch L, int64_t tiles) {
+    int mi;
+    int64_t local;
+    if (blockIdx.x >= tiles || !locate(L, kInvBorder, blockIdx.x, mi, local)) return;
+    const InvMat M = L.mats[mi];
+    if (M.n == M.d || threadIdx.x >= B) return;
+    const int i = (int)local, r = threadIdx.x;
+    const int64_t d = M.d, n = M.n, runs = border_runs(M.nb);
+    double ss = 0.0;
+    for (int q = 0; q < runs; ++q) ss += as_global(M.bvec)[border_ss_off(M.nb) + q];
+    double u = 0.0;
+    const int nq = (int)border_runs(M.nb - i);
+    for (int q = 0; q < nq; ++q) u += as_global(M.bvec)[border_u_off(M.nb) + ((int64_t)i * runs + q) * B + r];
+    const double xi = (double)as_global(M.x)[n * d + n] + L.gamma;
+    const double mu2 = xi - ss;
+    const double mu = sqrt(mu2);
+    const double v = -u / mu;
+    const int64_t row = (int64_t)i * B + r;
+    as_global(M.bvec)[row] = v;
+    const float zb = (float)(v / mu);
+    as_global(M.z)[row * d + n] = zb;
+    as_global(M.z)[n * d + row] = zb;
+    if (i == 0 && r == 0) {
+        as_global(M.z)[n * d + n] = (float)(1.0 / mu2);
+        if (!(mu2 > 0.0 && isfinite(mu2)) && *as_global(M.info) == 0) *as_global(M.info) = (int32_t)d;
     }
 }
 
@@ -1081,5 +1260,8 @@ hipError_t launch_inv_trtri_a(const InvLaunch& L, int64_t t, hipStream_t s) { re
 hipError_t launch_inv_trtri_b(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_trtri_b_kernel, L, t, s, true); }
 hipError_t launch_inv_lauum(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_lauum_kernel, L, t, s, true); }
 hipError_t launch_inv_lauum2(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_lauum2_kernel, L, t, s, true); }
+hipError_t launch_inv_border_w(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_border_w_kernel, L, t, s); }
+hipError_t launch_inv_border_u(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_border_u_kernel, L, t, s); }
+hipError_t launch_inv_border_v(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_border_v_kernel, L, t, s); }
 
 }  // namespace kfac

@@ -195,7 +195,7 @@ InvPlan plan_inverse(int n, const int64_t* d) {
     InvPlan p;
     p.order.resize(n);
     std::iota(p.order.begin(), p.order.end(), 0);
-    auto nb = [&](int i) { return (int)ceil_div(d[i], kInvNB); };
+    auto nb = [&](int i) { return (int)ceil_div(inv_extent(d[i]), kInvNB); };
     std::stable_sort(p.order.begin(), p.order.end(), [&](int a, int b) { return nb(a) > nb(b); });
     for (int s = 0; s < n; ++s) {
         const int b = nb(p.order[s]);
@@ -232,10 +232,11 @@ size_t inverse_ws(int n, const int64_t* d) {
     c.take(sizeof(InvMat) * n);
     c.take(sizeof(InvBucket) * n);
     for (int i = 0; i < n; ++i) {
-        const int64_t nb = ceil_div(d[i], kInvNB), D = nb * kInvNB;
+        const int64_t m = inv_extent(d[i]), nb = ceil_div(m, kInvNB), D = nb * kInvNB;
         c.take(sizeof(double) * (size_t)(D * D));
         c.take(sizeof(double) * (size_t)(D * kInvNB));
         if (fused) c.take(sizeof(double) * (size_t)(2 * vpart_slots(nb - 1) * kInvNB * kInvNB));
+        if (m < d[i]) c.take(sizeof(double) * (size_t)border_doubles(nb));
     }
     return c.used;
 }
@@ -404,19 +405,23 @@ kfac_status_t kfac_damped_inverse(int n, const float* const* x, const int64_t* d
     InvMat* mats_dev = static_cast<InvMat*>(c.take(sizeof(InvMat) * n));
     InvBucket* buckets_dev = static_cast<InvBucket*>(c.take(sizeof(InvBucket) * n));
     // per-matrix scratch in original order
-    std::vector<double*> w(n), dinv(n), part(n);
+    std::vector<double*> w(n), dinv(n), part(n), bvec(n);
+    bool bordered = false;
     for (int i = 0; i < n; ++i) {
-        const int64_t nb = ceil_div(d[i], kInvNB), D = nb * kInvNB;
+        const int64_t m = inv_extent(d[i]), nb = ceil_div(m, kInvNB), D = nb * kInvNB;
         w[i] = static_cast<double*>(c.take(sizeof(double) * (size_t)(D * D)));
         dinv[i] = static_cast<double*>(c.take(sizeof(double) * (size_t)(D * kInvNB)));
         part[i] = fused ? static_cast<double*>(c.take(sizeof(double) * (size_t)(2 * vpart_slots(nb - 1) * kInvNB * kInvNB)))
                           : nullptr;
+        bvec[i] = m < d[i] ? static_cast<double*>(c.take(sizeof(double) * (size_t)border_doubles(nb))) : nullptr;
+        bordered = bordered || m < d[i];
     }
     std::vector<InvMat> mats(n);
     for (int s = 0; s < n; ++s) {
         const int i = p.order[s];
-        mats[s] = InvMat{x[i], xinv[i], w[i], dinv[i], info + i, part[i], (int32_t)d[i],
-                         (int32_t)ceil_div(d[i], kInvNB)};
+        const int64_t m = inv_extent(d[i]);
+        mats[s] = InvMat{x[i], xinv[i], w[i], dinv[i], info + i, part[i], bvec[i], (int32_t)d[i], (int32_t)m,
+                         (int32_t)ceil_div(m, kInvNB), 0};
     }
     hipError_t e = upload_table(mats_dev, mats.data(), sizeof(InvMat) * n, stream);
     if (e == hipSuccess) e = upload_table(buckets_dev, p.buckets.data(), sizeof(InvBucket) * p.buckets.size(), stream);
@@ -453,6 +458,15 @@ kfac_status_t kfac_damped_inverse(int n, const float* const* x, const int64_t* d
         const int64_t t = bucket_tiles(p, kInvTrtri, lvl);
         e = launch_inv_trtri_a(L, t, stream);
         if (e == hipSuccess) e = launch_inv_trtri_b(L, t, stream);
+    }
+    if (bordered && e == hipSuccess) {
+        // the last row and column of the bordered matrices: w = V^T x, u = V w,
+        // then mu^2 = xi - w^T w, v = -u / mu and the border of the output
+        L.step = 0;
+        const int64_t runs = bucket_tiles(p, kInvBorderRun, 0);
+        e = launch_inv_border_w(L, runs, stream);
+        if (e == hipSuccess) e = launch_inv_border_u(L, runs, stream);
+        if (e == hipSuccess) e = launch_inv_border_v(L, bucket_tiles(p, kInvBorder, 0), stream);
     }
     if (e == hipSuccess) {
         L.step = 0;

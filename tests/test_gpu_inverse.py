@@ -100,6 +100,76 @@ def test_inverse_nan_reports_info():
     assert info[0] == rinfo == 11
 
 
+# Orders one above a multiple of 64 (the factor A of a layer with a bias)
+# factor the leading part in blocks and attach the last row and column
+# afterwards as a border; these cases aim at that path.
+@pytest.mark.parametrize("k", [1, 64, 65, 100, 129])
+def test_inverse_bordered_info_reports_first_failing_pivot(k):
+    d = 129
+    say("inverse bordered info", k)
+    gamma = np.float32(1e-3)
+    bad = np.eye(d, dtype=np.float32)
+    bad[k - 1, k - 1] = np.float32(-1.0) - gamma
+    good = spd_f32(np.random.default_rng(k), d, 300)
+    zs, info = gpu_inverse([good, bad, good], gamma)
+    _, rinfo = oracle.damped_inverse(bad, gamma)
+    assert rinfo == k
+    assert list(info) == [0, k, 0]
+    ref, _ = oracle.damped_inverse(good, gamma)
+    assert rel_fro(zs[0], ref) <= TOL and rel_fro(zs[2], ref) <= TOL
+
+
+@pytest.mark.parametrize("where", [(5, 128), (128, 128)])
+def test_inverse_bordered_nan_in_border_reports_info(where):
+    d = 129
+    x = np.eye(d, dtype=np.float32)
+    x[where] = np.nan
+    _, info = gpu_inverse([x], 1e-3)
+    _, rinfo = oracle.damped_inverse(x, np.float32(1e-3))
+    assert info[0] == rinfo == d
+
+
+def test_inverse_bordered_closed_form_and_upper_only():
+    gamma = np.float32(0.25)
+    d = 193
+    diag = np.linspace(0.0, 5.0, d).astype(np.float32)
+    zs, info = gpu_inverse([np.diag(diag)], gamma)
+    assert info[0] == 0
+    np.testing.assert_allclose(zs[0], np.diag(1.0 / (diag.astype(np.float64) + float(gamma))), rtol=1e-6, atol=1e-30)
+    x = spd_f32(np.random.default_rng(3), d, 400)
+    xg = x.copy()
+    xg[np.tril_indices(d, -1)] = 1e30
+    z1, _ = gpu_inverse([x], 1e-2)
+    z2, _ = gpu_inverse([xg], 1e-2)
+    np.testing.assert_array_equal(z1[0], z2[0])
+    ref, _ = oracle.damped_inverse(x, np.float32(1e-2))
+    assert rel_fro(z1[0], ref) <= TOL
+
+
+def test_inverse_bordered_nearly_dependent_last_row():
+    """The last row is nearly a combination of the others, so its pivot
+    xi - w^T w is small (cancellation) and the inverse is large along one
+    direction."""
+    rng = np.random.default_rng(12)
+    n = 128
+    x11 = spd_f32(rng, n, 3 * n).astype(np.float64)
+    a = rng.standard_normal(n) / np.sqrt(n)
+    col = x11 @ a
+    x = np.zeros((n + 1, n + 1))
+    x[:n, :n] = x11
+    x[:n, n] = x[n, :n] = col
+    x[n, n] = a @ x11 @ a + 1e-2
+    x = x.astype(np.float32)
+    gamma = np.float32(1e-3)
+    zs, info = gpu_inverse([x], gamma)
+    ref, rinfo = oracle.damped_inverse(x, gamma)
+    assert info[0] == rinfo == 0
+    err = rel_fro(zs[0], ref)
+    say("  bordered, small last pivot: err", err, "z_nn", zs[0][n, n])
+    assert err <= TOL
+    np.testing.assert_array_equal(zs[0], zs[0].T)
+
+
 def config_factor_inputs(cid, rows_cap=None):
     """float32 factors (A's then G's) of a workload's first step, from the
     oracle; rows_cap limits the rows drawn per layer (same recipe)."""
