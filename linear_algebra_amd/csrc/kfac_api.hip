@@ -4,6 +4,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <initializer_list>
 #include <numeric>
 #include <vector>
 
@@ -271,6 +272,27 @@ hipError_t upload_table(void* dst_device, const void* src_host, size_t nbytes, h
     return hipSuccess;
 }
 
+// Several tables carved one after another from the workspace, uploaded as
+// one stretch (the alignment gaps between them written as zeros), so that
+// they cost the launches of one table.
+struct TablePart {
+    void* dst;
+    const void* src;
+    size_t bytes;
+};
+hipError_t upload_tables(std::initializer_list<TablePart> parts, hipStream_t stream) {
+    uint8_t* lo = static_cast<uint8_t*>(parts.begin()->dst);
+    uint8_t* hi = lo;
+    for (const TablePart& t : parts) {
+        uint8_t* d = static_cast<uint8_t*>(t.dst);
+        if (d < lo) return hipErrorInvalidValue;
+        hi = std::max(hi, d + t.bytes);
+    }
+    std::vector<uint8_t> blob((size_t)(hi - lo), 0);
+    for (const TablePart& t : parts) std::memcpy(blob.data() + (static_cast<uint8_t*>(t.dst) - lo), t.src, t.bytes);
+    return upload_table(lo, blob.data(), blob.size(), stream);
+}
+
 }  // namespace kfac
 
 using namespace kfac;
@@ -423,8 +445,9 @@ kfac_status_t kfac_damped_inverse(int n, const float* const* x, const int64_t* d
         mats[s] = InvMat{x[i], xinv[i], w[i], dinv[i], info + i, part[i], bvec[i], (int32_t)d[i], (int32_t)m,
                          (int32_t)ceil_div(m, kInvNB), 0};
     }
-    hipError_t e = upload_table(mats_dev, mats.data(), sizeof(InvMat) * n, stream);
-    if (e == hipSuccess) e = upload_table(buckets_dev, p.buckets.data(), sizeof(InvBucket) * p.buckets.size(), stream);
+    hipError_t e = upload_tables({{mats_dev, mats.data(), sizeof(InvMat) * n},
+                                  {buckets_dev, p.buckets.data(), sizeof(InvBucket) * p.buckets.size()}},
+                                 stream);
     if (e != hipSuccess) return KFAC_ERR_HIP;
 
     InvLaunch L{mats_dev, buckets_dev, (int32_t)p.buckets.size(), 0, (double)gamma, 0, 0, 0, 0, fused ? 1 : 0, 0};
@@ -530,8 +553,8 @@ kfac_status_t kfac_precondition(int n, const float* const* ginv, const float* co
             part2 += (int64_t)b.ntiles * b.ksplit * kGemmTile * kGemmTile;
         }
     }
-    hipError_t e = upload_table(p1_dev, p.p1.data(), sizeof(GemmProb) * n, stream);
-    if (e == hipSuccess) e = upload_table(p2_dev, p.p2.data(), sizeof(GemmProb) * n, stream);
+    hipError_t e = upload_tables({{p1_dev, p.p1.data(), sizeof(GemmProb) * n}, {p2_dev, p.p2.data(), sizeof(GemmProb) * n}},
+                                 stream);
     if (e != hipSuccess) return KFAC_ERR_HIP;
     GemmLaunch L1{p1_dev, n, 0, 0.0f, 0};
     e = launch_gemm(L1, p.items1, stream, false);
