@@ -127,58 +127,74 @@ __device__ __forceinline__ void mma_block(doublex4 (&acc)[2][2], const double* A
 }
 
 // Products of many blocks stage their operands in halves of 32 k-columns,
-// double buffered: while the matrix cores work on one half, the next half is
-// written to LDS and the half after it is loaded from memory, with one
-// barrier per half.  Four staged halves (A and B, two buffers each) take as
-// much LDS as two whole blocks, so two workgroups still share a CU.
+// double buffered, one barrier per half.  The load units copy each half
+// from global memory straight into LDS (16 bytes per lane,
+// global_load_lds_dwordx4), so the data never passes through registers:
+// the loads of the next half are issued right after the barrier that frees
+// its buffer and land while the matrix cores work on the current one.  Four
+// staged halves (A and B, two buffers each) take 64 KB, so two workgroups
+// still share a CU.
 constexpr int KH = 32;            // k-columns per half
-constexpr int LDH = KH + 1;       // LDS row stride of a staged half (doubles)
-constexpr int HB = B * LDH;       // doubles per staged half
-constexpr int HPER = B * KH / NT; // half-block elements per thread (8)
-constexpr int STAGE = 4 * HB;     // LDS doubles of the staging area
+constexpr int HD = B * KH;        // doubles per staged half (unpadded)
 
-// Half h of block b, as [m][k] with k in [32h, 32h + 32): for an untransposed
-// block m is its row and k its column, for a transposed one the reverse.
-// Each wave reads 256- or 512-byte row segments.
-__device__ __forceinline__ void fetch_half(double (&v)[HPER], const Blk& b, int h) {
-    const int t = threadIdx.x;
-    if (!b.trans) {
-        const int c = KH * h + (t & 31), r = t >> 5;
-#pragma unroll
-        for (int s = 0; s < HPER; ++s) v[s] = as_global(b.p)[(int64_t)(r + 8 * s) * b.ld + c];
-    } else {
-        const int c = t & 63, r = KH * h + (t >> 6);
-#pragma unroll
-        for (int s = 0; s < HPER; ++s) v[s] = as_global(b.p)[(int64_t)(r + 4 * s) * b.ld + c];
-    }
+// The staging area: two LDS arrays of one padded 64 x 64 block each, which
+// hold the A and B halves of buffer 0 and of buffer 1.  They are separate
+// arrays, not one, so that the compiler can tell the copies into one buffer
+// from the reads of the other and does not wait for the copies first.
+constexpr int SLOT = B * LD;
+static_assert(SLOT >= 2 * HD, "the A and B halves of a buffer fit in one array");
+struct Stage {
+    double* s0;
+    double* s1;
+};
+
+// Layouts of a staged half, as [m][k] with k in [32h, 32h + 32) (for an
+// untransposed block m is its row and k its column, for a transposed one
+// the reverse):
+//   untransposed: row m holds its 16 pairs of k-values, pair k/2 at
+//     position (k/2) xor (m & 7), so the 16 rows an operand fragment reads
+//     at one k fall on 8 bank groups instead of one;
+//   transposed: [k][m], m contiguous, as the block's rows lie in memory.
+__device__ __forceinline__ int staged_at(bool trans, int m, int k) {
+    return trans ? k * B + m : m * KH + ((((k >> 1) ^ (m & 7)) << 1) | (k & 1));
 }
-__device__ __forceinline__ void put_half(double* S, const double (&v)[HPER], bool trans) {
-    const int t = threadIdx.x;
-    if (!trans) {
-        const int k = t & 31, m = t >> 5;
+
+// Issues the copy of half h of block b into S (HD doubles).  Wave w,
+// instruction s fills pairs 64 (4 w + s) + lane of the layout; each lane
+// fetches the pair that belongs there, so every row segment of the block is
+// read by consecutive lanes.
+__device__ __forceinline__ void stage_half(double* S, const Blk& b, int h) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
-        for (int s = 0; s < HPER; ++s) S[(m + 8 * s) * LDH + k] = v[s];
-    } else {
-        const int m = t & 63, k = t >> 6;
-#pragma unroll
-        for (int s = 0; s < HPER; ++s) S[m * LDH + k + 4 * s] = v[s];
+    for (int s = 0; s < HD / (2 * NT); ++s) {
+        const int first = (4 * w + s) * 64;
+        const int p = first + lane;
+        const double* src;
+        if (!b.trans) {
+            const int m = p >> 4, c = (p & 15) ^ (m & 7);
+            src = b.p + (int64_t)m * b.ld + KH * h + 2 * c;
+        } else {
+            const int k = p >> 5, mc = p & 31;
+            src = b.p + (int64_t)(KH * h + k) * b.ld + 2 * mc;
+        }
+        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                         (void __attribute__((address_space(3)))*)(S + 2 * first), 16, 0, 0);
     }
 }
 
 // acc[m][n] += (neg ? -1 : 1) * sum_k A[m][k] B[n][k] over one staged half;
 // the wave layout of mma_block.
-__device__ __forceinline__ void mma_half(doublex4 (&acc)[2][2], const double* A, const double* Bm, bool neg) {
+__device__ __forceinline__ void mma_staged(doublex4 (&acc)[2][2], const double* A, bool ta, const double* Bm, bool tb,
+                                           bool neg) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wr = wave >> 1, wc = wave & 1;
     const int li = lane & 15, lk = lane >> 4;
-    const double* a0p = A + (wr * 32 + li) * LDH + lk;
-    const double* a1p = a0p + 16 * LDH;
-    const double* b0p = Bm + (wc * 32 + li) * LDH + lk;
-    const double* b1p = b0p + 16 * LDH;
+    const int ma = wr * 32 + li, nb = wc * 32 + li;
 #pragma unroll
     for (int k0 = 0; k0 < KH; k0 += 4) {
-        double a0 = a0p[k0], a1 = a1p[k0];
-        const double b0 = b0p[k0], b1 = b1p[k0];
+        const int k = k0 + lk;
+        double a0 = A[staged_at(ta, ma, k)], a1 = A[staged_at(ta, ma + 16, k)];
+        const double b0 = Bm[staged_at(tb, nb, k)], b1 = Bm[staged_at(tb, nb + 16, k)];
         if (neg) { a0 = -a0; a1 = -a1; }
         acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, acc[0][0], 0, 0, 0);
         acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, acc[0][1], 0, 0, 0);
@@ -189,47 +205,40 @@ __device__ __forceinline__ void mma_half(doublex4 (&acc)[2][2], const double* A,
 
 // acc += (neg ? -1 : 1) sum_{t in [t0, t1)} A_t B_t^T, A_t and B_t the
 // 64 x 64 blocks srcA(t), srcB(t) (staged as [m][k]); `same` reuses A for B.
-// S is the staging area (STAGE doubles of LDS).  Each half's loads are in
-// flight for one half of products before they are written to LDS.  Ends
-// with a barrier, so S may be reused at once.
+// Half 0 of every block goes through buffer 0, half 1 through buffer 1.
+// For each half: wait for its copies, barrier (its data is visible, and the
+// other buffer, read by the half before, is free), issue the copies of the
+// next half into the other buffer, multiply.  Ends with a barrier, so the
+// staging area may be reused at once.
 template <typename FA, typename FB>
-__device__ __forceinline__ void block_gemm(doublex4 (&acc)[2][2], double* S, int t0, int t1, FA srcA, FB srcB,
+__device__ __forceinline__ void block_gemm(doublex4 (&acc)[2][2], const Stage& S, int t0, int t1, FA srcA, FB srcB,
                                            bool neg, bool same) {
     if (t0 >= t1) return;
-    double* A0 = S;
-    double* A1 = S + HB;
-    double* B0 = same ? A0 : S + 2 * HB;
-    double* B1 = same ? A1 : S + 3 * HB;
-    double ra0[HPER], rb0[HPER], ra1[HPER], rb1[HPER];
-    fetch_half(ra0, srcA(t0), 0);
-    if (!same) fetch_half(rb0, srcB(t0), 0);
-    fetch_half(ra1, srcA(t0), 1);
-    if (!same) fetch_half(rb1, srcB(t0), 1);
-    __syncthreads();   // earlier users of S are done
-    put_half(A0, ra0, srcA(t0).trans);
-    if (!same) put_half(B0, rb0, srcB(t0).trans);
-    __syncthreads();
+    // offsets, not a choice of pointers, so that each stays visibly inside
+    // its array
+    double* const A0 = S.s0;
+    double* const B0 = S.s0 + (same ? 0 : HD);
+    double* const A1 = S.s1;
+    double* const B1 = S.s1 + (same ? 0 : HD);
+    __syncthreads();   // earlier users of the staging area are done
+    stage_half(A0, srcA(t0), 0);
+    if (!same) stage_half(B0, srcB(t0), 0);
     for (int t = t0; t < t1; ++t) {
-        const bool more = t + 1 < t1;
-        // half 1 of step t into buffer 1; half 0 of step t + 1 in flight
-        put_half(A1, ra1, srcA(t).trans);
-        if (!same) put_half(B1, rb1, srcB(t).trans);
-        if (more) {
-            fetch_half(ra0, srcA(t + 1), 0);
-            if (!same) fetch_half(rb0, srcB(t + 1), 0);
-        }
-        mma_half(acc, A0, B0, neg);
+        const bool ta = srcA(t).trans, tb = same ? ta : srcB(t).trans;
+        __builtin_amdgcn_s_waitcnt(0);   // the copies of half 0 (the only loads in flight)
         __syncthreads();
-        // half 0 of step t + 1 into buffer 0; its half 1 in flight
-        if (more) {
-            put_half(A0, ra0, srcA(t + 1).trans);
-            if (!same) put_half(B0, rb0, srcB(t + 1).trans);
-            fetch_half(ra1, srcA(t + 1), 1);
-            if (!same) fetch_half(rb1, srcB(t + 1), 1);
-        }
-        mma_half(acc, A1, B1, neg);
+        stage_half(A1, srcA(t), 1);
+        if (!same) stage_half(B1, srcB(t), 1);
+        mma_staged(acc, A0, ta, B0, tb, neg);
+        __builtin_amdgcn_s_waitcnt(0);   // the copies of half 1
         __syncthreads();
+        if (t + 1 < t1) {
+            stage_half(A0, srcA(t + 1), 0);
+            if (!same) stage_half(B0, srcB(t + 1), 0);
+        }
+        mma_staged(acc, A1, ta, B1, tb, neg);
     }
+    __syncthreads();
 }
 
 // ---- 128 x 128 output tiles --------------------------------------------
@@ -744,7 +753,7 @@ __device__ __forceinline__ Blk v_low(const InvMat& M, int64_t D, int i, int m) {
 
 // Partial sum of column c = step - 1 of V, slot `local`: chunk q of row i,
 // sum_{m in chunk} V_im U_mc over m in [i + q kVChunk, min(i + (q + 1) kVChunk, c - 1)).
-__device__ __forceinline__ void v_partial(const InvLaunch& L, const InvMat& M, int64_t local, double* S) {
+__device__ __forceinline__ void v_partial(const InvLaunch& L, const InvMat& M, int64_t local, const Stage& S) {
     const int c = L.step - 1;
     const int64_t D = (int64_t)M.nb * B;
     int q = 0;
@@ -765,11 +774,11 @@ __device__ __forceinline__ void v_partial(const InvLaunch& L, const InvMat& M, i
 
 // Block (i, c) of V, c = step - 2: T = (its partial blocks) + V_i,c-1 U_c-1,c,
 // then V_ic = -T V_cc, stored into block (c, i) of W (below the diagonal).
-__device__ __forceinline__ void v_finalize(const InvLaunch& L, const InvMat& M, int64_t local, double* S) {
+__device__ __forceinline__ void v_finalize(const InvLaunch& L, const InvMat& M, int64_t local, const Stage& S) {
     const int c = L.step - 2, i = (int)local;
     const int64_t D = (int64_t)M.nb * B;
-    double* As = S;
-    double* Bs = S + B * LD;
+    double* As = S.s0;
+    double* Bs = S.s1;
     doublex4 acc[2][2];
     acc_zero(acc);
     const int nq = i <= c - 2 ? (c - 1 - i + kVChunk - 1) / kVChunk : 0;
@@ -810,10 +819,10 @@ __device__ __forceinline__ void v_finalize(const InvLaunch& L, const InvMat& M, 
 // W_ij -= U_{k-1,i}^T U_{k-1,j} to the blocks k < i <= j, XCD by XCD.
 __global__ __launch_bounds__(NT, 2) void inv_step_kernel(InvLaunch L, int64_t tiles) {
     __shared__ PanelScratch R;
-    __shared__ double S[STAGE];
-    static_assert(STAGE >= 2 * B * LD, "two 64 x 64 blocks fit in the staging area");
-    double* As = S;
-    double* Bs = S + B * LD;
+    __shared__ double S0[SLOT], S1[SLOT];
+    const Stage S{S0, S1};
+    double* As = S0;
+    double* Bs = S1;
     int mi;
     int64_t local;
     const int64_t b = blockIdx.x;
@@ -919,7 +928,8 @@ __device__ __forceinline__ bool trtri_decode(int64_t local, int nb, int step, in
 
 // T_IJ = sum_{t in G2, t <= J} U_It V_tJ, parked in W's lower block (J, I).
 __global__ __launch_bounds__(NT) void inv_trtri_a_kernel(InvLaunch L, int64_t tiles) {
-    __shared__ double S[STAGE];
+    __shared__ double S0[SLOT], S1[SLOT];
+    const Stage S{S0, S1};
     int mi;
     int64_t local;
     const int64_t item = xcd_runs<kRun>(blockIdx.x);
@@ -942,7 +952,8 @@ __global__ __launch_bounds__(NT) void inv_trtri_a_kernel(InvLaunch L, int64_t ti
 
 // V_IJ = - sum_{t in G1, t >= I} V_It T_tJ, written over U_IJ.
 __global__ __launch_bounds__(NT) void inv_trtri_b_kernel(InvLaunch L, int64_t tiles) {
-    __shared__ double S[STAGE];
+    __shared__ double S0[SLOT], S1[SLOT];
+    const Stage S{S0, S1};
     int mi;
     int64_t local;
     const int64_t item = xcd_runs<kRun>(blockIdx.x);
@@ -966,9 +977,9 @@ __global__ __launch_bounds__(NT) void inv_trtri_b_kernel(InvLaunch L, int64_t ti
 // Z_IJ = sum_{t >= J} V_It V_Jt^T for I <= J; float32 out, both triangles.
 // For a bordered matrix V has one more column, v, and Z_IJ gains v_I v_J^T.
 __global__ __launch_bounds__(NT) void inv_lauum_kernel(InvLaunch L, int64_t tiles) {
-    __shared__ double S[STAGE];
-    static_assert(STAGE >= B * LD, "the output is transposed through the staging area");
-    double* As = S;
+    __shared__ double S0[SLOT], S1[SLOT];
+    const Stage S{S0, S1};
+    double* As = S0;   // the output is transposed through one block of the staging area
     int mi;
     int64_t local;
     const int64_t item = xcd_runs<kRun>(blockIdx.x);
