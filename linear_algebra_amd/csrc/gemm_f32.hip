@@ -29,19 +29,8 @@ constexpr int BK = kGemmBK;
 constexpr int NT = kGemmThreads;
 constexpr int kGemmRun = 16;        // items per XCD run in large launches
 constexpr int64_t kGemmRunsMin = 2048;
-constexpr int LOADS = BK * BM / NT;  // elements of one operand slab per thread
 constexpr int KPL = BK / 2;          // slab rows each lane feeds to the matrix cores
-static_assert(LOADS % 4 == 0 && KPL % 4 == 0, "slabs move in float4 pieces");
 constexpr int SUB_STAGES = kGemmSubK / BK;
-
-template <bool BF16>
-__device__ __forceinline__ float load_op(const void* base, int64_t idx) {
-    if constexpr (BF16) {
-        return bf16_to_f32(static_cast<const uint16_t*>(base)[idx]);
-    } else {
-        return static_cast<const float*>(base)[idx];
-    }
-}
 
 __device__ __forceinline__ int find_prob(const GemmProb* probs, int nprob, int64_t item, bool reduce) {
     int lo = 0, hi = nprob - 1;
@@ -74,7 +63,6 @@ __device__ __forceinline__ void elem_store(const GemmProb& P, int i, int j, floa
     if (elem_kept(P, i, j)) as_global(P.c)[(int64_t)i * P.ldc + j] = r;
 }
 
-constexpr int LDK = BK + 4;        // LDS row stride (floats): [m][k], k contiguous
 constexpr uint32_t kOOB = 0x80000000u;  // buffer offset past any slab: loads return 0
 constexpr int RED_SLICES = 16;     // workgroups per partial tile in the reduce
 
@@ -87,16 +75,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const void* base, in
     // scalar registers (a per-lane descriptor would need a waterfall loop)
     const int bytes = __builtin_amdgcn_readfirstlane(rows * (int)ld * esz);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p), (short)0, bytes, 0x00020000);
-}
-
-template <bool BF16>
-__device__ __forceinline__ float slab_load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    if constexpr (BF16) {
-        return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
-    } else {
-        // the builtin returns the 32 bits as an integer: reinterpret, do not convert
-        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
-    }
 }
 
 // Writes a finished 128 x 128 tile: to the split-K partial buffer when K is
@@ -177,57 +155,71 @@ __device__ __forceinline__ TileWork decode_item(const GemmLaunch& L, int64_t ite
     return w;
 }
 
-template <bool BF16>
-__global__ __launch_bounds__(NT, 2) void gemm_tn_kernel(GemmLaunch L, int64_t items) {
-    __shared__ __attribute__((aligned(16))) float As[2][BM * LDK];
-    __shared__ __attribute__((aligned(16))) float Bs[2][BM * LDK];
+// float32 slabs are copied by the load units straight into LDS
+// (buffer_load_dwordx4 ... lds, 16 bytes per lane), as [k][m] rows of the
+// tile, the way they lie in memory: no registers, no transposing stores.
+// A lane copies 4 consecutive columns of one slab row; a chunk wholly past
+// the last column gets an offset beyond the descriptor and reads as zero
+// (one that straddles it reads a few values of the next row, which only
+// reach outputs that are not stored), and rows past the end of the slab
+// read as zero through the descriptor.  The two buffers of each operand
+// are separate LDS arrays, so that the compiler can tell the copies into
+// one from the reads of the other.
+constexpr int SLAB = BK * BM;                 // floats per staged slab
+constexpr int kSlabCopies = SLAB / (4 * NT);  // copy instructions per wave and slab (4)
 
-    const int64_t item = L.runs ? xcd_runs<kGemmRun>(blockIdx.x) : xcd_remap(blockIdx.x, gridDim.x);
-    if (item >= items) return;
-    const TileWork W = decode_item(L, item);
+__device__ __forceinline__ void stage_slab(float* S, __amdgpu_buffer_rsrc_t r, const uint32_t (&off)[kSlabCopies]) {
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int s = 0; s < kSlabCopies; ++s)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(S + 256 * (4 * w + s)), 16,
+                                                 off[s], 0, 0, 0);
+}
+
+// acc += one staged slab: lane l supplies row/column (l % 32) of its
+// 32-wide blocks and, at step s, the slab row 16 (l / 32) + s (the sum over
+// the slab does not depend on how its rows are paired).
+__device__ __forceinline__ void mma_slab(floatx16 (&acc)[2][2], const float* A, const float* Bm, int wm, int wn,
+                                         int lane) {
+    const int fr = lane & 31, fk = (lane >> 5) * KPL;
+    const float* pa = A + fk * BM + wm * 64 + fr;
+    const float* pb = Bm + fk * BM + wn * 64 + fr;
+#pragma unroll
+    for (int s = 0; s < KPL; ++s) {
+        const float a0 = pa[s * BM], a1 = pa[s * BM + 32];
+        const float b0 = pb[s * BM], b1 = pb[s * BM + 32];
+        acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
+        acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
+        acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
+        acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
+    }
+}
+
+// One tile; SAME (a factor tile on the diagonal) stages only A and reads
+// both operands from it.
+template <bool SAME>
+__device__ __forceinline__ void gemm_f32_tile(const GemmLaunch& L, const TileWork& W, float* A0, float* A1, float* B0,
+                                              float* B1) {
     const GemmProb& P = W.P;
-    const int kc = W.kc, t = W.t, m0 = W.m0, n0 = W.n0, k_begin = W.k_begin, k_end = W.k_end;
-    const bool same = W.same;
-    constexpr int esz = BF16 ? 2 : 4;
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int k_begin = W.k_begin, k_end = W.k_end;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const bool active = W.active;
+    float* const Bb0 = SAME ? A0 : B0;
+    float* const Bb1 = SAME ? A1 : B1;
 
-    // Thread t loads column lc of the tile, slab rows lr8 .. lr8 + LOADS - 1;
-    // the byte offsets inside a slab are the same for every slab.
-    const int lc = tid & (BM - 1);
-    const int lr8 = (tid >> 7) * LOADS;
-    uint32_t offa[LOADS], offb[LOADS];
+    // copy s of this lane: slab row k, columns 4c .. 4c + 3 of the tile
+    uint32_t offa[kSlabCopies], offb[kSlabCopies];
 #pragma unroll
-    for (int s = 0; s < LOADS; ++s) {
-        const int row = lr8 + s;
-        offa[s] = (m0 + lc < P.M) ? (uint32_t)((row * P.lda + m0 + lc) * esz) : kOOB;
-        offb[s] = (n0 + lc < P.N) ? (uint32_t)((row * P.ldb + n0 + lc) * esz) : kOOB;
+    for (int s = 0; s < kSlabCopies; ++s) {
+        const int chunk = (4 * wave + s) * 64 + lane;
+        const int k = chunk >> 5, m = 4 * (chunk & 31);
+        offa[s] = (W.m0 + m < P.M) ? (uint32_t)((k * P.lda + W.m0 + m) * 4) : kOOB;
+        offb[s] = (W.n0 + m < P.N) ? (uint32_t)((k * P.ldb + W.n0 + m) * 4) : kOOB;
     }
-
-    float ra[LOADS], rb[LOADS];
-    auto gload = [&](int k0) {
-        const __amdgpu_buffer_rsrc_t rA = slab_rsrc(P.a, P.lda, k0, k_end, esz);
-#pragma unroll
-        for (int s = 0; s < LOADS; ++s) ra[s] = slab_load<BF16>(rA, offa[s]);
-        if (!same) {
-            const __amdgpu_buffer_rsrc_t rB = slab_rsrc(P.b, P.ldb, k0, k_end, esz);
-#pragma unroll
-            for (int s = 0; s < LOADS; ++s) rb[s] = slab_load<BF16>(rB, offb[s]);
-        }
-    };
-    auto sstore = [&](int buf) {
-        float4* da = reinterpret_cast<float4*>(&As[buf][lc * LDK + lr8]);
-#pragma unroll
-        for (int q = 0; q < LOADS / 4; ++q) da[q] = make_float4(ra[4 * q], ra[4 * q + 1], ra[4 * q + 2], ra[4 * q + 3]);
-        if (!same) {
-            float4* db = reinterpret_cast<float4*>(&Bs[buf][lc * LDK + lr8]);
-#pragma unroll
-            for (int q = 0; q < LOADS / 4; ++q) db[q] = make_float4(rb[4 * q], rb[4 * q + 1], rb[4 * q + 2], rb[4 * q + 3]);
-        }
+    auto stage = [&](float* SA, float* SB, int k0) {
+        stage_slab(SA, slab_rsrc(P.a, P.lda, k0, k_end, 4), offa);
+        if (!SAME) stage_slab(SB, slab_rsrc(P.b, P.ldb, k0, k_end, 4), offb);
     };
 
     floatx16 acc[2][2], sum[2][2];
@@ -237,62 +229,53 @@ __global__ __launch_bounds__(NT, 2) void gemm_tn_kernel(GemmLaunch L, int64_t it
         for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r) { acc[a][b][r] = 0.0f; sum[a][b][r] = 0.0f; }
+    auto fold = [&](int st, int nstages) {
+        if ((st + 1) % SUB_STAGES == 0 || st + 1 == nstages) {
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    sum[a][b] += acc[a][b];
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+                }
+        }
+    };
 
     const int nstages = (k_end - k_begin + BK - 1) / BK;
-    if (nstages > 0) {
-        gload(k_begin);
-        sstore(0);
-    }
-    __syncthreads();
-
-    // MFMA fragments: lane l supplies rows/columns (l % 32) of its 32-wide
-    // blocks and, over the KPL steps s of a slab, the slab rows KPL*(l/32) + s
-    // (the sum over the slab does not depend on how its rows are paired).
-    const int fr = lane & 31;
-    const int fk = (lane >> 5) * KPL;
-
-    for (int st = 0; st < nstages; ++st) {
-        const int buf = st & 1;
-        if (st + 1 < nstages) gload(k_begin + (st + 1) * BK);
-        if (active) {
-            const float* Ab = As[buf];
-            const float* Bb = same ? As[buf] : Bs[buf];
-            float4 fa[2][KPL / 4], fb[2][KPL / 4];
-#pragma unroll
-            for (int a = 0; a < 2; ++a) {
-                const float4* pa = reinterpret_cast<const float4*>(&Ab[(wm * 64 + a * 32 + fr) * LDK + fk]);
-                const float4* pb = reinterpret_cast<const float4*>(&Bb[(wn * 64 + a * 32 + fr) * LDK + fk]);
-#pragma unroll
-                for (int q = 0; q < KPL / 4; ++q) {
-                    fa[a][q] = pa[q];
-                    fb[a][q] = pb[q];
-                }
-            }
-#pragma unroll
-            for (int s = 0; s < KPL; ++s) {
-                const float a0 = fa[0][s >> 2][s & 3], a1 = fa[1][s >> 2][s & 3];
-                const float b0 = fb[0][s >> 2][s & 3], b1 = fb[1][s >> 2][s & 3];
-                acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
-                acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
-                acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
-                acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
-            }
-            if ((st + 1) % SUB_STAGES == 0 || st + 1 == nstages) {
-#pragma unroll
-                for (int a = 0; a < 2; ++a)
-#pragma unroll
-                    for (int b = 0; b < 2; ++b) {
-                        sum[a][b] += acc[a][b];
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
-                    }
-            }
-        }
-        if (st + 1 < nstages) sstore(buf ^ 1);
+    if (nstages > 0) stage(A0, B0, k_begin);
+    // slab st in buffer st % 2; the copies of slab st + 1 are issued right
+    // after the barrier that frees their buffer
+    for (int st = 0; st < nstages; st += 2) {
+        __builtin_amdgcn_s_waitcnt(0);   // this slab's copies (the only loads in flight)
         __syncthreads();
+        if (st + 1 < nstages) stage(A1, B1, k_begin + (st + 1) * BK);
+        if (active) {
+            mma_slab(acc, A0, Bb0, wm, wn, lane);
+            fold(st, nstages);
+        }
+        if (st + 1 >= nstages) break;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (st + 2 < nstages) stage(A0, B0, k_begin + (st + 2) * BK);
+        if (active) {
+            mma_slab(acc, A1, Bb1, wm, wn, lane);
+            fold(st + 1, nstages);
+        }
     }
+    store_tile(P, L, sum, W.kc, W.t, W.m0, W.n0, wm, wn, lane);
+}
 
-    store_tile(P, L, sum, kc, t, m0, n0, wm, wn, lane);
+__global__ __launch_bounds__(NT, 2) void gemm_tn_kernel(GemmLaunch L, int64_t items) {
+    __shared__ __attribute__((aligned(16))) float A0[SLAB];
+    __shared__ __attribute__((aligned(16))) float A1[SLAB];
+    __shared__ __attribute__((aligned(16))) float B0[SLAB];
+    __shared__ __attribute__((aligned(16))) float B1[SLAB];
+    const int64_t item = L.runs ? xcd_runs<kGemmRun>(blockIdx.x) : xcd_remap(blockIdx.x, gridDim.x);
+    if (item >= items) return;
+    const TileWork W = decode_item(L, item);
+    if (W.same) gemm_f32_tile<true>(L, W, A0, A1, B0, B1);
+    else gemm_f32_tile<false>(L, W, A0, A1, B0, B1);
 }
 
 
@@ -482,7 +465,7 @@ hipError_t launch_gemm(const GemmLaunch& L, int64_t items, hipStream_t stream, b
     if (bf16) {
         hipLaunchKernelGGL(gemm_tn_bf16_kernel, dim3((unsigned)grid), dim3(NT), 0, stream, R, items);
     } else {
-        hipLaunchKernelGGL(gemm_tn_kernel<false>, dim3((unsigned)grid), dim3(NT), 0, stream, R, items);
+        hipLaunchKernelGGL(gemm_tn_kernel, dim3((unsigned)grid), dim3(NT), 0, stream, R, items);
     }
     return hipGetLastError();
 }
