@@ -68,12 +68,17 @@ constexpr int RED_SLICES = 16;     // workgroups per partial tile in the reduce
 
 // Buffer resource over rows [k0, min(k0 + BK, k_end)) of a row-major
 // operand; rows past the end of the slab read as zero.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const void* base, int64_t ld, int k0, int k_end, int esz) {
+// The range ends at column `cols` of the slab's last row (the operand's
+// last element there), not at the end of that row: a 16-byte copy that
+// straddles the last column then stops at the operand's end instead of
+// reading past it.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const void* base, int64_t ld, int k0, int k_end, int esz,
+                                                            int cols) {
     const char* p = static_cast<const char*>(base) + (int64_t)k0 * ld * esz;
     const int rows = max(0, min(BK, k_end - k0));
     // every operand is uniform; readfirstlane keeps the descriptor in
     // scalar registers (a per-lane descriptor would need a waterfall loop)
-    const int bytes = __builtin_amdgcn_readfirstlane(rows * (int)ld * esz);
+    const int bytes = __builtin_amdgcn_readfirstlane(rows > 0 ? ((rows - 1) * (int)ld + cols) * esz : 0);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p), (short)0, bytes, 0x00020000);
 }
 
@@ -161,8 +166,9 @@ __device__ __forceinline__ TileWork decode_item(const GemmLaunch& L, int64_t ite
 // A lane copies 4 consecutive columns of one slab row; a chunk wholly past
 // the last column gets an offset beyond the descriptor and reads as zero
 // (one that straddles it reads a few values of the next row, which only
-// reach outputs that are not stored), and rows past the end of the slab
-// read as zero through the descriptor.  The two buffers of each operand
+// reach outputs that are not stored, or, in the slab's last row, stops at
+// the descriptor's end), and rows past the end of the slab read as zero
+// through the descriptor.  The two buffers of each operand
 // are separate LDS arrays, so that the compiler can tell the copies into
 // one from the reads of the other.
 constexpr int SLAB = BK * BM;                 // floats per staged slab
@@ -218,8 +224,8 @@ __device__ __forceinline__ void gemm_f32_tile(const GemmLaunch& L, const TileWor
         offb[s] = (W.n0 + m < P.N) ? (uint32_t)((k * P.ldb + W.n0 + m) * 4) : kOOB;
     }
     auto stage = [&](float* SA, float* SB, int k0) {
-        stage_slab(SA, slab_rsrc(P.a, P.lda, k0, k_end, 4), offa);
-        if (!SAME) stage_slab(SB, slab_rsrc(P.b, P.ldb, k0, k_end, 4), offb);
+        stage_slab(SA, slab_rsrc(P.a, P.lda, k0, k_end, 4, P.M), offa);
+        if (!SAME) stage_slab(SB, slab_rsrc(P.b, P.ldb, k0, k_end, 4, P.N), offb);
     };
 
     floatx16 acc[2][2], sum[2][2];
