@@ -6,18 +6,20 @@
 // contiguous row segments and the global loads coalesce.
 //
 // Tile 128 x 128 per workgroup of 4 waves (2 x 2, 64 x 64 each, four
-// v_mfma_f32_32x32x2f32 accumulators per wave).  K is staged through two LDS
-// buffers of kGemmBK rows per operand; the next slab is fetched into registers
-// while the current one feeds the matrix cores.  Products are summed in
-// float32 over sub-chunks of kGemmSubK rows and then folded into a second
-// float32 sum, which keeps the rounding error of long reductions (hundreds of
-// thousands of rows) near that of a 512-term sum.
+// accumulators per wave).  K is staged through two LDS buffers of kGemmBK
+// rows per operand: the copies of the next slab are in flight while the
+// current one feeds the matrix cores.  Products are summed in float32 over
+// sub-chunks of kGemmSubK rows and then folded into a second float32 sum,
+// which keeps the rounding error of long reductions (hundreds of thousands
+// of rows) near that of a 512-term sum.
 //
 // Operands are read with buffer loads whose descriptor covers one K-slab:
 // rows past the end of the input read as zero without a branch, and the
-// per-thread offsets inside a slab are computed once.  LDS holds each slab
-// as [m][k] with k contiguous, so a lane fetches its k-values of a block
-// with 128-bit reads and the slab's MFMAs issue back to back.
+// per-thread offsets inside a slab are computed once.  float32 slabs go
+// from memory straight into LDS as [k][m] rows (v_mfma_f32_32x32x2f32 takes
+// one k-value per lane); bfloat16 slabs pass through registers and are
+// stored as [m][k], because v_mfma_f32_32x32x16_bf16 takes 8 consecutive
+// k-values per lane, read as one 16-byte LDS access.
 #include "device_common.h"
 #include "internal.h"
 

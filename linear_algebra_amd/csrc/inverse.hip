@@ -46,8 +46,9 @@
 // step, so independent inverses of different layers run side by side.
 //
 // Block products stage their operands in LDS in halves of 32 k-columns,
-// double buffered, so that the next half is written and the one after it
-// fetched while the matrix cores work on the current one.
+// double buffered: the load units copy the next half straight into LDS
+// while the matrix cores work on the current one.  The 128 x 128 products
+// of lauum2 stage quarters through registers.
 #include <float.h>
 
 #include "device_common.h"
