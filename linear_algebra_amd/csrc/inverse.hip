@@ -138,10 +138,11 @@ __device__ __forceinline__ void mma_block(doublex4 (&acc)[2][2], const double* A
 constexpr int KH = 32;            // k-columns per half
 constexpr int HD = B * KH;        // doubles per staged half (unpadded)
 
-// The staging area: two LDS arrays of one padded 64 x 64 block each, which
-// hold the A and B halves of buffer 0 and of buffer 1.  They are separate
-// arrays, not one, so that the compiler can tell the copies into one buffer
-// from the reads of the other and does not wait for the copies first.
+// The staging area: two LDS arrays, which hold the A and B halves of
+// buffer 0 and of buffer 1 (the first is a padded 64 x 64 block, which the
+// epilogues also use).  They are separate arrays, not one, so that the
+// compiler can tell the copies into one buffer from the reads of the other
+// and does not wait for the copies first.
 constexpr int SLOT = B * LD;
 static_assert(SLOT >= 2 * HD, "the A and B halves of a buffer fit in one array");
 struct Stage {
@@ -149,42 +150,47 @@ struct Stage {
     double* s1;
 };
 
-// Layouts of a staged half, as [m][k] with k in [32h, 32h + 32) (for an
-// untransposed block m is its row and k its column, for a transposed one
-// the reverse):
-//   untransposed: row m holds its 16 pairs of k-values, pair k/2 at
+// Layouts of a staged piece of K k-columns (K = 32: a half, K = 16: a
+// quarter), as [m][k] (for an untransposed block m is its row and k its
+// column, for a transposed one the reverse):
+//   untransposed: row m holds its K / 2 pairs of k-values, pair k/2 at
 //     position (k/2) xor (m & 7), so the 16 rows an operand fragment reads
 //     at one k fall on 8 bank groups instead of one;
 //   transposed: [k][m], m contiguous, as the block's rows lie in memory.
+template <int K>
 __device__ __forceinline__ int staged_at(bool trans, int m, int k) {
-    return trans ? k * B + m : m * KH + ((((k >> 1) ^ (m & 7)) << 1) | (k & 1));
+    return trans ? k * B + m : m * K + ((((k >> 1) ^ (m & 7)) << 1) | (k & 1));
 }
 
-// Issues the copy of half h of block b into S (HD doubles).  Wave w,
-// instruction s fills pairs 64 (4 w + s) + lane of the layout; each lane
-// fetches the pair that belongs there, so every row segment of the block is
-// read by consecutive lanes.
-__device__ __forceinline__ void stage_half(double* S, const Blk& b, int h) {
+// Issues the copy of piece q (k-columns [K q, K q + K)) of block b into S
+// (B K doubles).  Wave w, instruction s fills pairs 64 (n w + s) + lane of
+// the layout; each lane fetches the pair that belongs there, so every row
+// segment of the block is read by consecutive lanes.
+template <int K>
+__device__ __forceinline__ void stage_piece(double* S, const Blk& b, int q) {
+    constexpr int n = B * K / (2 * NT);   // copy instructions per wave
+    constexpr int rowpairs = K / 2;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
-    for (int s = 0; s < HD / (2 * NT); ++s) {
-        const int first = (4 * w + s) * 64;
+    for (int s = 0; s < n; ++s) {
+        const int first = (n * w + s) * 64;
         const int p = first + lane;
         const double* src;
         if (!b.trans) {
-            const int m = p >> 4, c = (p & 15) ^ (m & 7);
-            src = b.p + (int64_t)m * b.ld + KH * h + 2 * c;
+            const int m = p / rowpairs, c = (p % rowpairs) ^ (m & 7);
+            src = b.p + (int64_t)m * b.ld + K * q + 2 * c;
         } else {
             const int k = p >> 5, mc = p & 31;
-            src = b.p + (int64_t)(KH * h + k) * b.ld + 2 * mc;
+            src = b.p + (int64_t)(K * q + k) * b.ld + 2 * mc;
         }
         __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
                                          (void __attribute__((address_space(3)))*)(S + 2 * first), 16, 0, 0);
     }
 }
 
-// acc[m][n] += (neg ? -1 : 1) * sum_k A[m][k] B[n][k] over one staged half;
+// acc[m][n] += (neg ? -1 : 1) * sum_k A[m][k] B[n][k] over one staged piece;
 // the wave layout of mma_block.
+template <int K>
 __device__ __forceinline__ void mma_staged(doublex4 (&acc)[2][2], const double* A, bool ta, const double* Bm, bool tb,
                                            bool neg) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -192,10 +198,10 @@ __device__ __forceinline__ void mma_staged(doublex4 (&acc)[2][2], const double* 
     const int li = lane & 15, lk = lane >> 4;
     const int ma = wr * 32 + li, nb = wc * 32 + li;
 #pragma unroll
-    for (int k0 = 0; k0 < KH; k0 += 4) {
+    for (int k0 = 0; k0 < K; k0 += 4) {
         const int k = k0 + lk;
-        double a0 = A[staged_at(ta, ma, k)], a1 = A[staged_at(ta, ma + 16, k)];
-        const double b0 = Bm[staged_at(tb, nb, k)], b1 = Bm[staged_at(tb, nb + 16, k)];
+        double a0 = A[staged_at<K>(ta, ma, k)], a1 = A[staged_at<K>(ta, ma + 16, k)];
+        const double b0 = Bm[staged_at<K>(tb, nb, k)], b1 = Bm[staged_at<K>(tb, nb + 16, k)];
         if (neg) { a0 = -a0; a1 = -a1; }
         acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, acc[0][0], 0, 0, 0);
         acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, acc[0][1], 0, 0, 0);
@@ -206,38 +212,46 @@ __device__ __forceinline__ void mma_staged(doublex4 (&acc)[2][2], const double* 
 
 // acc += (neg ? -1 : 1) sum_{t in [t0, t1)} A_t B_t^T, A_t and B_t the
 // 64 x 64 blocks srcA(t), srcB(t) (staged as [m][k]); `same` reuses A for B.
-// Half 0 of every block goes through buffer 0, half 1 through buffer 1.
-// For each half: wait for its copies, barrier (its data is visible, and the
-// other buffer, read by the half before, is free), issue the copies of the
-// next half into the other buffer, multiply.  Ends with a barrier, so the
-// staging area may be reused at once.
-template <typename FA, typename FB>
+// Each block is staged in 64 / K pieces of K k-columns; even pieces go
+// through buffer 0, odd ones through buffer 1 (each buffer holds the A and
+// B pieces, 2 B K doubles, at the start of its array).  For each piece: wait
+// for its copies, barrier (its data is visible, and the other buffer, read
+// by the piece before, is free), issue the copies of the next piece into
+// the other buffer, multiply.  Ends with a barrier, so the staging area may
+// be reused at once.
+template <int K = KH, typename FA, typename FB>
 __device__ __forceinline__ void block_gemm(doublex4 (&acc)[2][2], const Stage& S, int t0, int t1, FA srcA, FB srcB,
                                            bool neg, bool same) {
+    constexpr int P = B / K;   // pieces per block, even
+    constexpr int PD = B * K;  // doubles per staged piece
+    static_assert(P % 2 == 0, "pieces alternate between the buffers within a block");
     if (t0 >= t1) return;
     // offsets, not a choice of pointers, so that each stays visibly inside
     // its array
     double* const A0 = S.s0;
-    double* const B0 = S.s0 + (same ? 0 : HD);
+    double* const B0 = S.s0 + (same ? 0 : PD);
     double* const A1 = S.s1;
-    double* const B1 = S.s1 + (same ? 0 : HD);
+    double* const B1 = S.s1 + (same ? 0 : PD);
     __syncthreads();   // earlier users of the staging area are done
-    stage_half(A0, srcA(t0), 0);
-    if (!same) stage_half(B0, srcB(t0), 0);
-    for (int t = t0; t < t1; ++t) {
+    stage_piece<K>(A0, srcA(t0), 0);
+    if (!same) stage_piece<K>(B0, srcB(t0), 0);
+    const int pieces = P * (t1 - t0);
+    for (int j = 0; j < pieces; j += 2) {
+        const int t = t0 + j / P, q = j % P;   // pieces q (buffer 0) and q + 1 (buffer 1) of block t
         const bool ta = srcA(t).trans, tb = same ? ta : srcB(t).trans;
-        __builtin_amdgcn_s_waitcnt(0);   // the copies of half 0 (the only loads in flight)
+        __builtin_amdgcn_s_waitcnt(0);   // the copies of piece j (the only loads in flight)
         __syncthreads();
-        stage_half(A1, srcA(t), 1);
-        if (!same) stage_half(B1, srcB(t), 1);
-        mma_staged(acc, A0, ta, B0, tb, neg);
-        __builtin_amdgcn_s_waitcnt(0);   // the copies of half 1
+        stage_piece<K>(A1, srcA(t), q + 1);
+        if (!same) stage_piece<K>(B1, srcB(t), q + 1);
+        mma_staged<K>(acc, A0, ta, B0, tb, neg);
+        __builtin_amdgcn_s_waitcnt(0);   // the copies of piece j + 1
         __syncthreads();
-        if (t + 1 < t1) {
-            stage_half(A0, srcA(t + 1), 0);
-            if (!same) stage_half(B0, srcB(t + 1), 0);
+        if (j + 2 < pieces) {
+            const int tn = t0 + (j + 2) / P, qn = (j + 2) % P;
+            stage_piece<K>(A0, srcA(tn), qn);
+            if (!same) stage_piece<K>(B0, srcB(tn), qn);
         }
-        mma_staged(acc, A1, ta, B1, tb, neg);
+        mma_staged<K>(acc, A1, ta, B1, tb, neg);
     }
     __syncthreads();
 }
@@ -927,9 +941,12 @@ __device__ __forceinline__ bool trtri_decode(int64_t local, int nb, int step, in
     return true;
 }
 
+constexpr int KT = 16;   // k-columns per staged piece in the triangular-inverse products
+
 // T_IJ = sum_{t in G2, t <= J} U_It V_tJ, parked in W's lower block (J, I).
-__global__ __launch_bounds__(NT) void inv_trtri_a_kernel(InvLaunch L, int64_t tiles) {
-    __shared__ double S0[SLOT], S1[SLOT];
+__global__ __launch_bounds__(NT, 4) void inv_trtri_a_kernel(InvLaunch L, int64_t tiles) {
+    // quarters of 16 k-columns (a 32 KB staging area): four workgroups share a CU
+    __shared__ double S0[2 * B * KT], S1[2 * B * KT];
     const Stage S{S0, S1};
     int mi;
     int64_t local;
@@ -941,7 +958,7 @@ __global__ __launch_bounds__(NT) void inv_trtri_a_kernel(InvLaunch L, int64_t ti
     const int64_t D = (int64_t)M.nb * B;
     doublex4 acc[2][2];
     acc_zero(acc);
-    block_gemm(acc, S, g1_end, J + 1,
+    block_gemm<KT>(acc, S, g1_end, J + 1,
                [&](int t) { return Blk{M.w + (int64_t)I * B * D + (int64_t)t * B, D, false}; },   // U_It
                [&](int t) {                                                                     // V_tJ
                    return t == J ? Blk{M.dinv + (int64_t)J * BB, B, true}
@@ -952,8 +969,9 @@ __global__ __launch_bounds__(NT) void inv_trtri_a_kernel(InvLaunch L, int64_t ti
 }
 
 // V_IJ = - sum_{t in G1, t >= I} V_It T_tJ, written over U_IJ.
-__global__ __launch_bounds__(NT) void inv_trtri_b_kernel(InvLaunch L, int64_t tiles) {
-    __shared__ double S0[SLOT], S1[SLOT];
+__global__ __launch_bounds__(NT, 4) void inv_trtri_b_kernel(InvLaunch L, int64_t tiles) {
+    // quarters of 16 k-columns (a 32 KB staging area): four workgroups share a CU
+    __shared__ double S0[2 * B * KT], S1[2 * B * KT];
     const Stage S{S0, S1};
     int mi;
     int64_t local;
@@ -965,7 +983,7 @@ __global__ __launch_bounds__(NT) void inv_trtri_b_kernel(InvLaunch L, int64_t ti
     const int64_t D = (int64_t)M.nb * B;
     doublex4 acc[2][2];
     acc_zero(acc);
-    block_gemm(acc, S, I, g1_end,
+    block_gemm<KT>(acc, S, I, g1_end,
                [&](int t) {                                                                     // V_It
                    return t == I ? Blk{M.dinv + (int64_t)I * BB, B, false}
                                  : Blk{M.w + (int64_t)I * B * D + (int64_t)t * B, D, false};
@@ -977,10 +995,15 @@ __global__ __launch_bounds__(NT) void inv_trtri_b_kernel(InvLaunch L, int64_t ti
 
 // Z_IJ = sum_{t >= J} V_It V_Jt^T for I <= J; float32 out, both triangles.
 // For a bordered matrix V has one more column, v, and Z_IJ gains v_I v_J^T.
-__global__ __launch_bounds__(NT) void inv_lauum_kernel(InvLaunch L, int64_t tiles) {
-    __shared__ double S0[SLOT], S1[SLOT];
+__global__ __launch_bounds__(NT, 4) void inv_lauum_kernel(InvLaunch L, int64_t tiles) {
+    // quarters of 16 k-columns, and the output transposed through LDS as
+    // float32: the staging area is 33 KB and four workgroups share a CU
+    constexpr int KL = 16;
+    constexpr int FD = B * (B + 1) / 2;   // a 64 x 65 float32 block, in doubles
+    static_assert(FD >= 2 * B * KL, "the first array also holds the A and B quarters of buffer 0");
+    __shared__ double S0[FD], S1[2 * B * KL];
     const Stage S{S0, S1};
-    double* As = S0;   // the output is transposed through one block of the staging area
+    float* F = reinterpret_cast<float*>(S0);
     int mi;
     int64_t local;
     const int64_t item = xcd_runs<kRun>(blockIdx.x);
@@ -1005,10 +1028,15 @@ __global__ __launch_bounds__(NT) void inv_lauum_kernel(InvLaunch L, int64_t tile
         return t == row ? Blk{M.dinv + (int64_t)row * BB, B, false}
                         : Blk{M.w + (int64_t)row * B * D + (int64_t)t * B, D, false};
     };
-    block_gemm(acc, S, J, M.nb, [&](int t) { return V(I, t); }, [&](int t) { return V(J, t); }, false,
+    block_gemm<KL>(acc, S, J, M.nb, [&](int t) { return V(I, t); }, [&](int t) { return V(J, t); }, false,
                I == J);
-    __syncthreads();
-    acc_to_lds(acc, As);
+    // each element with its border term, rounded to float32, into F; both
+    // triangles are written from F, so the output is exactly symmetric
+    for_acc([&](int a, int b, int r, int row, int col) {
+        double v = acc[a][b][r];
+        if (bord) v += vb[row] * vb[B + col];
+        F[row * (B + 1) + col] = (float)v;
+    });
     __syncthreads();
     const int64_t r0 = (int64_t)I * B, c0 = (int64_t)J * B;
     const int q0 = threadIdx.x >> 6, l = threadIdx.x & 63;
@@ -1016,22 +1044,14 @@ __global__ __launch_bounds__(NT) void inv_lauum_kernel(InvLaunch L, int64_t tile
     for (int s = 0; s < PER; ++s) {
         const int r = q0 + 4 * s, c = l;
         const int64_t i = r0 + r, j = c0 + c;
-        if (i < n && j < n) {
-            double v = (I != J || c >= r) ? As[r * LD + c] : As[c * LD + r];
-            if (bord) v += vb[r] * vb[B + c];
-            as_global(M.z)[i * d + j] = (float)v;
-        }
+        if (i < n && j < n) as_global(M.z)[i * d + j] = (I != J || c >= r) ? F[r * (B + 1) + c] : F[c * (B + 1) + r];
     }
     if (I != J) {
 #pragma unroll
         for (int s = 0; s < PER; ++s) {
             const int c = q0 + 4 * s, r = l;      // destination row c0+c, column r0+r
             const int64_t i = c0 + c, j = r0 + r;
-            if (i < n && j < n) {
-                double v = As[r * LD + c];
-                if (bord) v += vb[B + c] * vb[r];
-                as_global(M.z)[i * d + j] = (float)v;
-            }
+            if (i < n && j < n) as_global(M.z)[i * d + j] = F[r * (B + 1) + c];
         }
     }
 }
