@@ -199,7 +199,7 @@ constexpr int kMaxPassDepth = 3;
 // given potrf step (trsm, syrk) or trtri level.  Shared by the host, which
 // sizes the grids, and the kernels, which decode their tile index.
 enum InvKind : int32_t {
-    kInvPrepare = 0, kInvPanel = 1, kInvSyrk = 2, kInvTrtri = 3, kInvLauum = 4, kInvLauum2 = 5,
+    kInvPrepare = 0, kInvPanel = 1, kInvSyrk = 2, kInvTrtri = 3, kInvLauum = 4,
     kInvVPart = 6, kInvVFin = 7, kInvBorder = 8, kInvBorderRun = 9
 };
 
@@ -234,10 +234,6 @@ __host__ __device__ inline int64_t inv_tiles(int kind, int64_t nb, int64_t step)
         case kInvPrepare:
         case kInvLauum:
             return nb * (nb + 1) / 2;
-        case kInvLauum2: {  // 2 x 2 groups of blocks, upper triangle
-            const int64_t n2 = (nb + 1) / 2;
-            return n2 * (n2 + 1) / 2;
-        }
         case kInvVPart: {  // partial sums of column step - 1
             const int64_t c = step - 1;
             return c >= 2 && c < nb ? vpart_slots(c) : 0;
@@ -282,7 +278,6 @@ hipError_t launch_inv_step(const InvLaunch& L, int64_t tiles, hipStream_t s);
 hipError_t launch_inv_trtri_a(const InvLaunch& L, int64_t tiles, hipStream_t s);
 hipError_t launch_inv_trtri_b(const InvLaunch& L, int64_t tiles, hipStream_t s);
 hipError_t launch_inv_lauum(const InvLaunch& L, int64_t tiles, hipStream_t s);
-hipError_t launch_inv_lauum2(const InvLaunch& L, int64_t tiles, hipStream_t s);
 hipError_t launch_inv_border_w(const InvLaunch& L, int64_t tiles, hipStream_t s);
 hipError_t launch_inv_border_u(const InvLaunch& L, int64_t tiles, hipStream_t s);
 hipError_t launch_inv_border_v(const InvLaunch& L, int64_t tiles, hipStream_t s);

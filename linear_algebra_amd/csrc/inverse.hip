@@ -47,8 +47,7 @@
 //
 // Block products stage their operands in LDS in halves of 32 k-columns,
 // double buffered: the load units copy the next half straight into LDS
-// while the matrix cores work on the current one.  The 128 x 128 products
-// of lauum2 stage quarters through registers.
+// while the matrix cores work on the current one.
 #include <float.h>
 
 #include "device_common.h"
@@ -254,157 +253,6 @@ __device__ __forceinline__ void block_gemm(doublex4 (&acc)[2][2], const Stage& S
         mma_staged<K>(acc, A1, ta, B1, tb, neg);
     }
     __syncthreads();
-}
-
-// ---- 128 x 128 output tiles --------------------------------------------
-// A workgroup computes a 2 x 2 group of output blocks, wave (a, b) block
-// (a, b), from panels of two stacked 64 x 64 blocks.  Per flop this loads half
-// as many bytes from memory and writes half as many to LDS as 64 x 64 tiles.
-// The panels are staged in quarters of 16 k-columns, double buffered, which
-// keeps two workgroups on a CU.
-constexpr int KQ = 16;                // k-columns per staged quarter
-constexpr int LDQ = KQ + 1;           // LDS row stride of a staged quarter (doubles)
-constexpr int QB = 2 * B * LDQ;       // doubles per staged panel quarter (128 rows)
-constexpr int QPER = 2 * B * KQ / NT; // panel-quarter elements per thread (8)
-constexpr int STAGE2 = 4 * QB;        // LDS doubles of the staging area
-
-// Two 64 x 64 blocks stacked into a 128-row panel (in the [m][k] convention
-// of Blk); a block flagged zero is staged as zeros and not read.
-struct Panel {
-    Blk blk[2];
-    bool zero[2];
-};
-
-// Loads go through buffer descriptors whose base moves with the quarter, so
-// a thread keeps one 32-bit offset per block instead of a 64-bit address per
-// element and quarter (which do not fit in registers next to the tile).
-__device__ __forceinline__ double load_f64(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
-    return __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0));
-}
-__device__ __forceinline__ void fetch_quarter(double (&v)[QPER], const Panel& P, int q) {
-    const int t = threadIdx.x;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const Blk& b = P.blk[h];
-        if (P.zero[h]) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) v[4 * h + s] = 0.0;
-            continue;
-        }
-        const int ld = __builtin_amdgcn_readfirstlane((int)b.ld);
-        const char* base = reinterpret_cast<const char*>(b.p) + (b.trans ? (int64_t)KQ * q * ld : (int64_t)KQ * q) * 8;
-        const __amdgpu_buffer_rsrc_t r =
-            __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, B * ld * 8, 0x00020000);
-        if (!b.trans) {   // rows (t >> 4) + 16 s, columns 16 q + (t & 15)
-            const uint32_t off = (uint32_t)(((t >> 4) * ld + (t & 15)) * 8);
-#pragma unroll
-            for (int s = 0; s < 4; ++s) v[4 * h + s] = load_f64(r, off, (uint32_t)(16 * s * ld * 8));
-        } else {          // rows 16 q + (t >> 6) + 4 s, columns t & 63
-            const uint32_t off = (uint32_t)(((t >> 6) * ld + (t & 63)) * 8);
-#pragma unroll
-            for (int s = 0; s < 4; ++s) v[4 * h + s] = load_f64(r, off, (uint32_t)(4 * s * ld * 8));
-        }
-    }
-}
-__device__ __forceinline__ void put_quarter(double* S, const double (&v)[QPER], const Panel& P) {
-    const int t = threadIdx.x;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        if (P.zero[h] || !P.blk[h].trans) {
-            const int k = t & 15, m = B * h + (t >> 4);
-#pragma unroll
-            for (int s = 0; s < 4; ++s) S[(m + 16 * s) * LDQ + k] = v[4 * h + s];
-        } else {
-            const int m = B * h + (t & 63), k = t >> 6;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) S[m * LDQ + k + 4 * s] = v[4 * h + s];
-        }
-    }
-}
-
-// acc[i][j] += (neg ? -1 : 1) sum_k A[64a + 16i + .][k] B[64b + 16j + .][k]
-// over one staged quarter: wave (a, b) computes its whole 64 x 64 block as
-// 4 x 4 blocks of v_mfma_f64_16x16x4f64.
-__device__ __forceinline__ void mma_quarter(doublex4 (&acc)[4][4], const double* SA, const double* SB, int a, int b,
-                                            bool neg) {
-    const int lane = threadIdx.x & 63, li = lane & 15, lk = lane >> 4;
-    const double* ap = SA + (B * a + li) * LDQ + lk;
-    const double* bp = SB + (B * b + li) * LDQ + lk;
-#pragma unroll
-    for (int k0 = 0; k0 < KQ; k0 += 4) {
-        double av[4], bv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            av[i] = ap[16 * i * LDQ + k0];
-            if (neg) av[i] = -av[i];
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) bv[j] = bp[16 * j * LDQ + k0];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[i], bv[j], acc[i][j], 0, 0, 0);
-    }
-}
-
-// acc += (neg ? -1 : 1) sum_{t in [t0, t1)} PA_t PB_t^T restricted to wave
-// (a, b)'s block, PA_t = panelA(t) and PB_t = panelB(t); `same` reuses the A
-// panel for B; a wave with `active` false stages but skips its products.
-// Ends with a barrier.
-template <typename FA, typename FB>
-__device__ __forceinline__ void panel_gemm(doublex4 (&acc)[4][4], double* S, int t0, int t1, FA panelA, FB panelB,
-                                           bool neg, bool same, int a, int b, bool active) {
-    if (t0 >= t1) return;
-    double* A0 = S;
-    double* A1 = S + QB;
-    double* B0 = same ? A0 : S + 2 * QB;
-    double* B1 = same ? A1 : S + 3 * QB;
-    const int H = 4 * (t1 - t0);   // quarters, even
-    double ra0[QPER], rb0[QPER], ra1[QPER], rb1[QPER];
-    // quarter h of the run: step t0 + h / 4, k-quarter h % 4
-    fetch_quarter(ra0, panelA(t0), 0);
-    if (!same) fetch_quarter(rb0, panelB(t0), 0);
-    fetch_quarter(ra1, panelA(t0), 1);
-    if (!same) fetch_quarter(rb1, panelB(t0), 1);
-    __syncthreads();   // earlier users of S are done
-    put_quarter(A0, ra0, panelA(t0));
-    if (!same) put_quarter(B0, rb0, panelB(t0));
-    __syncthreads();
-#pragma unroll 1   // unrolled, the phases' loads overlap and the registers do not suffice
-    for (int h = 0; h < H; h += 2) {
-        const int t1q = t0 + ((h + 1) >> 2), t2 = t0 + ((h + 2) >> 2), t3 = t0 + ((h + 3) >> 2);
-        // quarter h + 1 into buffer 1; quarter h + 2 in flight
-        put_quarter(A1, ra1, panelA(t1q));
-        if (!same) put_quarter(B1, rb1, panelB(t1q));
-        if (h + 2 < H) {
-            fetch_quarter(ra0, panelA(t2), (h + 2) & 3);
-            if (!same) fetch_quarter(rb0, panelB(t2), (h + 2) & 3);
-        }
-        if (active) mma_quarter(acc, A0, B0, a, b, neg);
-        __syncthreads();
-        // quarter h + 2 into buffer 0; quarter h + 3 in flight
-        if (h + 2 < H) {
-            put_quarter(A0, ra0, panelA(t2));
-            if (!same) put_quarter(B0, rb0, panelB(t2));
-            fetch_quarter(ra1, panelA(t3), (h + 3) & 3);
-            if (!same) fetch_quarter(rb1, panelB(t3), (h + 3) & 3);
-        }
-        if (active) mma_quarter(acc, A1, B1, a, b, neg);
-        __syncthreads();
-    }
-}
-
-// 16 x 16 block (i, j) of a wave's 64 x 64 block: lane l holds column
-// 16 j + l % 16 and rows 16 i + l / 16 + 4 r.
-template <typename F>
-__device__ __forceinline__ void for_acc4(F&& f) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) f(i, j, r, 16 * i + (lane >> 4) + 4 * r, 16 * j + (lane & 15));
 }
 
 // Output layout of a 16 x 16 f64 MFMA block (checked on gfx950): lane l holds
@@ -1056,77 +904,6 @@ __global__ __launch_bounds__(NT, 4) void inv_lauum_kernel(InvLaunch L, int64_t t
     }
 }
 
-// Z = V V^T on 2 x 2 groups of blocks: group (I2, J2), I2 <= J2, holds the
-// blocks (2 I2 + a, 2 J2 + b); wave (a, b) owns one, summing over t >= 2 J2.
-// Blocks of V below the diagonal are zero (their storage holds trtri's
-// parked products) and are staged as zeros; in a diagonal group the wave of
-// the block below the diagonal computes nothing (its block is the mirror).
-// float32 out, both triangles, mirrored through LDS.
-__global__ __launch_bounds__(NT, 2) void inv_lauum2_kernel(InvLaunch L, int64_t tiles) {
-    __shared__ double S[STAGE2];
-    static_assert(STAGE2 * 2 >= 4 * B * (B + 1), "the four blocks are mirrored through the staging area");
-    int mi;
-    int64_t local;
-    const int64_t item = xcd_runs<kRun>(blockIdx.x);
-    if (item >= tiles || !locate(L, kInvLauum2, item, mi, local)) return;
-    const InvMat M = L.mats[mi];
-    int I2, J2;
-    column_decode(local, I2, J2);
-    const int nb = M.nb;
-    const int64_t D = (int64_t)nb * B, d = M.d, n = M.n;
-    const int w = threadIdx.x >> 6, a = w >> 1, b = w & 1;
-    const int I = 2 * I2 + a, J = 2 * J2 + b;
-    const bool active = I < nb && J < nb && !(I2 == J2 && a > b);
-    auto V = [&](int row, int t) {
-        if (row >= nb || t < row) return Blk{M.w, D, false};
-        if (L.vlow) return v_low(M, D, row, t);
-        return t == row ? Blk{M.dinv + (int64_t)row * BB, B, false}
-                        : Blk{M.w + (int64_t)row * B * D + (int64_t)t * B, D, false};
-    };
-    auto panel = [&](int r0, int t) {
-        return Panel{{V(r0, t), V(r0 + 1, t)}, {r0 >= nb || t < r0, r0 + 1 >= nb || t < r0 + 1}};
-    };
-    // the border column of V at the rows of block rows 2 I2, 2 I2 + 1
-    // (vb[0, 128)) and 2 J2, 2 J2 + 1 (vb[128, 256)), visible after the first
-    // barrier of the panel product
-    const bool bord = n < d;
-    __shared__ double vb[4 * B];
-    if (bord) {
-        const int64_t row = (threadIdx.x < 2 * B ? 2 * I2 * B : 2 * J2 * B - 2 * B) + threadIdx.x;
-        vb[threadIdx.x] = row < n ? as_global(M.bvec)[row] : 0.0;
-    }
-    doublex4 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = doublex4{0.0, 0.0, 0.0, 0.0};
-    panel_gemm(acc, S, 2 * J2, nb, [&](int t) { return panel(2 * I2, t); }, [&](int t) { return panel(2 * J2, t); },
-               false, I2 == J2, a, b, active);
-    // each wave's block as float32 in LDS, then written with coalesced rows
-    float* F = reinterpret_cast<float*>(S) + w * B * (B + 1);
-    for_acc4([&](int i, int j, int r, int row, int col) {
-        double v = acc[i][j][r];
-        if (bord) v += vb[a * B + row] * vb[2 * B + b * B + col];
-        F[row * (B + 1) + col] = (float)v;
-    });
-    __syncthreads();
-    if (!active) return;
-    const int64_t r0 = (int64_t)I * B, c0 = (int64_t)J * B;
-    const int l = threadIdx.x & 63;
-    for (int r = 0; r < B; ++r) {
-        const int c = l;
-        const int64_t i = r0 + r, j = c0 + c;
-        if (i < n && j < n) as_global(M.z)[i * d + j] = (I != J || c >= r) ? F[r * (B + 1) + c] : F[c * (B + 1) + r];
-    }
-    if (I != J) {
-        for (int c = 0; c < B; ++c) {
-            const int r = l;   // destination row c0 + c, column r0 + r
-            const int64_t i = c0 + c, j = r0 + r;
-            if (i < n && j < n) as_global(M.z)[i * d + j] = F[r * (B + 1) + c];
-        }
-    }
-}
-
 // Block (row, t) of V = U^-1 in whichever place it is kept: above the
 // diagonal, or in block (t, row) below it when formed beside potrf; the
 // diagonal blocks in dinv.
@@ -1291,7 +1068,6 @@ hipError_t launch_inv_step(const InvLaunch& L, int64_t t, hipStream_t s) { retur
 hipError_t launch_inv_trtri_a(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_trtri_a_kernel, L, t, s, true); }
 hipError_t launch_inv_trtri_b(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_trtri_b_kernel, L, t, s, true); }
 hipError_t launch_inv_lauum(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_lauum_kernel, L, t, s, true); }
-hipError_t launch_inv_lauum2(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_lauum2_kernel, L, t, s, true); }
 hipError_t launch_inv_border_w(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_border_w_kernel, L, t, s); }
 hipError_t launch_inv_border_u(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_border_u_kernel, L, t, s); }
 hipError_t launch_inv_border_v(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_border_v_kernel, L, t, s); }

@@ -402,8 +402,6 @@ kfac_status_t kfac_pack_sym(int n, float* const* m, const int64_t* d, float* pac
 
 // ---------------------------------------------------------------- inverse --
 
-constexpr int64_t kLauum2MinTiles = 1024;
-
 size_t kfac_inverse_workspace_size(int n, const int64_t* d) {
     if (!valid_dims(n, d)) return 0;
     return inverse_ws(n, d);
@@ -493,11 +491,7 @@ kfac_status_t kfac_damped_inverse(int n, const float* const* x, const int64_t* d
     }
     if (e == hipSuccess) {
         L.step = 0;
-        // 2 x 2 groups of blocks when there are enough of them to fill the
-        // chip a few times over, single blocks otherwise
-        const int64_t t2 = bucket_tiles(p, kInvLauum2, 0);
-        e = t2 >= kLauum2MinTiles ? launch_inv_lauum2(L, t2, stream)
-                                  : launch_inv_lauum(L, bucket_tiles(p, kInvLauum, 0), stream);
+        e = launch_inv_lauum(L, bucket_tiles(p, kInvLauum, 0), stream);
     }
     return hip_status(e);
 }
