@@ -175,13 +175,14 @@ __device__ __forceinline__ TileWork decode_item(const GemmLaunch& L, int64_t ite
 // one from the reads of the other.
 constexpr int SLAB = BK * BM;                 // floats per staged slab
 constexpr int kSlabCopies = SLAB / (4 * NT);  // copy instructions per wave and slab (4)
+static_assert(kSlabCopies * 4 * NT == SLAB && BM % 4 == 0, "a slab is a whole number of 16-byte copies per lane");
 
 __device__ __forceinline__ void stage_slab(float* S, __amdgpu_buffer_rsrc_t r, const uint32_t (&off)[kSlabCopies]) {
     const int w = threadIdx.x >> 6;
 #pragma unroll
     for (int s = 0; s < kSlabCopies; ++s)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(S + 256 * (4 * w + s)), 16,
-                                                 off[s], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            r, (__attribute__((address_space(3))) void*)(S + 256 * (kSlabCopies * w + s)), 16, off[s], 0, 0, 0);
 }
 
 // acc += one staged slab: lane l supplies row/column (l % 32) of its
@@ -220,7 +221,7 @@ __device__ __forceinline__ void gemm_f32_tile(const GemmLaunch& L, const TileWor
     uint32_t offa[kSlabCopies], offb[kSlabCopies];
 #pragma unroll
     for (int s = 0; s < kSlabCopies; ++s) {
-        const int chunk = (4 * wave + s) * 64 + lane;
+        const int chunk = (kSlabCopies * wave + s) * 64 + lane;
         const int k = chunk >> 5, m = 4 * (chunk & 31);
         offa[s] = (W.m0 + m < P.M) ? (uint32_t)((k * P.lda + W.m0 + m) * 4) : kOOB;
         offb[s] = (W.n0 + m < P.N) ? (uint32_t)((k * P.ldb + W.n0 + m) * 4) : kOOB;
