@@ -17,9 +17,10 @@
 // rows past the end of the input read as zero without a branch, and the
 // per-thread offsets inside a slab are computed once.  float32 slabs go
 // from memory straight into LDS as [k][m] rows (v_mfma_f32_32x32x2f32 takes
-// one k-value per lane); bfloat16 slabs pass through registers and are
-// stored as [m][k], because v_mfma_f32_32x32x16_bf16 takes 8 consecutive
-// k-values per lane, read as one 16-byte LDS access.
+// one k-value per lane).  bfloat16 slabs of 4-byte aligned rows do the same
+// and are read back with transposing LDS reads, since
+// v_mfma_f32_32x32x16_bf16 takes 8 consecutive k-values per lane; rows of
+// odd width pass through registers and are stored as [m][k].
 #include "device_common.h"
 #include "internal.h"
 
@@ -291,8 +292,9 @@ __global__ __launch_bounds__(NT, 2) void gemm_tn_kernel(GemmLaunch L, int64_t it
 // bfloat16 inputs on v_mfma_f32_32x32x16_bf16 (products exact in float32,
 // float32 accumulation).  Slabs of 32 rows are staged as [m][k] bf16 with k
 // contiguous; a lane's eight k-values of a block are one 16-byte LDS read,
-// and each slab feeds 2 x 4 MFMAs per wave.  Elements are loaded one at a
-// time because rows of odd width are not 4-byte aligned.
+// and each slab feeds 2 x 4 MFMAs per wave.  This path loads elements one
+// at a time and serves rows that are not 4-byte aligned (odd width), which
+// the 16-byte copies into LDS cannot read.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 constexpr int BK16 = 32;
 constexpr int LDK16 = BK16 + 8;    // LDS row stride in bf16 (80 bytes)
@@ -305,13 +307,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc16(const void* base, 
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p), (short)0, bytes, 0x00020000);
 }
 
-__global__ __launch_bounds__(NT, 2) void gemm_tn_bf16_kernel(GemmLaunch L, int64_t items) {
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDK16];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BM * LDK16];
-
-    const int64_t item = L.runs ? xcd_runs<kGemmRun>(blockIdx.x) : xcd_remap(blockIdx.x, gridDim.x);
-    if (item >= items) return;
-    const TileWork W = decode_item(L, item);
+__device__ __forceinline__ void gemm_bf16_reg_tile(const GemmLaunch& L, const TileWork& W,
+                                                   uint16_t (&As)[2][BM * LDK16], uint16_t (&Bs)[2][BM * LDK16]) {
     const GemmProb& P = W.P;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -411,6 +408,145 @@ __global__ __launch_bounds__(NT, 2) void gemm_tn_bf16_kernel(GemmLaunch L, int64
         __syncthreads();
     }
     store_tile(P, L, sum, W.kc, W.t, W.m0, W.n0, wm, wn, lane);
+}
+
+// bfloat16 slabs are copied straight into LDS as [k][m] (16 bytes, 8
+// columns, per lane).  The matrix cores take 8 consecutive k-values per
+// lane; two transposing LDS reads (ds_read_b64_tr_b16) assemble them: in a
+// group of 16 lanes, lane p points at k-row k0 + p/4, columns mb + 4 (p % 4),
+// and lane i receives column mb + i of rows k0 .. k0 + 3.  The 16-byte chunks
+// of row k sit at position c xor 2 (k % 4), so the 8 chunks a group reads
+// fall on distinct banks.
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef short short8v __attribute__((ext_vector_type(8)));
+constexpr int SLAB16 = BK16 * BM;                  // bf16 per staged slab (8 KB)
+constexpr int kSlab16Copies = SLAB16 / (8 * NT);   // copy instructions per wave and slab (2)
+static_assert(kSlab16Copies * 8 * NT == SLAB16, "a slab is a whole number of 16-byte copies per lane");
+
+__device__ __forceinline__ int tr_at(int k, int m) {
+    return k * BM + ((((m >> 3) ^ (2 * (k & 3))) << 3) | (m & 7));
+}
+
+__device__ __forceinline__ void stage_slab16(uint16_t* S, __amdgpu_buffer_rsrc_t r,
+                                             const uint32_t (&off)[kSlab16Copies]) {
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int s = 0; s < kSlab16Copies; ++s)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            r, (__attribute__((address_space(3))) void*)(S + 512 * (kSlab16Copies * w + s)), 16, off[s], 0, 0, 0);
+}
+
+// 8 consecutive k-values (k0 .. k0 + 7 of the lane's group) of column mb + (lane % 16)
+__device__ __forceinline__ bf16x8 tr_frag(const uint16_t* S, int k0, int mb, int p) {
+    const int m = mb + 4 * (p & 3);
+    const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) short4v*)(S + tr_at(k0 + (p >> 2), m)));
+    const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) short4v*)(S + tr_at(k0 + 4 + (p >> 2), m)));
+    const short8v v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ void mma_slab16(floatx16 (&acc)[2][2], const uint16_t* A, const uint16_t* Bm, int wm,
+                                           int wn, int lane) {
+    const int g = lane >> 4, p = lane & 15;
+#pragma unroll
+    for (int s = 0; s < BK16 / 16; ++s) {
+        const int k0 = 16 * s + 8 * (g >> 1);
+        bf16x8 fa[2], fb[2];
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+            fa[a] = tr_frag(A, k0, wm * 64 + a * 32 + 16 * (g & 1), p);
+            fb[a] = tr_frag(Bm, k0, wn * 64 + a * 32 + 16 * (g & 1), p);
+        }
+        acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0], fb[0], acc[0][0], 0, 0, 0);
+        acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0], fb[1], acc[0][1], 0, 0, 0);
+        acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1], fb[0], acc[1][0], 0, 0, 0);
+        acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1], fb[1], acc[1][1], 0, 0, 0);
+    }
+}
+
+template <bool SAME>
+__device__ __forceinline__ void gemm_bf16_lds_tile(const GemmLaunch& L, const TileWork& W, uint16_t* A0, uint16_t* A1,
+                                               uint16_t* B0, uint16_t* B1) {
+    const GemmProb& P = W.P;
+    const int k_begin = W.k_begin, k_end = W.k_end;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const bool active = W.active;
+    uint16_t* const Bb0 = SAME ? A0 : B0;
+    uint16_t* const Bb1 = SAME ? A1 : B1;
+    uint32_t offa[kSlab16Copies], offb[kSlab16Copies];
+#pragma unroll
+    for (int s = 0; s < kSlab16Copies; ++s) {
+        const int q = (kSlab16Copies * wave + s) * 64 + lane;
+        const int k = q >> 4, c = (q & 15) ^ (2 * (k & 3)), m = 8 * c;   // this copy's row and columns
+        offa[s] = (W.m0 + m < P.M) ? (uint32_t)((k * P.lda + W.m0 + m) * 2) : kOOB;
+        offb[s] = (W.n0 + m < P.N) ? (uint32_t)((k * P.ldb + W.n0 + m) * 2) : kOOB;
+    }
+    auto stage = [&](uint16_t* SA, uint16_t* SB, int k0) {
+        stage_slab16(SA, slab_rsrc(P.a, P.lda, k0, k_end, 2, P.M), offa);
+        if (!SAME) stage_slab16(SB, slab_rsrc(P.b, P.ldb, k0, k_end, 2, P.N), offb);
+    };
+    floatx16 acc[2][2], sum[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) { acc[a][b][r] = 0.0f; sum[a][b][r] = 0.0f; }
+    constexpr int SUB16 = kGemmSubK / BK16;
+    auto fold = [&](int st, int nstages) {
+        if ((st + 1) % SUB16 == 0 || st + 1 == nstages) {
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    sum[a][b] += acc[a][b];
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+                }
+        }
+    };
+    const int nstages = (k_end - k_begin + BK16 - 1) / BK16;
+    if (nstages > 0) stage(A0, B0, k_begin);
+    for (int st = 0; st < nstages; st += 2) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (st + 1 < nstages) stage(A1, B1, k_begin + (st + 1) * BK16);
+        if (active) {
+            mma_slab16(acc, A0, Bb0, wm, wn, lane);
+            fold(st, nstages);
+        }
+        if (st + 1 >= nstages) break;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (st + 2 < nstages) stage(A0, B0, k_begin + (st + 2) * BK16);
+        if (active) {
+            mma_slab16(acc, A1, Bb1, wm, wn, lane);
+            fold(st + 1, nstages);
+        }
+    }
+    store_tile(P, L, sum, W.kc, W.t, W.m0, W.n0, wm, wn, lane);
+}
+
+// Rows whose starts are all 4-byte aligned (an even row pitch and an
+// aligned base) take the copy path; others are loaded element by element.
+__global__ __launch_bounds__(NT, 2) void gemm_tn_bf16_kernel(GemmLaunch L, int64_t items) {
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDK16];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BM * LDK16];
+    __shared__ __attribute__((aligned(16))) uint16_t A0[SLAB16];
+    __shared__ __attribute__((aligned(16))) uint16_t A1[SLAB16];
+    __shared__ __attribute__((aligned(16))) uint16_t B0[SLAB16];
+    __shared__ __attribute__((aligned(16))) uint16_t B1[SLAB16];
+    const int64_t item = L.runs ? xcd_runs<kGemmRun>(blockIdx.x) : xcd_remap(blockIdx.x, gridDim.x);
+    if (item >= items) return;
+    const TileWork W = decode_item(L, item);
+    const GemmProb& P = W.P;
+    const bool copy = ((P.lda | P.ldb) & 1) == 0 && (((uintptr_t)P.a | (uintptr_t)P.b) & 3) == 0;
+    if (!copy) gemm_bf16_reg_tile(L, W, As, Bs);
+    else if (W.same) gemm_bf16_lds_tile<true>(L, W, A0, A1, B0, B1);
+    else gemm_bf16_lds_tile<false>(L, W, A0, A1, B0, B1);
 }
 
 // Sums the split-K partial tiles in chunk order and applies the epilogue.

@@ -84,6 +84,43 @@ def test_factors_bf16_small():
         assert err <= TOL_BF16
 
 
+def test_factors_bf16_row_alignment():
+    """bfloat16 rows that start 4-byte aligned (even width, aligned base) are
+    copied into LDS whole; rows of odd width, or an input whose base sits one
+    element past an aligned address, are read element by element.  One call
+    mixes both kinds (widths that are even but not a multiple of 8, an odd
+    one, a tall split-K one), two running-average steps, and the same data
+    at both alignments gives results within rounding of each other."""
+    import torch
+    from workloads import f32_to_bf16_bits
+    say("factors bf16 row alignment")
+    rng = np.random.default_rng(6)
+    shapes = [(300, 70), (257, 33), (1000, 1026), (90000, 130), (513, 128)]
+    ms = [nan_f32(d, d) for _, d in shapes]
+    ref = [None] * len(shapes)
+    for step in range(2):
+        hs = [f32_to_bf16_bits(0.05 * rng.standard_normal((r, d)).astype(np.float32)) for r, d in shapes]
+        xs = [to_dev(h) for h in hs]
+        # the last input: same values, base one element past an aligned address
+        r, d = shapes[-1]
+        flat = torch.empty(r * d + 8, dtype=torch.bfloat16, device=xs[-1].device)
+        shifted = flat[1:1 + r * d].view(r, d)
+        shifted.copy_(xs[-1])
+        assert shifted.data_ptr() % 4 == 2
+        m_shift = nan_f32(d, d)
+        gpu_factors(xs, ms, EPS, step == 0)
+        gpu_factors([shifted], [m_shift], EPS, True)
+        for k, h in enumerate(hs):
+            ref[k] = oracle.running_average(ref[k], oracle.factor(oracle.upcast(h, "bf16")), np.float32(EPS), step == 0)
+            err = upper_rel_fro(to_host(ms[k]), ref[k])
+            say("  bf16 err", shapes[k], step, err)
+            assert err <= TOL_BF16, (shapes[k], step, err)
+        one = oracle.factor(oracle.upcast(hs[-1], "bf16"))
+        assert upper_rel_fro(to_host(m_shift), one) <= TOL_BF16
+        if step == 0:
+            assert upper_rel_fro(to_host(m_shift), to_host(ms[-1]).astype(np.float64)) <= 1e-6
+
+
 def run_config_factors(cid, steps=None):
     """A factors then G factors of every layer, as one call each, for the
     given steps of the workload's schedule; full comparison with the oracle."""
