@@ -189,6 +189,9 @@ __device__ __forceinline__ void stage_slab(float* S, __amdgpu_buffer_rsrc_t r, c
 // acc += one staged slab: lane l supplies row/column (l % 32) of its
 // 32-wide blocks and, at step s, the slab row 16 (l / 32) + s (the sum over
 // the slab does not depend on how its rows are paired).
+// NA x NB of the wave's 32 x 32 blocks (the others lie wholly past the
+// last row or column of the problem and are left at zero)
+template <int NA, int NB>
 __device__ __forceinline__ void mma_slab(floatx16 (&acc)[2][2], const float* A, const float* Bm, int wm, int wn,
                                          int lane) {
     const int fr = lane & 31, fk = (lane >> 5) * KPL;
@@ -196,13 +199,22 @@ __device__ __forceinline__ void mma_slab(floatx16 (&acc)[2][2], const float* A, 
     const float* pb = Bm + fk * BM + wn * 64 + fr;
 #pragma unroll
     for (int s = 0; s < KPL; ++s) {
-        const float a0 = pa[s * BM], a1 = pa[s * BM + 32];
-        const float b0 = pb[s * BM], b1 = pb[s * BM + 32];
+        const float a0 = pa[s * BM], a1 = NA > 1 ? pa[s * BM + 32] : 0.0f;
+        const float b0 = pb[s * BM], b1 = NB > 1 ? pb[s * BM + 32] : 0.0f;
         acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
-        acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
-        acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
-        acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
+        if (NB > 1) acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
+        if (NA > 1) acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
+        if (NA > 1 && NB > 1) acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
     }
+}
+
+// full == both blocks in each direction hold rows / columns of the problem
+__device__ __forceinline__ void mma_slab_edge(floatx16 (&acc)[2][2], const float* A, const float* Bm, int wm,
+                                              int wn, int lane, bool full, bool a2, bool b2) {
+    if (full) mma_slab<2, 2>(acc, A, Bm, wm, wn, lane);
+    else if (a2) mma_slab<2, 1>(acc, A, Bm, wm, wn, lane);
+    else if (b2) mma_slab<1, 2>(acc, A, Bm, wm, wn, lane);
+    else mma_slab<1, 1>(acc, A, Bm, wm, wn, lane);
 }
 
 // One tile; SAME (a factor tile on the diagonal) stages only A and reads
@@ -214,7 +226,11 @@ __device__ __forceinline__ void gemm_f32_tile(const GemmLaunch& L, const TileWor
     const int k_begin = W.k_begin, k_end = W.k_end;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const bool active = W.active;
+    // a wave whose 64 rows or columns all lie past the problem's edge has
+    // nothing to compute; one whose second 32 do skips those blocks
+    const int wr = W.m0 + 64 * wm, wc = W.n0 + 64 * wn;
+    const bool active = W.active && wr < P.M && wc < P.N;
+    const bool a2 = wr + 32 < P.M, b2 = wc + 32 < P.N, full = a2 && b2;
     float* const Bb0 = SAME ? A0 : B0;
     float* const Bb1 = SAME ? A1 : B1;
 
@@ -261,7 +277,7 @@ __device__ __forceinline__ void gemm_f32_tile(const GemmLaunch& L, const TileWor
         __syncthreads();
         if (st + 1 < nstages) stage(A1, B1, k_begin + (st + 1) * BK);
         if (active) {
-            mma_slab(acc, A0, Bb0, wm, wn, lane);
+            mma_slab_edge(acc, A0, Bb0, wm, wn, lane, full, a2, b2);
             fold(st, nstages);
         }
         if (st + 1 >= nstages) break;
@@ -269,7 +285,7 @@ __device__ __forceinline__ void gemm_f32_tile(const GemmLaunch& L, const TileWor
         __syncthreads();
         if (st + 2 < nstages) stage(A0, B0, k_begin + (st + 2) * BK);
         if (active) {
-            mma_slab(acc, A1, Bb1, wm, wn, lane);
+            mma_slab_edge(acc, A1, Bb1, wm, wn, lane, full, a2, b2);
             fold(st + 1, nstages);
         }
     }
