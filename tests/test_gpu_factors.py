@@ -121,6 +121,31 @@ def test_factors_bf16_row_alignment():
             assert upper_rel_fro(to_host(m_shift), to_host(ms[-1]).astype(np.float64)) <= 1e-6
 
 
+@pytest.mark.parametrize("dtype,rows,d", [
+    ("bf16", 97, 1025), ("bf16", 33, 65), ("bf16", 1000, 33), ("bf16", 65, 4097),
+    ("bf16", 97, 130), ("f32", 97, 1025), ("f32", 1000, 33),
+])
+def test_factors_slab_and_matrix_ends(dtype, rows, d):
+    """Only the last two columns are nonzero, in the last row of every 32-row
+    slab and in the matrix's last row: the elements read at the end of each
+    slab's address range and at the very end of the input.  The factor is a
+    handful of exact sums, so any element lost at a range end shows."""
+    from workloads import f32_to_bf16_bits
+    say("factors slab ends", dtype, rows, d)
+    x = np.zeros((rows, d), dtype=np.float32)
+    ends = sorted(set(list(range(31, rows, 32)) + [rows - 1]))
+    x[ends, d - 1] = 1.0
+    if d > 1:
+        x[ends, d - 2] = 2.0
+    h = f32_to_bf16_bits(x) if dtype == "bf16" else x
+    m = nan_f32(d, d)
+    gpu_factors([h], [m], EPS, True)
+    ref = oracle.factor(oracle.upcast(h, "bf16") if dtype == "bf16" else oracle.upcast(h))
+    got = to_host(m).astype(np.float64)
+    assert got[d - 1, d - 1] == pytest.approx(len(ends) / rows, rel=1e-6)
+    assert upper_rel_fro(got, ref) <= 1e-6
+
+
 def run_config_factors(cid, steps=None):
     """A factors then G factors of every layer, as one call each, for the
     given steps of the workload's schedule; full comparison with the oracle."""
