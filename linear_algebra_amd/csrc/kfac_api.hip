@@ -105,7 +105,8 @@ size_t factors_ws(const FactorPlan& p, int n) {
 // Two launches of plain products per call: S^T = grad^T ginv, then
 // P = (S^T)^T ainv.  When a launch has too few 128 x 128 tiles to give every
 // CU several, K is split into equal chunks (partials summed in chunk order
-// by the reduce kernel) so the last round of tiles is not left half empty.
+// by the reduce kernel) so the last round of tiles is not left half empty;
+// a cost estimate chooses between two split targets.
 struct PrecondPlan {
     std::vector<GemmProb> p1, p2;
     int64_t items1 = 0, items2 = 0, red1 = 0, red2 = 0;
@@ -114,22 +115,52 @@ struct PrecondPlan {
 
 constexpr int64_t kGemmSlots = 512;   // 256 CUs x 2 resident 128 x 128 tiles
 
-void plan_plain_launch(std::vector<GemmProb>& probs, int64_t& items, int64_t& red, int64_t& part_elems) {
+// Chunk length for a split-K target of `per_slot` tiles per slot (0: no split).
+int64_t plain_chunk(const std::vector<GemmProb>& probs, int per_slot) {
     int64_t tiles = 0;
     double work = 0.0;
+    for (const GemmProb& g : probs) {
+        tiles += g.ntiles;
+        work += (double)g.ntiles * g.K;
+    }
+    if (tiles >= per_slot * kGemmSlots) return 0;
+    return std::max<int64_t>(256, align_up((int64_t)std::ceil(work / ((double)per_slot * kGemmSlots)), 256));
+}
+
+// Estimated time of a launch in units of one 128 x 128 tile-row of products:
+// the work spread over the slots, half the longest item for the last round,
+// a fixed cost per item, and the split-K partials written and read back.
+// Tiles with at most 32 valid rows or columns cost about a quarter.
+double plain_cost(const std::vector<GemmProb>& probs, int64_t kc) {
+    double total = 0.0, longest = 0.0, part_bytes = 0.0;
+    for (const GemmProb& g : probs) {
+        const int64_t ks = kc == 0 ? 1 : std::max<int64_t>(1, ceil_div(g.K, kc));
+        const double rows = (double)align_up(ceil_div(g.K, ks), kGemmBK);
+        int64_t thin = 0;
+        if (g.M - (int64_t)kGemmTile * (g.tiles_m - 1) <= 32) thin += g.tiles_n;
+        if (g.N - (int64_t)kGemmTile * (g.tiles_n - 1) <= 32) thin += g.tiles_m;
+        thin = std::min<int64_t>(thin, g.ntiles);
+        const double full = rows + 40.0, cheap = 0.25 * rows + 40.0;
+        total += (double)ks * ((double)(g.ntiles - thin) * full + (double)thin * cheap);
+        longest = std::max(longest, g.ntiles > thin ? full : cheap);
+        if (ks > 1) part_bytes += 2.0 * (double)g.ntiles * ks * kGemmTile * kGemmTile * sizeof(float);
+    }
+    return total / kGemmSlots + 0.5 * longest + part_bytes / 6.4e5;
+}
+
+void plan_plain_launch(std::vector<GemmProb>& probs, int64_t& items, int64_t& red, int64_t& part_elems) {
     for (GemmProb& g : probs) {
         g.tiles_m = (int32_t)ceil_div(g.M, kGemmTile);
         g.tiles_n = (int32_t)ceil_div(g.N, kGemmTile);
         g.ntiles = g.tiles_m * g.tiles_n;
-        tiles += g.ntiles;
-        work += (double)g.ntiles * g.K;
     }
-    // aim for at least four tiles per slot; chunks of at least 256 rows
-    int64_t kc = INT64_MAX;
-    if (tiles < 4 * kGemmSlots) kc = std::max<int64_t>(256, align_up((int64_t)std::ceil(work / (4.0 * kGemmSlots)), 256));
+    // split K for two or four tiles per slot (chunks of at least 256 rows),
+    // whichever the cost estimate prefers
+    const int64_t kc2 = plain_chunk(probs, 2), kc4 = plain_chunk(probs, 4);
+    const int64_t kc = plain_cost(probs, kc2) < plain_cost(probs, kc4) ? kc2 : kc4;
     items = red = part_elems = 0;
     for (GemmProb& g : probs) {
-        const int64_t ks = (kc == INT64_MAX) ? 1 : std::max<int64_t>(1, ceil_div(g.K, kc));
+        const int64_t ks = (kc == 0) ? 1 : std::max<int64_t>(1, ceil_div(g.K, kc));
         g.ksplit = (int32_t)ks;
         g.kchunk = (int32_t)align_up(ceil_div(g.K, ks), kGemmBK);
         g.mode = kModePlain;
