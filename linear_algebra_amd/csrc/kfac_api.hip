@@ -62,7 +62,7 @@ FactorPlan plan_factors(int n, const int64_t* rows, const int64_t* d) {
         const int64_t t = ceil_div(d[i], kGemmTile);
         work += (double)(t * (t + 1) / 2) * (double)rows[i];
     }
-    const double target_items = 4096.0;
+    const double target_items = 8192.0;   // 16 per slot
     int64_t kc = (int64_t)std::ceil(work / target_items);
     kc = std::max<int64_t>(kc, 1024);
     kc = align_up(kc, kGemmSubK);
