@@ -195,28 +195,35 @@ def test_factors_config4_bf16_full():
 
 
 def test_factors_config5_sampled():
-    """Large-factor workload: every layer in one call, checked on sampled
-    entries (and every diagonal) against the oracle's entry-wise sums."""
+    """Large-factor workload: the A factors and the G factors of every layer,
+    one call per side, checked on sampled entries and on every diagonal
+    entry against the oracle's entry-wise sums."""
     cfg = CONFIGS[5]
-    say("config 5 factors (16 large layers), sampled")
+    say("config 5 factors (16 large layers, A and G), sampled")
     data = gen_layer_step(cfg, 0, threads=16)
     L = cfg.layers
-    ma = [nan_f32(l.d_a, l.d_a) for l in L]
-    la.kfac_factors([to_dev(t[0]) for t in data], ma, EPS, True)
     rng = np.random.default_rng(55)
     worst = 0.0
-    for k in range(0, len(L), 3):
-        x = data[k][0]
-        d = x.shape[1]
-        got = to_host(ma[k])
-        ii = rng.integers(0, d, 24)
-        jj = rng.integers(0, d, 24)
-        ii, jj = np.minimum(ii, jj), np.maximum(ii, jj)
-        diag = oracle.factor_diagonal(x)
-        ref = oracle.factor_entries(x, ii, jj)
-        scale = np.sqrt(diag[ii] * diag[jj])
-        err = np.abs(got[ii, jj] - ref) / scale
-        derr = np.abs(np.diag(got) - diag) / diag
-        worst = max(worst, err.max(), derr.max())
-        assert err.max() <= TOL_F32 and derr.max() <= TOL_F32, (L[k].name, err.max(), derr.max())
+    for side in (0, 1):
+        dims = [l.d_a if side == 0 else l.d_g for l in L]
+        ms = [nan_f32(d, d) for d in dims]
+        la.kfac_factors([to_dev(t[side]) for t in data], ms, EPS, True)
+        for k in range(len(L)):
+            x = data[k][side]
+            d = x.shape[1]
+            got = to_host(ms[k])
+            ii = rng.integers(0, d, 24)
+            jj = rng.integers(0, d, 24)
+            ii, jj = np.minimum(ii, jj), np.maximum(ii, jj)
+            # the last row and column (a bias column of ones on the A side)
+            ii = np.concatenate([ii, [0, d - 1]])
+            jj = np.concatenate([jj, [d - 1, d - 1]])
+            diag = oracle.factor_diagonal(x)
+            ref = oracle.factor_entries(x, ii, jj)
+            scale = np.sqrt(diag[ii] * diag[jj])
+            err = np.abs(got[ii, jj] - ref) / scale
+            derr = np.abs(np.diag(got) - diag) / diag
+            worst = max(worst, err.max(), derr.max())
+            assert err.max() <= TOL_F32 and derr.max() <= TOL_F32, ("AG"[side], L[k].name, err.max(), derr.max())
+        del ms
     say(f"config 5: worst sampled relative error {worst:.3e}")

@@ -170,18 +170,35 @@ def test_inverse_bordered_nearly_dependent_last_row():
     np.testing.assert_array_equal(zs[0], zs[0].T)
 
 
+_FACTOR_CACHE = {}
+
+
 def config_factor_inputs(cid, rows_cap=None):
     """float32 factors (A's then G's) of a workload's first step, from the
-    oracle; rows_cap limits the rows drawn per layer (same recipe)."""
+    oracle; rows_cap limits the rows drawn per layer (same recipe).  Layers
+    are drawn and reduced in parallel threads (numpy releases the GIL), and
+    the result is kept for the other tests of this module."""
+    from concurrent.futures import ThreadPoolExecutor
+    key = (cid, rows_cap)
+    if key in _FACTOR_CACHE:
+        return _FACTOR_CACHE[key]
     cfg = CONFIGS[cid]
-    xs = []
-    for li, l in enumerate(cfg.layers):
-        r = l.rows if rows_cap is None else min(l.rows, rows_cap)
-        xs.append(factor_input(gen_a(cfg, 0, li, rows=r), cfg.in_dtype))
-    for li in reversed(range(cfg.n_layers)):
-        l = cfg.layers[li]
-        r = l.rows if rows_cap is None else min(l.rows, rows_cap)
-        xs.append(factor_input(gen_g(cfg, 0, li, rows=r), cfg.in_dtype))
+
+    def rows(l):
+        return l.rows if rows_cap is None else min(l.rows, rows_cap)
+
+    jobs = [(gen_a, li) for li in range(cfg.n_layers)] + [(gen_g, li) for li in reversed(range(cfg.n_layers))]
+
+    def one(j):
+        f = factor_input(j[0](cfg, 0, j[1], rows=rows(cfg.layers[j[1]])), cfg.in_dtype)
+        if f.shape[0] >= 1024:
+            say(f"  oracle factor: config {cid} layer {j[1]} {'A' if j[0] is gen_a else 'G'} ({f.shape[0]})")
+        return f
+
+    with ThreadPoolExecutor(max_workers=4) as ex:
+        xs = list(ex.map(one, jobs))
+    _FACTOR_CACHE.clear()
+    _FACTOR_CACHE[key] = xs
     return xs
 
 
@@ -196,6 +213,8 @@ def check_sampled(xs, zs, gamma, pick, ncols=6, seed=0):
         assert info == 0
         err = rel_fro(zs[k][:, cols].T, ref)
         worst = max(worst, err)
+        if d >= 1024:
+            say(f"  matrix {k} (order {d}): {len(cols)} oracle columns, rel err {err:.3e}")
         assert err <= TOL, (k, d, err)
     return worst
 
@@ -240,9 +259,10 @@ def bucket_representatives(xs):
 
 
 def test_inverse_config3_full_batch():
-    """All 108 ResNet-50 factors in one call; one matrix of every size bucket
-    checked against oracle columns, every output checked for symmetry."""
-    xs = config_factor_inputs(3, rows_cap=8192)
+    """All 108 ResNet-50 factors, at the workload's full row counts, in one
+    call; one matrix of every size bucket checked against oracle columns,
+    every output checked for symmetry."""
+    xs = config_factor_inputs(3)
     gamma = np.float32(1e-3)
     say("config 3 inverse: 108 matrices")
     zs, info = gpu_inverse(xs, gamma)
@@ -251,6 +271,51 @@ def test_inverse_config3_full_batch():
         np.testing.assert_array_equal(z, z.T)
     worst = check_sampled(xs, zs, gamma, bucket_representatives(xs))
     say(f"config 3 inverse: worst sampled rel err {worst:.3e}")
+
+
+def size_representatives(xs):
+    """The first and the last matrix of every distinct order."""
+    first, last = {}, {}
+    for k, x in enumerate(xs):
+        first.setdefault(x.shape[0], k)
+        last[x.shape[0]] = k
+    return sorted(set(first.values()) | set(last.values()))
+
+
+@pytest.mark.timeout(600)
+def test_inverse_config4_full_batch():
+    """The encoder's 96 factors (orders 1024, 1025, 3072, 4096, 4097; the
+    bf16 inputs upcast exactly) in one call, the configuration the benchmark
+    runs: the first and last matrix of every order against oracle columns,
+    every output checked for symmetry."""
+    xs = config_factor_inputs(4)
+    gamma = np.float32(1e-3)
+    say("config 4 inverse:", len(xs), "matrices, orders", sorted({x.shape[0] for x in xs}))
+    zs, info = gpu_inverse(xs, gamma)
+    assert np.all(info == 0), info
+    for z in zs:
+        np.testing.assert_array_equal(z, z.T)
+    worst = check_sampled(xs, zs, gamma, size_representatives(xs), ncols=6, seed=4)
+    say(f"config 4 inverse: worst sampled rel err {worst:.3e}")
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("gamma", [1e-2, 1e-4])
+def test_inverse_config5_full_batch(gamma):
+    """The large-factor workload's 32 factors at its full 25,088 rows, in one
+    call as the benchmark makes it (the bordered 2305 and 4609 with the
+    plain 512, 2048 and 4096 in one launch sequence): every matrix against
+    oracle columns, every output checked for symmetry.  gamma = 1e-4 is
+    held to the same bound."""
+    xs = config_factor_inputs(5)
+    gamma = np.float32(gamma)
+    say("config 5 inverse, full batch, gamma", float(gamma), [x.shape[0] for x in xs])
+    zs, info = gpu_inverse(xs, gamma)
+    assert np.all(info == 0), info
+    for z in zs:
+        np.testing.assert_array_equal(z, z.T)
+    worst = check_sampled(xs, zs, gamma, range(len(xs)), ncols=3, seed=int(1 / gamma))
+    say(f"config 5 inverse gamma={float(gamma)}: worst sampled rel err {worst:.3e}")
 
 
 @pytest.mark.parametrize("gamma", [1e-2, 1e-4])

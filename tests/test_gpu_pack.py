@@ -61,7 +61,7 @@ def test_pack_layer_boundaries_inside_vector():
     run_pack_case(dims, np.random.default_rng(11))
 
 
-@pytest.mark.parametrize("cid", [1, 2, 3, 5])
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
 def test_pack_unpack_full_config(cid):
     """All factors of a workload, at its real dimensions, in one call each way."""
     dims = CONFIGS[cid].factor_dims()
