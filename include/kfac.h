@@ -105,11 +105,23 @@ kfac_status_t kfac_factors(int n, const void* const* x, const int64_t* rows, con
  * (kfac_packed_size() float32 elements).  KFAC_UNPACK reads `packed` and
  * writes every element of m[l]: entry (i, j) and its mirror (j, i).  Values
  * are copied bit for bit.  The m[l] must not overlap each other or `packed`.
+ * The host passes only the pointers and orders; the offsets off_l are
+ * formed on the device, as a prefix sum across a wavefront.  The workspace
+ * (kfac_pack_workspace_size() bytes) holds that layer table.
  */
 int64_t kfac_packed_size(int n, const int64_t* d);
 size_t kfac_pack_workspace_size(int n, const int64_t* d);
 kfac_status_t kfac_pack_sym(int n, float* const* m, const int64_t* d, float* packed, kfac_pack_dir_t dir,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Plain device-to-device copy of `bytes` bytes (16-byte loads and stores,
+ * one per lane).  It computes nothing of the method: it is the measured
+ * streaming rate that the HBM-bound figures of pack and unpack are set
+ * against, beside the published peak.  src and dst are device pointers,
+ * 16-byte aligned, not overlapping; bytes is a multiple of 16 (0 is a no-op),
+ * else KFAC_ERR_INVALID_VALUE.
+ */
+kfac_status_t kfac_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------- inverse --
  * Tikhonov-damped inverse of each factor (paragraph on damping before

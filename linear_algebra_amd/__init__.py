@@ -25,7 +25,7 @@ KFAC_PACK, KFAC_UNPACK = 0, 1
 EXPORTS = (
     "kfac_abi_version", "kfac_status_string",
     "kfac_factors_workspace_size", "kfac_factors",
-    "kfac_packed_size", "kfac_pack_workspace_size", "kfac_pack_sym",
+    "kfac_packed_size", "kfac_pack_workspace_size", "kfac_pack_sym", "kfac_stream_copy",
     "kfac_inverse_workspace_size", "kfac_damped_inverse",
     "kfac_precondition_workspace_size", "kfac_precondition",
     "kfac_im2col_workspace_size", "kfac_im2col",
@@ -73,6 +73,7 @@ def load_library(path: str = LIB_PATH):
         "kfac_packed_size": (i64, [i32, vp]),
         "kfac_pack_workspace_size": (sz, [i32, vp]),
         "kfac_pack_sym": (i32, [i32, vp, vp, vp, i32, vp, sz, vp]),
+        "kfac_stream_copy": (i32, [vp, vp, sz, vp]),
         "kfac_inverse_workspace_size": (sz, [i32, vp]),
         "kfac_damped_inverse": (i32, [i32, vp, vp, f32, vp, vp, vp, sz, vp]),
         "kfac_precondition_workspace_size": (sz, [i32, vp, vp]),
@@ -114,6 +115,14 @@ def _stream(device, stream):
     import torch
     s = torch.cuda.current_stream(device) if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
+
+
+def _keep_for(ws, stream) -> None:
+    """The workspace comes from torch's allocator on the current stream; when
+    the kernels run on another stream, the block must not be handed out
+    again before that stream has passed them."""
+    if stream is not None:
+        ws.record_stream(stream)
 
 
 def _check(tensors, dtype, name):
@@ -174,6 +183,7 @@ def kfac_factors(xs: Sequence, ms: Sequence, eps: float, first_step: bool, strea
     ws = _workspace(ws_bytes, dev)
     _call(lib.kfac_factors(n, _ptrs(xs), r64, d64, dtype, _ptrs(ms), ctypes.c_float(eps), int(bool(first_step)),
                            ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(dev, stream)), "kfac_factors")
+    _keep_for(ws, stream)
 
 
 def kfac_packed_size(dims: Sequence[int]) -> int:
@@ -202,6 +212,18 @@ def kfac_pack_sym(ms: Sequence, packed, direction: int, stream=None) -> None:
     ws = _workspace(ws_bytes, dev)
     _call(lib.kfac_pack_sym(n, _ptrs(ms), d64, ctypes.c_void_p(packed.data_ptr()), int(direction),
                             ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(dev, stream)), "kfac_pack_sym")
+    _keep_for(ws, stream)
+
+
+def kfac_stream_copy(src, dst, stream=None) -> None:
+    """dst <- src, a plain device copy (the streaming reference of pack)."""
+    lib = load_library()
+    dev = _check([src, dst], None, "kfac_stream_copy")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("kfac_stream_copy: source and destination sizes differ")
+    _call(lib.kfac_stream_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), nbytes,
+                               _stream(dev, stream)), "kfac_stream_copy")
 
 
 def kfac_damped_inverse(xs: Sequence, gamma: float, xinvs: Sequence, info, stream=None) -> None:
@@ -225,6 +247,7 @@ def kfac_damped_inverse(xs: Sequence, gamma: float, xinvs: Sequence, info, strea
     _call(lib.kfac_damped_inverse(n, _ptrs(xs), d64, ctypes.c_float(gamma), _ptrs(xinvs),
                                   ctypes.c_void_p(info.data_ptr()), ctypes.c_void_p(ws.data_ptr()), ws.numel(),
                                   _stream(dev, stream)), "kfac_damped_inverse")
+    _keep_for(ws, stream)
 
 
 def kfac_precondition(ginvs: Sequence, grads: Sequence, ainvs: Sequence, outs: Sequence, stream=None) -> None:
@@ -247,11 +270,13 @@ def kfac_precondition(ginvs: Sequence, grads: Sequence, ainvs: Sequence, outs: S
     _call(lib.kfac_precondition(n, _ptrs(ginvs), _ptrs(grads), _ptrs(ainvs), g64, a64, _ptrs(outs),
                                 ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(dev, stream)),
           "kfac_precondition")
+    _keep_for(ws, stream)
 
 
 __all__ = [
     "load_library", "status_string", "KfacError", "KfacLibraryError",
-    "kfac_factors", "kfac_packed_size", "kfac_pack_sym", "kfac_damped_inverse", "kfac_precondition",
+    "kfac_factors", "kfac_packed_size", "kfac_pack_sym", "kfac_stream_copy", "kfac_damped_inverse",
+    "kfac_precondition",
     "KFAC_F32", "KFAC_BF16", "KFAC_PACK", "KFAC_UNPACK", "EXPORTS",
 ]
 
@@ -292,6 +317,7 @@ def kfac_im2col(xs: Sequence, shapes: Sequence[dict], outs: Sequence, stream=Non
     dtype = KFAC_BF16 if dt == torch.bfloat16 else KFAC_F32
     _call(lib.kfac_im2col(n, _ptrs(xs), ctypes.cast(arr, ctypes.c_void_p), dtype, _ptrs(outs),
                           ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(dev, stream)), "kfac_im2col")
+    _keep_for(ws, stream)
 
 
 def kfac_grad_rows(gys: Sequence, scale: float, outs: Sequence, stream=None) -> None:
@@ -320,6 +346,7 @@ def kfac_grad_rows(gys: Sequence, scale: float, outs: Sequence, stream=None) -> 
     dtype = KFAC_BF16 if dt == torch.bfloat16 else KFAC_F32
     _call(lib.kfac_grad_rows(n, _ptrs(gys), _i64(b), _i64(c), _i64(hw), dtype, ctypes.c_float(scale), _ptrs(outs),
                              ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream(dev, stream)), "kfac_grad_rows")
+    _keep_for(ws, stream)
 
 
 def kfac_grad_matrix(wgrads: Sequence, bgrads: Sequence, mats: Sequence, direction: int, stream=None) -> None:
@@ -346,3 +373,4 @@ def kfac_grad_matrix(wgrads: Sequence, bgrads: Sequence, mats: Sequence, directi
     _call(lib.kfac_grad_matrix(n, _ptrs(wgrads), ctypes.cast(bptr, ctypes.c_void_p), _i64(d_out), _i64(d_in),
                                _ptrs(mats), int(direction), ctypes.c_void_p(ws.data_ptr()), ws.numel(),
                                _stream(dev, stream)), "kfac_grad_matrix")
+    _keep_for(ws, stream)

@@ -115,18 +115,30 @@ hipError_t launch_grad_rows(const GradRowsLayer* layers, int n, int64_t tiles, b
 hipError_t launch_grad_matrix(const GradMatLayer* layers, int n, int64_t chunks, bool pack, hipStream_t stream);
 
 // ------------------------------------------------------------------- pack --
+// The host uploads (pointer, order) per factor; one wavefront on the device
+// turns them into the layer table, whose offsets are exclusive prefix sums of
+// d (d + 1) / 2 (packed elements) and of T (T + 1) / 2, T = ceil(d / 64)
+// (unpack tiles).
+struct PackSrc {
+    float* m;
+    int64_t d;
+};
 struct PackLayer {
     float* m;             // [d][d] matrix
     int64_t d;
     int64_t off;          // first packed element of this layer
-    int64_t tile_begin;   // first work unit of this layer (pack chunk or unpack tile)
+    int64_t tile_begin;   // first unpack tile of this layer
     int64_t tiles_1d;     // unpack tiles per edge
 };
-constexpr int kPackChunk = 4096;  // packed elements per pack workgroup
-hipError_t launch_pack(const PackLayer* layers_dev, int n, float* packed, int64_t blocks, hipStream_t stream);
-hipError_t launch_unpack(const PackLayer* layers_dev, int n, const float* packed, int64_t tiles,
-                         hipStream_t stream);
 constexpr int kUnpackTile = 64;
+constexpr int kPackThreads = 256;
+constexpr int kPackUnits = 2;    // 16-byte units per pack thread: 2048 packed elements per workgroup
+hipError_t launch_pack_table(const PackSrc* src, int n, PackLayer* out, hipStream_t stream);
+hipError_t launch_pack(const PackLayer* layers, int n, float* packed, int64_t total, hipStream_t stream);
+hipError_t launch_unpack(const PackLayer* layers, int n, const float* packed, int64_t tiles, hipStream_t stream);
+// Device copy of `bytes` (a multiple of 16, both pointers 16-byte aligned),
+// one 16-byte unit per lane: the streaming reference for the pack figures.
+hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
 
 // ---------------------------------------------------------------- inverse --
 // Every matrix is padded with the identity to D = NB * kInvNB and factored in

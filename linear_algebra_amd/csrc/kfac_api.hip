@@ -283,6 +283,7 @@ int64_t bucket_tiles(const InvPlan& p, int kind, int step) {
 
 size_t pack_ws(int n) {
     Carver c(nullptr);
+    c.take(sizeof(PackSrc) * n);
     c.take(sizeof(PackLayer) * n);
     return c.used;
 }
@@ -412,23 +413,34 @@ kfac_status_t kfac_pack_sym(int n, float* const* m, const int64_t* d, float* pac
     const size_t need = pack_ws(n);
     if (workspace == nullptr || !aligned(workspace, kAlign) || workspace_bytes < need) return KFAC_ERR_WORKSPACE;
 
-    // work units: pack chunks never cross a factor; unpack works on tiles
-    std::vector<PackLayer> layers(n);
-    int64_t off = 0, units = 0;
+    // the host keeps only the totals that size the grid; the per-layer
+    // offsets are prefix sums formed on the device
+    std::vector<PackSrc> src(n);
+    int64_t total = 0, tiles = 0;
     for (int i = 0; i < n; ++i) {
+        src[i] = PackSrc{m[i], d[i]};
         const int64_t t1 = ceil_div(d[i], kUnpackTile);
-        const int64_t elems = d[i] * (d[i] + 1) / 2;
-        layers[i] = PackLayer{m[i], d[i], off, units, t1};
-        off += elems;
-        units += (dir == KFAC_PACK) ? ceil_div(elems, kPackChunk) : t1 * (t1 + 1) / 2;
+        total += d[i] * (d[i] + 1) / 2;
+        tiles += t1 * (t1 + 1) / 2;
     }
     Carver c(workspace);
-    PackLayer* dev = static_cast<PackLayer*>(c.take(sizeof(PackLayer) * n));
-    hipError_t e = upload_table(dev, layers.data(), sizeof(PackLayer) * n, stream);
-    if (e != hipSuccess) return KFAC_ERR_HIP;
-    if (dir == KFAC_PACK) return hip_status(launch_pack(dev, n, packed, units, stream));
-    const int64_t tiles = units;
-    return hip_status(launch_unpack(dev, n, packed, tiles, stream));
+    PackSrc* src_dev = static_cast<PackSrc*>(c.take(sizeof(PackSrc) * n));
+    PackLayer* layers_dev = static_cast<PackLayer*>(c.take(sizeof(PackLayer) * n));
+    hipError_t e = upload_table(src_dev, src.data(), sizeof(PackSrc) * n, stream);
+    if (e == hipSuccess) e = launch_pack_table(src_dev, n, layers_dev, stream);
+    if (e == hipSuccess)
+        e = dir == KFAC_PACK ? launch_pack(layers_dev, n, packed, total, stream)
+                             : launch_unpack(layers_dev, n, packed, tiles, stream);
+    return hip_status(e);
+}
+
+kfac_status_t kfac_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t stream) {
+    if (bytes % 16 != 0) return KFAC_ERR_INVALID_VALUE;
+    if (bytes == 0) return KFAC_OK;
+    if (src == nullptr || dst == nullptr || !aligned(src, 16) || !aligned(dst, 16)) return KFAC_ERR_INVALID_VALUE;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+    if (a < b + bytes && b < a + bytes) return KFAC_ERR_INVALID_VALUE;
+    return hip_status(launch_stream_copy(src, dst, bytes, stream));
 }
 
 // ---------------------------------------------------------------- inverse --

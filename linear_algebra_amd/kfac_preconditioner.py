@@ -57,6 +57,7 @@ class KFACPreconditioner:
         self.steps = 0
         self.A = self.G = self.Ainv = self.Ginv = None
         self.info = None
+        self.failed: List[int] = []
 
     def _save_input(self, module, inputs):
         if module.training:
@@ -109,6 +110,32 @@ class KFACPreconditioner:
         kfac_grad_rows(gys, scale, gouts)
         return outs, gouts
 
+    def _update_inverses(self, first: bool) -> None:
+        """Damped inverses of every factor.  A factor whose Cholesky
+        factorisation fails (info != 0: a non-finite input, or gamma = 0 on a
+        singular factor) keeps its previous inverse and is listed in
+        ``self.failed``; with no previous inverse the step raises."""
+        import warnings
+
+        import torch
+        facs = self.A + self.G
+        new = [torch.empty_like(f) for f in facs]
+        kfac_damped_inverse(facs, self.damping, new, self.info)
+        info = self.info.cpu().tolist()
+        self.failed = [k for k, v in enumerate(info) if v != 0]
+        if self.failed and first:
+            raise RuntimeError(f"KFACPreconditioner: damped inverse failed (info {info}) with no previous inverse")
+        nl = len(self.layers)
+        for k, z in enumerate(new):
+            if info[k] == 0:
+                if k < nl:
+                    self.Ainv[k] = z
+                else:
+                    self.Ginv[k - nl] = z
+        if self.failed:
+            warnings.warn(f"KFACPreconditioner: damped inverse failed for factors {self.failed} "
+                          f"(info {[info[k] for k in self.failed]}); their previous inverses are kept")
+
     def step(self) -> None:
         """Precondition the gradients of every layer in place."""
         import torch
@@ -131,7 +158,7 @@ class KFACPreconditioner:
         kfac_factors(a, self.A, self.eps, first)
         kfac_factors(g, self.G, self.eps, first)
         if self.steps % self.inv_update_freq == 0:
-            kfac_damped_inverse(self.A + self.G, self.damping, self.Ainv + self.Ginv, self.info)
+            self._update_inverses(first)
         wg = [m.weight.grad for m in self.layers]
         bg = [m.bias.grad if m.bias is not None else None for m in self.layers]
         mats = [torch.empty(w.shape[0], w[0].numel() + (b is not None), device=dev) for w, b in zip(wg, bg)]

@@ -131,6 +131,16 @@ def test_pack_and_precondition_reject_bad_arguments(lib):
     assert lib.kfac_precondition(1, p, p, p, i64([4]), i64([4]), p, ws, 8, None) == la.KFAC_ERR_WORKSPACE
 
 
+def test_stream_copy_rejects_bad_arguments(lib):
+    src, dst = ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE + (1 << 20))
+    assert lib.kfac_stream_copy(src, dst, 0, None) == la.KFAC_OK                          # nothing to do
+    assert lib.kfac_stream_copy(src, dst, 24, None) == la.KFAC_ERR_INVALID_VALUE          # not a multiple of 16
+    assert lib.kfac_stream_copy(ctypes.c_void_p(FAKE + 4), dst, 16, None) == la.KFAC_ERR_INVALID_VALUE
+    assert lib.kfac_stream_copy(src, ctypes.c_void_p(FAKE + 8), 4096, None) == la.KFAC_ERR_INVALID_VALUE
+    assert lib.kfac_stream_copy(src, ctypes.c_void_p(FAKE + 16), 4096, None) == la.KFAC_ERR_INVALID_VALUE  # overlap
+    assert lib.kfac_stream_copy(ctypes.c_void_p(0), dst, 16, None) == la.KFAC_ERR_INVALID_VALUE
+
+
 def test_python_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros(4, 3)

@@ -100,3 +100,45 @@ def test_preconditioner_two_steps_against_oracle():
     for h in hooks:
         h.remove()
     pre.remove()
+
+
+def test_preconditioner_failed_inverse_keeps_previous():
+    """A factor whose damped inverse fails (here a NaN planted in the running
+    factor) keeps its previous inverse: the step warns, lists the factor in
+    ``failed``, and the preconditioned gradients stay finite."""
+    import torch
+    from linear_algebra_amd.kfac_preconditioner import KFACPreconditioner
+    model = build_model()
+    pre = KFACPreconditioner(model, damping=GAMMA, factor_decay=EPS, inv_update_freq=1)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(5)
+    y = torch.randint(0, 10, (8,), device=DEV, generator=gen)
+    for step in range(2):
+        x = torch.randn(8, 3, 12, 12, device=DEV, generator=gen)
+        model.zero_grad()
+        torch.nn.functional.cross_entropy(model(x), y).backward()
+        if step == 0:
+            pre.step()
+            assert pre.failed == []
+            kept = pre.Ginv[0].clone()
+            pre.G[0][0, 0] = float("nan")
+        else:
+            with pytest.warns(UserWarning, match="previous inverses are kept"):
+                pre.step()
+    nl = len(pre.layers)
+    assert pre.failed == [nl]
+    torch.testing.assert_close(pre.Ginv[0], kept, rtol=0, atol=0)
+    for m in pre.layers:
+        assert bool(torch.isfinite(m.weight.grad).all())
+
+
+def test_preconditioner_failed_first_inverse_raises():
+    import torch
+    from linear_algebra_amd.kfac_preconditioner import KFACPreconditioner
+    model = build_model()
+    pre = KFACPreconditioner(model, damping=GAMMA, factor_decay=EPS, inv_update_freq=1)
+    x = torch.randn(4, 3, 12, 12, device=DEV)
+    x[0, 0, 0, 0] = float("nan")
+    torch.nn.functional.cross_entropy(model(x), torch.zeros(4, dtype=torch.long, device=DEV)).backward()
+    with pytest.raises(RuntimeError, match="no previous inverse"):
+        pre.step()
