@@ -114,6 +114,21 @@ size_t kfac_pack_workspace_size(int n, const int64_t* d);
 kfac_status_t kfac_pack_sym(int n, float* const* m, const int64_t* d, float* packed, kfac_pack_dir_t dir,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* kfac_pack_sym without a workspace, for callers that cannot allocate device
+ * memory (code under stream capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments, results and errors as kfac_pack_sym;
+ * the layer table lives in a device array of the library instead (64 KiB per
+ * GPU, held until the process ends).  It allocates nothing: no hipMalloc, no
+ * hipFree, no allocating library call.  At most KFAC_STATIC_MAX_FACTORS
+ * factors per call, else KFAC_ERR_UNSUPPORTED (nothing enqueued).  Every call
+ * on one GPU shares that array, and the last call's table stays in it: calls
+ * that may overlap on one GPU (different streams, or different host threads
+ * without ordering) race and must not be made.
+ */
+#define KFAC_STATIC_MAX_FACTORS 1024
+kfac_status_t kfac_pack_sym_static(int n, float* const* m, const int64_t* d, float* packed, kfac_pack_dir_t dir,
+                                   hipStream_t stream);
+
 /* Plain device-to-device copy of `bytes` bytes (16-byte loads and stores,
  * one per lane).  It computes nothing of the method: it is the measured
  * streaming rate that the HBM-bound figures of pack and unpack are set

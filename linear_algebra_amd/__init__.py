@@ -25,7 +25,7 @@ KFAC_PACK, KFAC_UNPACK = 0, 1
 EXPORTS = (
     "kfac_abi_version", "kfac_status_string",
     "kfac_factors_workspace_size", "kfac_factors",
-    "kfac_packed_size", "kfac_pack_workspace_size", "kfac_pack_sym", "kfac_stream_copy",
+    "kfac_packed_size", "kfac_pack_workspace_size", "kfac_pack_sym", "kfac_pack_sym_static", "kfac_stream_copy",
     "kfac_inverse_workspace_size", "kfac_damped_inverse",
     "kfac_precondition_workspace_size", "kfac_precondition",
     "kfac_im2col_workspace_size", "kfac_im2col",
@@ -73,6 +73,7 @@ def load_library(path: str = LIB_PATH):
         "kfac_packed_size": (i64, [i32, vp]),
         "kfac_pack_workspace_size": (sz, [i32, vp]),
         "kfac_pack_sym": (i32, [i32, vp, vp, vp, i32, vp, sz, vp]),
+        "kfac_pack_sym_static": (i32, [i32, vp, vp, vp, i32, vp]),
         "kfac_stream_copy": (i32, [vp, vp, sz, vp]),
         "kfac_inverse_workspace_size": (sz, [i32, vp]),
         "kfac_damped_inverse": (i32, [i32, vp, vp, f32, vp, vp, vp, sz, vp]),
@@ -215,6 +216,24 @@ def kfac_pack_sym(ms: Sequence, packed, direction: int, stream=None) -> None:
     _keep_for(ws, stream)
 
 
+def kfac_pack_sym_static(ms: Sequence, packed, direction: int, stream=None) -> None:
+    """kfac_pack_sym without a workspace: the library's own device array holds
+    the layer table, and nothing is allocated (at most 1024 factors; calls
+    that may overlap on one GPU race)."""
+    import torch
+    lib = load_library()
+    dev = _check(list(ms) + [packed], torch.float32, "kfac_pack_sym_static")
+    d = []
+    for m in ms:
+        if m.dim() != 2 or m.shape[0] != m.shape[1]:
+            raise ValueError("kfac_pack_sym_static: factors must be square")
+        d.append(m.shape[0])
+    if packed.numel() != kfac_packed_size(d):
+        raise ValueError("kfac_pack_sym_static: packed buffer has the wrong length")
+    _call(lib.kfac_pack_sym_static(len(ms), _ptrs(ms), _i64(d), ctypes.c_void_p(packed.data_ptr()), int(direction),
+                                   _stream(dev, stream)), "kfac_pack_sym_static")
+
+
 def kfac_stream_copy(src, dst, stream=None) -> None:
     """dst <- src, a plain device copy (the streaming reference of pack)."""
     lib = load_library()
@@ -275,7 +294,8 @@ def kfac_precondition(ginvs: Sequence, grads: Sequence, ainvs: Sequence, outs: S
 
 __all__ = [
     "load_library", "status_string", "KfacError", "KfacLibraryError",
-    "kfac_factors", "kfac_packed_size", "kfac_pack_sym", "kfac_stream_copy", "kfac_damped_inverse",
+    "kfac_factors", "kfac_packed_size", "kfac_pack_sym", "kfac_pack_sym_static", "kfac_stream_copy",
+    "kfac_damped_inverse",
     "kfac_precondition",
     "KFAC_F32", "KFAC_BF16", "KFAC_PACK", "KFAC_UNPACK", "EXPORTS",
 ]

@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstring>
 #include <initializer_list>
+#include <mutex>
 #include <numeric>
 #include <vector>
 
@@ -325,6 +326,71 @@ hipError_t upload_tables(std::initializer_list<TablePart> parts, hipStream_t str
     return upload_table(lo, blob.data(), blob.size(), stream);
 }
 
+namespace {
+
+// --------------------------------------------------------------- packing --
+
+kfac_status_t pack_args(int n, float* const* m, const int64_t* d, const float* packed, kfac_pack_dir_t dir) {
+    if (!valid_dims(n, d) || m == nullptr || packed == nullptr || !aligned(packed, 4)) return KFAC_ERR_INVALID_VALUE;
+    if (dir != KFAC_PACK && dir != KFAC_UNPACK) return KFAC_ERR_INVALID_VALUE;
+    for (int i = 0; i < n; ++i)
+        if (m[i] == nullptr || !aligned(m[i], 4)) return KFAC_ERR_INVALID_VALUE;
+    return KFAC_OK;
+}
+
+// The host keeps only the totals that size the grid; the per-layer offsets
+// are prefix sums formed on the device, in the tables carved from `ws`.
+hipError_t pack_run(int n, float* const* m, const int64_t* d, float* packed, kfac_pack_dir_t dir, void* ws,
+                    hipStream_t stream) {
+    std::vector<PackSrc> src(n);
+    int64_t total = 0, tiles = 0;
+    for (int i = 0; i < n; ++i) {
+        src[i] = PackSrc{m[i], d[i]};
+        const int64_t t1 = ceil_div(d[i], kUnpackTile);
+        total += d[i] * (d[i] + 1) / 2;
+        tiles += t1 * (t1 + 1) / 2;
+    }
+    Carver c(ws);
+    PackSrc* src_dev = static_cast<PackSrc*>(c.take(sizeof(PackSrc) * n));
+    PackLayer* layers_dev = static_cast<PackLayer*>(c.take(sizeof(PackLayer) * n));
+    hipError_t e = upload_table(src_dev, src.data(), sizeof(PackSrc) * n, stream);
+    if (e == hipSuccess) e = launch_pack_table(src_dev, n, layers_dev, stream);
+    if (e == hipSuccess)
+        e = dir == KFAC_PACK ? launch_pack(layers_dev, n, packed, total, stream)
+                             : launch_unpack(layers_dev, n, packed, tiles, stream);
+    return e;
+}
+
+// ------------------------------------------------- allocation-free scratch --
+// The tables of kfac_pack_sym_static live in this array instead of a
+// caller's workspace.  In host code `scratch` names a host-side stand-in,
+// not the device memory: its device address is looked up once per device
+// (with that device current) and only that address is handed to kernels.
+constexpr size_t kStaticScratchBytes = 64 * 1024;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t static_scratch(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
 }  // namespace kfac
 
 using namespace kfac;
@@ -406,31 +472,23 @@ size_t kfac_pack_workspace_size(int n, const int64_t* d) {
 
 kfac_status_t kfac_pack_sym(int n, float* const* m, const int64_t* d, float* packed, kfac_pack_dir_t dir,
                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    if (!valid_dims(n, d) || m == nullptr || packed == nullptr || !aligned(packed, 4)) return KFAC_ERR_INVALID_VALUE;
-    if (dir != KFAC_PACK && dir != KFAC_UNPACK) return KFAC_ERR_INVALID_VALUE;
-    for (int i = 0; i < n; ++i)
-        if (m[i] == nullptr || !aligned(m[i], 4)) return KFAC_ERR_INVALID_VALUE;
+    const kfac_status_t st = pack_args(n, m, d, packed, dir);
+    if (st != KFAC_OK) return st;
     const size_t need = pack_ws(n);
     if (workspace == nullptr || !aligned(workspace, kAlign) || workspace_bytes < need) return KFAC_ERR_WORKSPACE;
+    return hip_status(pack_run(n, m, d, packed, dir, workspace, stream));
+}
 
-    // the host keeps only the totals that size the grid; the per-layer
-    // offsets are prefix sums formed on the device
-    std::vector<PackSrc> src(n);
-    int64_t total = 0, tiles = 0;
-    for (int i = 0; i < n; ++i) {
-        src[i] = PackSrc{m[i], d[i]};
-        const int64_t t1 = ceil_div(d[i], kUnpackTile);
-        total += d[i] * (d[i] + 1) / 2;
-        tiles += t1 * (t1 + 1) / 2;
-    }
-    Carver c(workspace);
-    PackSrc* src_dev = static_cast<PackSrc*>(c.take(sizeof(PackSrc) * n));
-    PackLayer* layers_dev = static_cast<PackLayer*>(c.take(sizeof(PackLayer) * n));
-    hipError_t e = upload_table(src_dev, src.data(), sizeof(PackSrc) * n, stream);
-    if (e == hipSuccess) e = launch_pack_table(src_dev, n, layers_dev, stream);
-    if (e == hipSuccess)
-        e = dir == KFAC_PACK ? launch_pack(layers_dev, n, packed, total, stream)
-                             : launch_unpack(layers_dev, n, packed, tiles, stream);
+kfac_status_t kfac_pack_sym_static(int n, float* const* m, const int64_t* d, float* packed, kfac_pack_dir_t dir,
+                                   hipStream_t stream) {
+    const kfac_status_t st = pack_args(n, m, d, packed, dir);
+    if (st != KFAC_OK) return st;
+    if (n > KFAC_STATIC_MAX_FACTORS) return KFAC_ERR_UNSUPPORTED;
+    static_assert(kStaticScratchBytes >= (sizeof(PackSrc) + sizeof(PackLayer)) * KFAC_STATIC_MAX_FACTORS + 2 * kAlign,
+                  "the static scratch holds the tables of KFAC_STATIC_MAX_FACTORS factors");
+    void* ws = nullptr;
+    hipError_t e = static_scratch(&ws);
+    if (e == hipSuccess) e = pack_run(n, m, d, packed, dir, ws, stream);
     return hip_status(e);
 }
 

@@ -131,6 +131,19 @@ def test_pack_and_precondition_reject_bad_arguments(lib):
     assert lib.kfac_precondition(1, p, p, p, i64([4]), i64([4]), p, ws, 8, None) == la.KFAC_ERR_WORKSPACE
 
 
+def test_static_pack_rejects_bad_arguments(lib):
+    """The allocation-free pack validates like kfac_pack_sym and refuses more
+    factors than its array holds, all before any device call."""
+    n = 1025
+    m = vps([FAKE] * n)
+    packed = ctypes.c_void_p(FAKE)
+    assert lib.kfac_pack_sym_static(n, m, i64([4] * n), packed, 0, None) == la.KFAC_ERR_UNSUPPORTED
+    assert lib.kfac_pack_sym_static(1, m, i64([4]), packed, 2, None) == la.KFAC_ERR_INVALID_VALUE
+    assert lib.kfac_pack_sym_static(1, m, i64([0]), packed, 0, None) == la.KFAC_ERR_INVALID_VALUE
+    assert lib.kfac_pack_sym_static(1, m, i64([4]), ctypes.c_void_p(0), 0, None) == la.KFAC_ERR_INVALID_VALUE
+    assert lib.kfac_pack_sym_static(1, vps([FAKE + 2]), i64([4]), packed, 1, None) == la.KFAC_ERR_INVALID_VALUE
+
+
 def test_stream_copy_rejects_bad_arguments(lib):
     src, dst = ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE + (1 << 20))
     assert lib.kfac_stream_copy(src, dst, 0, None) == la.KFAC_OK                          # nothing to do
