@@ -20,7 +20,9 @@
 // one k-value per lane).  bfloat16 slabs of 4-byte aligned rows do the same
 // and are read back with transposing LDS reads, since
 // v_mfma_f32_32x32x16_bf16 takes 8 consecutive k-values per lane; rows of
-// odd width pass through registers and are stored as [m][k].
+// odd width are first repacked to an aligned pitch (bf16_repack.hip), and
+// only an input of even width at a base one element off a 4-byte boundary
+// passes through registers, stored as [m][k].
 #include "device_common.h"
 #include "internal.h"
 
@@ -67,21 +69,22 @@ __device__ __forceinline__ void elem_store(const GemmProb& P, int i, int j, floa
 }
 
 constexpr uint32_t kOOB = 0x80000000u;  // buffer offset past any slab: loads return 0
-constexpr int RED_SLICES = 16;     // workgroups per partial tile in the reduce
 
 // Buffer resource over rows [k0, min(k0 + BK, k_end)) of a row-major
 // operand; rows past the end of the slab read as zero.
 // The range ends at column `cols` of the slab's last row (the operand's
 // last element there), not at the end of that row: a 16-byte copy that
 // straddles the last column then stops at the operand's end instead of
-// reading past it.
+// reading past it.  The range is checked per dword, so it is rounded up to
+// a 4-byte boundary: otherwise a last bf16 element sharing its dword with
+// the next (a row of odd width repacked to an even pitch) would read as zero.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const void* base, int64_t ld, int k0, int k_end, int esz,
                                                             int cols) {
     const char* p = static_cast<const char*>(base) + (int64_t)k0 * ld * esz;
     const int rows = max(0, min(BK, k_end - k0));
     // every operand is uniform; readfirstlane keeps the descriptor in
     // scalar registers (a per-lane descriptor would need a waterfall loop)
-    const int bytes = __builtin_amdgcn_readfirstlane(rows > 0 ? ((rows - 1) * (int)ld + cols) * esz : 0);
+    const int bytes = __builtin_amdgcn_readfirstlane(rows > 0 ? (((rows - 1) * (int)ld + cols) * esz + 3) & ~3 : 0);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p), (short)0, bytes, 0x00020000);
 }
 
@@ -566,13 +569,16 @@ __global__ __launch_bounds__(NT, 2) void gemm_tn_bf16_kernel(GemmLaunch L, int64
 }
 
 // Sums the split-K partial tiles in chunk order and applies the epilogue.
-// Each partial tile is spread over RED_SLICES workgroups; thread t sums
-// four consecutive elements, with the loads of four chunks in flight.
+// Each partial tile (T x T, T the launch's tile edge) is spread over
+// T * T / 1024 workgroups; thread t sums four consecutive elements, with
+// the loads of four chunks in flight.
 __global__ __launch_bounds__(NT) void gemm_reduce_kernel(GemmLaunch L, int64_t slices) {
     const int64_t g = blockIdx.x;
     if (g >= slices) return;
-    const int64_t tile = g / RED_SLICES;
-    const int slice = (int)(g % RED_SLICES);
+    const int T = L.tile;
+    const int per_tile = T * T / (4 * NT);
+    const int64_t tile = g / per_tile;
+    const int slice = (int)(g % per_tile);
     const GemmProb P = L.probs[find_prob(L.probs, L.nprob, tile, true)];
     const int t = (int)(tile - P.red_begin);
     int ti, tj;
@@ -582,9 +588,9 @@ __global__ __launch_bounds__(NT) void gemm_reduce_kernel(GemmLaunch L, int64_t s
         ti = t / P.tiles_n;
         tj = t % P.tiles_n;
     }
-    const int e0 = slice * (BM * BM / RED_SLICES) + threadIdx.x * 4;
-    const int64_t stride4 = (int64_t)P.ntiles * (BM * BM) / 4;
-    const float4* base = reinterpret_cast<const float4*>(P.part + (int64_t)t * (BM * BM) + e0);
+    const int e0 = slice * (4 * NT) + threadIdx.x * 4;
+    const int64_t stride4 = (int64_t)P.ntiles * T * T / 4;
+    const float4* base = reinterpret_cast<const float4*>(P.part + (int64_t)t * T * T + e0);
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
     int k = 0;
     for (; k + 4 <= P.ksplit; k += 4) {
@@ -603,12 +609,12 @@ __global__ __launch_bounds__(NT) void gemm_reduce_kernel(GemmLaunch L, int64_t s
     float res[4] = {0.f, 0.f, 0.f, 0.f};
     if (P.mode == kModeFactor && !L.first_step) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) res[q] = elem_prev(P, ti * BM + (e0 + q) / BM, tj * BM + (e0 + q) % BM);
+        for (int q = 0; q < 4; ++q) res[q] = elem_prev(P, ti * T + (e0 + q) / T, tj * T + (e0 + q) % T);
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) res[q] = elem_value(P, sv[q], res[q], L.eps, L.first_step);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) elem_store(P, ti * BM + (e0 + q) / BM, tj * BM + (e0 + q) % BM, res[q]);
+    for (int q = 0; q < 4; ++q) elem_store(P, ti * T + (e0 + q) / T, tj * T + (e0 + q) % T, res[q]);
 }
 
 }  // namespace
@@ -633,7 +639,7 @@ hipError_t launch_gemm(const GemmLaunch& L, int64_t items, hipStream_t stream, b
 
 hipError_t launch_gemm_reduce(const GemmLaunch& L, int64_t tiles, hipStream_t stream) {
     if (tiles <= 0) return hipSuccess;
-    const int64_t slices = tiles * RED_SLICES;
+    const int64_t slices = tiles * (int64_t)(L.tile * L.tile / (4 * NT));
     hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)slices), dim3(NT), 0, stream, L, slices);
     return hipGetLastError();
 }

@@ -59,11 +59,27 @@ struct GemmLaunch {
     int32_t nprob;
     int32_t first_step;
     float eps;
-    int32_t runs;         // set by launch_gemm: items go to XCDs in runs (large launches)
+    int32_t runs;         // set by the launchers: items go to XCDs in runs (large launches)
+    int32_t tile;         // output tile edge of the launch (kGemmTile)
 };
 
+// C = alpha Aop^T Bop on 128 x 128 tiles (float32 operands, or bfloat16
+// operands when `bf16`), then, for split K, the partials summed in chunk
+// order and the epilogue
 hipError_t launch_gemm(const GemmLaunch& L, int64_t items, hipStream_t stream, bool bf16);
 hipError_t launch_gemm_reduce(const GemmLaunch& L, int64_t tiles, hipStream_t stream);
+
+// An odd-width bf16 input copied to a pitch that is a multiple of 8 elements
+// (columns past d zero); 256 groups of 8 elements per workgroup.
+struct RepackLayer {
+    const uint16_t* src;   // [rows][d]
+    uint16_t* dst;         // [rows][pitch], 16-byte aligned
+    int64_t rows;
+    int64_t block_begin;   // first workgroup of this layer
+    int32_t d, pitch;
+};
+__host__ __device__ inline int64_t repack_pitch(int64_t d) { return (d + 7) / 8 * 8; }
+hipError_t launch_repack_bf16(const RepackLayer* layers, int n, int64_t blocks, hipStream_t stream);
 
 // ----------------------------------------------------------------- layers --
 constexpr int kLayerTile = 64;       // im2col and gradient-row tiles are 64 x 64

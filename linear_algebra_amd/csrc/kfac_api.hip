@@ -51,11 +51,14 @@ struct FactorPlan {
     int64_t items = 0;
     int64_t red_tiles = 0;
     size_t part_bytes = 0;
+    std::vector<int> repack;        // bf16 inputs of odd width, copied to an aligned pitch first
+    size_t repack_bytes = 0;        // their copies, each 256-byte aligned
 };
 
 // Rows per K chunk: enough chunks overall to keep every CU busy, never so
-// many that the partial tiles outweigh the work.
-FactorPlan plan_factors(int n, const int64_t* rows, const int64_t* d) {
+// many that the partial tiles outweigh the work.  bf16 inputs of odd width
+// are repacked to an aligned pitch first (bf16_repack.hip).
+FactorPlan plan_factors(int n, const int64_t* rows, const int64_t* d, bool bf16) {
     FactorPlan p;
     p.probs.resize(n);
     double work = 0.0;
@@ -91,13 +94,22 @@ FactorPlan plan_factors(int n, const int64_t* rows, const int64_t* d) {
         }
     }
     p.part_bytes = (size_t)part_elems * sizeof(float);
+    for (int i = 0; bf16 && i < n; ++i) {
+        if (d[i] % 2 == 0) continue;
+        p.repack.push_back(i);
+        p.repack_bytes += align_up((size_t)rows[i] * (size_t)repack_pitch(d[i]) * 2, kAlign);
+    }
     return p;
 }
 
+// Workspace: the two tables next to each other (one upload), then the
+// split-K partials and the repacked inputs.
 size_t factors_ws(const FactorPlan& p, int n) {
     Carver c(nullptr);
     c.take(sizeof(GemmProb) * n);
+    c.take(sizeof(RepackLayer) * p.repack.size());
     c.take(p.part_bytes);
+    c.take(p.repack_bytes);
     return c.used;
 }
 
@@ -416,7 +428,7 @@ size_t kfac_factors_workspace_size(int n, const int64_t* rows, const int64_t* d,
     if (!valid_dims(n, d) || rows == nullptr || (in_dtype != KFAC_F32 && in_dtype != KFAC_BF16)) return 0;
     for (int i = 0; i < n; ++i)
         if (rows[i] < 1 || rows[i] > INT32_MAX) return 0;
-    return factors_ws(plan_factors(n, rows, d), n);
+    return factors_ws(plan_factors(n, rows, d, in_dtype == KFAC_BF16), n);
 }
 
 kfac_status_t kfac_factors(int n, const void* const* x, const int64_t* rows, const int64_t* d,
@@ -430,28 +442,50 @@ kfac_status_t kfac_factors(int n, const void* const* x, const int64_t* rows, con
         if (rows[i] < 1 || rows[i] > INT32_MAX) return KFAC_ERR_INVALID_VALUE;
         if (x[i] == nullptr || m[i] == nullptr || !aligned(x[i], esz) || !aligned(m[i], 4)) return KFAC_ERR_INVALID_VALUE;
     }
-    FactorPlan p = plan_factors(n, rows, d);
+    const bool bf16 = in_dtype == KFAC_BF16;
+    FactorPlan p = plan_factors(n, rows, d, bf16);
     const size_t need = factors_ws(p, n);
     if (workspace == nullptr || !aligned(workspace, kAlign) || workspace_bytes < need) return KFAC_ERR_WORKSPACE;
 
     Carver c(workspace);
     GemmProb* probs_dev = static_cast<GemmProb*>(c.take(sizeof(GemmProb) * n));
+    RepackLayer* repack_dev = static_cast<RepackLayer*>(c.take(sizeof(RepackLayer) * p.repack.size()));
     float* part = static_cast<float*>(c.take(p.part_bytes));
+    uint8_t* repack_buf = static_cast<uint8_t*>(c.take(p.repack_bytes));
+    std::vector<RepackLayer> rl(p.repack.size());
+    int64_t repack_blocks = 0;
+    for (size_t r = 0; r < p.repack.size(); ++r) {
+        const int i = p.repack[r];
+        const int64_t pitch = repack_pitch(d[i]);
+        rl[r] = RepackLayer{static_cast<const uint16_t*>(x[i]), reinterpret_cast<uint16_t*>(repack_buf), rows[i],
+                            repack_blocks, (int32_t)d[i], (int32_t)pitch};
+        repack_buf += align_up((size_t)rows[i] * (size_t)pitch * 2, kAlign);
+        repack_blocks += ceil_div(rows[i] * (pitch / 8), 256);
+    }
     int64_t part_off = 0;
+    for (size_t r = 0; r < p.repack.size(); ++r) {
+        GemmProb& g = p.probs[p.repack[r]];
+        g.a = g.b = rl[r].dst;
+        g.lda = g.ldb = rl[r].pitch;
+    }
     for (int i = 0; i < n; ++i) {
         GemmProb& g = p.probs[i];
-        g.a = g.b = x[i];
+        if (g.a == nullptr) g.a = g.b = x[i];
         g.c = m[i];
-        g.bf16 = in_dtype == KFAC_BF16;
+        g.bf16 = bf16;
         if (g.ksplit > 1) {
             g.part = part + part_off;
             part_off += (int64_t)g.ntiles * g.ksplit * kGemmTile * kGemmTile;
         }
     }
-    hipError_t e = upload_table(probs_dev, p.probs.data(), sizeof(GemmProb) * n, stream);
+    hipError_t e = rl.empty() ? upload_table(probs_dev, p.probs.data(), sizeof(GemmProb) * n, stream)
+                              : upload_tables({{probs_dev, p.probs.data(), sizeof(GemmProb) * n},
+                                               {repack_dev, rl.data(), sizeof(RepackLayer) * rl.size()}},
+                                              stream);
+    if (e == hipSuccess && !rl.empty()) e = launch_repack_bf16(repack_dev, (int)rl.size(), repack_blocks, stream);
     if (e != hipSuccess) return KFAC_ERR_HIP;
-    GemmLaunch L{probs_dev, n, first_step ? 1 : 0, eps, 0};
-    e = launch_gemm(L, p.items, stream, in_dtype == KFAC_BF16);
+    GemmLaunch L{probs_dev, n, first_step ? 1 : 0, eps, 0, kGemmTile};
+    e = launch_gemm(L, p.items, stream, bf16);
     if (e != hipSuccess) return KFAC_ERR_HIP;
     return hip_status(launch_gemm_reduce(L, p.red_tiles, stream));
 }
@@ -651,11 +685,11 @@ kfac_status_t kfac_precondition(int n, const float* const* ginv, const float* co
     hipError_t e = upload_tables({{p1_dev, p.p1.data(), sizeof(GemmProb) * n}, {p2_dev, p.p2.data(), sizeof(GemmProb) * n}},
                                  stream);
     if (e != hipSuccess) return KFAC_ERR_HIP;
-    GemmLaunch L1{p1_dev, n, 0, 0.0f, 0};
+    GemmLaunch L1{p1_dev, n, 0, 0.0f, 0, kGemmTile};
     e = launch_gemm(L1, p.items1, stream, false);
     if (e == hipSuccess) e = launch_gemm_reduce(L1, p.red1, stream);
     if (e != hipSuccess) return KFAC_ERR_HIP;
-    GemmLaunch L2{p2_dev, n, 0, 0.0f, 0};
+    GemmLaunch L2{p2_dev, n, 0, 0.0f, 0, kGemmTile};
     e = launch_gemm(L2, p.items2, stream, false);
     if (e == hipSuccess) e = launch_gemm_reduce(L2, p.red2, stream);
     return hip_status(e);
