@@ -295,7 +295,7 @@ __device__ __forceinline__ void gemm_f32_tile(const GemmLaunch& L, const TileWor
     store_tile(P, L, sum, W.kc, W.t, W.m0, W.n0, wm, wn, lane);
 }
 
-__global__ __launch_bounds__(NT, 2) void gemm_tn_kernel(GemmLaunch L, int64_t items) {
+__device__ __forceinline__ void gemm_f32_item(const GemmLaunch& L, int64_t items) {
     __shared__ __attribute__((aligned(16))) float A0[SLAB];
     __shared__ __attribute__((aligned(16))) float A1[SLAB];
     __shared__ __attribute__((aligned(16))) float B0[SLAB];
@@ -306,6 +306,11 @@ __global__ __launch_bounds__(NT, 2) void gemm_tn_kernel(GemmLaunch L, int64_t it
     if (W.same) gemm_f32_tile<true>(L, W, A0, A1, B0, B1);
     else gemm_f32_tile<false>(L, W, A0, A1, B0, B1);
 }
+
+// The same kernel under the name of each stage, so that kernel traces give
+// the factors and the preconditioning products their own figures.
+__global__ __launch_bounds__(NT, 2) void factor_f32_kernel(GemmLaunch L, int64_t items) { gemm_f32_item(L, items); }
+__global__ __launch_bounds__(NT, 2) void precond_f32_kernel(GemmLaunch L, int64_t items) { gemm_f32_item(L, items); }
 
 
 // bfloat16 inputs on v_mfma_f32_32x32x16_bf16 (products exact in float32,
@@ -551,7 +556,7 @@ __device__ __forceinline__ void gemm_bf16_lds_tile(const GemmLaunch& L, const Ti
 
 // Rows whose starts are all 4-byte aligned (an even row pitch and an
 // aligned base) take the copy path; others are loaded element by element.
-__global__ __launch_bounds__(NT, 2) void gemm_tn_bf16_kernel(GemmLaunch L, int64_t items) {
+__global__ __launch_bounds__(NT, 2) void factor_bf16_kernel(GemmLaunch L, int64_t items) {
     __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDK16];
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BM * LDK16];
     __shared__ __attribute__((aligned(16))) uint16_t A0[SLAB16];
@@ -572,7 +577,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_tn_bf16_kernel(GemmLaunch L, int64
 // Each partial tile (T x T, T the launch's tile edge) is spread over
 // T * T / 1024 workgroups; thread t sums four consecutive elements, with
 // the loads of four chunks in flight.
-__global__ __launch_bounds__(NT) void gemm_reduce_kernel(GemmLaunch L, int64_t slices) {
+__device__ __forceinline__ void gemm_reduce(const GemmLaunch& L, int64_t slices) {
     const int64_t g = blockIdx.x;
     if (g >= slices) return;
     const int T = L.tile;
@@ -617,9 +622,12 @@ __global__ __launch_bounds__(NT) void gemm_reduce_kernel(GemmLaunch L, int64_t s
     for (int q = 0; q < 4; ++q) elem_store(P, ti * T + (e0 + q) / T, tj * T + (e0 + q) % T, res[q]);
 }
 
+__global__ __launch_bounds__(NT) void factor_reduce_kernel(GemmLaunch L, int64_t slices) { gemm_reduce(L, slices); }
+__global__ __launch_bounds__(NT) void precond_reduce_kernel(GemmLaunch L, int64_t slices) { gemm_reduce(L, slices); }
+
 }  // namespace
 
-hipError_t launch_gemm(const GemmLaunch& L, int64_t items, hipStream_t stream, bool bf16) {
+hipError_t launch_gemm(const GemmLaunch& L, int64_t items, hipStream_t stream, bool bf16, bool factor) {
     if (items <= 0) return hipSuccess;
     // Items of different problems differ in cost (K chunks of different
     // length, diagonal tiles with an idle wave).  Large launches hand items to
@@ -630,17 +638,22 @@ hipError_t launch_gemm(const GemmLaunch& L, int64_t items, hipStream_t stream, b
     R.runs = items >= kGemmRunsMin ? 1 : 0;
     const int64_t grid = R.runs ? (items + 8 * kGemmRun - 1) / (8 * kGemmRun) * (8 * kGemmRun) : items;
     if (bf16) {
-        hipLaunchKernelGGL(gemm_tn_bf16_kernel, dim3((unsigned)grid), dim3(NT), 0, stream, R, items);
+        hipLaunchKernelGGL(factor_bf16_kernel, dim3((unsigned)grid), dim3(NT), 0, stream, R, items);
+    } else if (factor) {
+        hipLaunchKernelGGL(factor_f32_kernel, dim3((unsigned)grid), dim3(NT), 0, stream, R, items);
     } else {
-        hipLaunchKernelGGL(gemm_tn_kernel, dim3((unsigned)grid), dim3(NT), 0, stream, R, items);
+        hipLaunchKernelGGL(precond_f32_kernel, dim3((unsigned)grid), dim3(NT), 0, stream, R, items);
     }
     return hipGetLastError();
 }
 
-hipError_t launch_gemm_reduce(const GemmLaunch& L, int64_t tiles, hipStream_t stream) {
+hipError_t launch_gemm_reduce(const GemmLaunch& L, int64_t tiles, hipStream_t stream, bool factor) {
     if (tiles <= 0) return hipSuccess;
     const int64_t slices = tiles * (int64_t)(L.tile * L.tile / (4 * NT));
-    hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)slices), dim3(NT), 0, stream, L, slices);
+    if (factor)
+        hipLaunchKernelGGL(factor_reduce_kernel, dim3((unsigned)slices), dim3(NT), 0, stream, L, slices);
+    else
+        hipLaunchKernelGGL(precond_reduce_kernel, dim3((unsigned)slices), dim3(NT), 0, stream, L, slices);
     return hipGetLastError();
 }
 

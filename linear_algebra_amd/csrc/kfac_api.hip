@@ -485,9 +485,9 @@ kfac_status_t kfac_factors(int n, const void* const* x, const int64_t* rows, con
     if (e == hipSuccess && !rl.empty()) e = launch_repack_bf16(repack_dev, (int)rl.size(), repack_blocks, stream);
     if (e != hipSuccess) return KFAC_ERR_HIP;
     GemmLaunch L{probs_dev, n, first_step ? 1 : 0, eps, 0, kGemmTile};
-    e = launch_gemm(L, p.items, stream, bf16);
+    e = launch_gemm(L, p.items, stream, bf16, true);
     if (e != hipSuccess) return KFAC_ERR_HIP;
-    return hip_status(launch_gemm_reduce(L, p.red_tiles, stream));
+    return hip_status(launch_gemm_reduce(L, p.red_tiles, stream, true));
 }
 
 // ------------------------------------------------------------------- pack --
@@ -686,12 +686,12 @@ kfac_status_t kfac_precondition(int n, const float* const* ginv, const float* co
                                  stream);
     if (e != hipSuccess) return KFAC_ERR_HIP;
     GemmLaunch L1{p1_dev, n, 0, 0.0f, 0, kGemmTile};
-    e = launch_gemm(L1, p.items1, stream, false);
-    if (e == hipSuccess) e = launch_gemm_reduce(L1, p.red1, stream);
+    e = launch_gemm(L1, p.items1, stream, false, false);
+    if (e == hipSuccess) e = launch_gemm_reduce(L1, p.red1, stream, false);
     if (e != hipSuccess) return KFAC_ERR_HIP;
     GemmLaunch L2{p2_dev, n, 0, 0.0f, 0, kGemmTile};
-    e = launch_gemm(L2, p.items2, stream, false);
-    if (e == hipSuccess) e = launch_gemm_reduce(L2, p.red2, stream);
+    e = launch_gemm(L2, p.items2, stream, false, false);
+    if (e == hipSuccess) e = launch_gemm_reduce(L2, p.red2, stream, false);
     return hip_status(e);
 }
 
