@@ -439,7 +439,8 @@ def main(argv=None):
     for k in stages:
         bound, rate, peak, unit = stage_rate[k]
         stages_out[k] = {"ms": round(stage_ms[k], 4), "achieved": round(rate / scale[unit], 3), "unit": unit,
-                         "peak": peak / scale[unit], "frac": round(rate / peak, 4)}
+                         "peak": peak / scale[unit], "frac": round(rate / peak, 4),
+                         "traffic": measured_traffic(cfg.name, k)}
         if bound == "hbm":
             stages_out[k]["frac_of_copy"] = round(rate / copy_rate, 4)
     dom = max(stages, key=lambda k: stage_ms[k])

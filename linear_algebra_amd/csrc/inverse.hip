@@ -187,8 +187,22 @@ __device__ __forceinline__ void stage_piece(double* S, const Blk& b, int q) {
     }
 }
 
+// The k-values k and k + 1 (k even) of row m of a staged piece.  Untransposed
+// they are one 16-byte pair; transposed they sit in consecutive k-rows.
+template <int K>
+__device__ __forceinline__ double2 frag_pair(const double* S, bool trans, int m, int k) {
+    if (!trans) return *reinterpret_cast<const double2*>(S + staged_at<K>(false, m, k));
+    return make_double2(S[staged_at<K>(true, m, k)], S[staged_at<K>(true, m, k + 1)]);
+}
+
 // acc[m][n] += (neg ? -1 : 1) * sum_k A[m][k] B[n][k] over one staged piece;
-// the wave layout of mma_block.
+// the wave layout of mma_block.  The sum does not depend on which k-values
+// each MFMA takes, so every lane group reads a pair of them at once: in
+// steps of 8 k-values, lane group g (lanes 16 g .. 16 g + 15) takes k0 + 2 g
+// in the first product and k0 + 2 g + 1 in the second.  An untransposed
+// operand is then one 16-byte read per row, whole swizzled pairs, which
+// meet no bank conflict (8-byte reads of one half of each pair can reach
+// only half of the banks).
 template <int K>
 __device__ __forceinline__ void mma_staged(doublex4 (&acc)[2][2], const double* A, bool ta, const double* Bm, bool tb,
                                            bool neg) {
@@ -197,15 +211,22 @@ __device__ __forceinline__ void mma_staged(doublex4 (&acc)[2][2], const double* 
     const int li = lane & 15, lk = lane >> 4;
     const int ma = wr * 32 + li, nb = wc * 32 + li;
 #pragma unroll
-    for (int k0 = 0; k0 < K; k0 += 4) {
-        const int k = k0 + lk;
-        double a0 = A[staged_at<K>(ta, ma, k)], a1 = A[staged_at<K>(ta, ma + 16, k)];
-        const double b0 = Bm[staged_at<K>(tb, nb, k)], b1 = Bm[staged_at<K>(tb, nb + 16, k)];
-        if (neg) { a0 = -a0; a1 = -a1; }
-        acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, acc[0][0], 0, 0, 0);
-        acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, acc[0][1], 0, 0, 0);
-        acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, acc[1][0], 0, 0, 0);
-        acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, acc[1][1], 0, 0, 0);
+    for (int k0 = 0; k0 < K; k0 += 8) {
+        const int k = k0 + 2 * lk;
+        double2 a0 = frag_pair<K>(A, ta, ma, k), a1 = frag_pair<K>(A, ta, ma + 16, k);
+        const double2 b0 = frag_pair<K>(Bm, tb, nb, k), b1 = frag_pair<K>(Bm, tb, nb + 16, k);
+        if (neg) {
+            a0.x = -a0.x; a0.y = -a0.y;
+            a1.x = -a1.x; a1.y = -a1.y;
+        }
+        acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0.x, b0.x, acc[0][0], 0, 0, 0);
+        acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0.x, b1.x, acc[0][1], 0, 0, 0);
+        acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1.x, b0.x, acc[1][0], 0, 0, 0);
+        acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1.x, b1.x, acc[1][1], 0, 0, 0);
+        acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0.y, b0.y, acc[0][0], 0, 0, 0);
+        acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0.y, b1.y, acc[0][1], 0, 0, 0);
+        acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1.y, b0.y, acc[1][0], 0, 0, 0);
+        acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1.y, b1.y, acc[1][1], 0, 0, 0);
     }
 }
 
@@ -682,7 +703,7 @@ __device__ __forceinline__ void v_finalize(const InvLaunch& L, const InvMat& M, 
 // W_ij -= U_{k-1,i}^T U_{k-1,j} to the blocks k < i <= j, XCD by XCD.
 __global__ __launch_bounds__(NT, 2) void inv_step_kernel(InvLaunch L, int64_t tiles) {
     __shared__ PanelScratch R;
-    __shared__ double S0[SLOT], S1[SLOT];
+    __shared__ __attribute__((aligned(16))) double S0[SLOT], S1[SLOT];
     const Stage S{S0, S1};
     double* As = S0;
     double* Bs = S1;
@@ -794,7 +815,7 @@ constexpr int KT = 16;   // k-columns per staged piece in the triangular-inverse
 // T_IJ = sum_{t in G2, t <= J} U_It V_tJ, parked in W's lower block (J, I).
 __global__ __launch_bounds__(NT, 4) void inv_trtri_a_kernel(InvLaunch L, int64_t tiles) {
     // quarters of 16 k-columns (a 32 KB staging area): four workgroups share a CU
-    __shared__ double S0[2 * B * KT], S1[2 * B * KT];
+    __shared__ __attribute__((aligned(16))) double S0[2 * B * KT], S1[2 * B * KT];
     const Stage S{S0, S1};
     int mi;
     int64_t local;
@@ -819,7 +840,7 @@ __global__ __launch_bounds__(NT, 4) void inv_trtri_a_kernel(InvLaunch L, int64_t
 // V_IJ = - sum_{t in G1, t >= I} V_It T_tJ, written over U_IJ.
 __global__ __launch_bounds__(NT, 4) void inv_trtri_b_kernel(InvLaunch L, int64_t tiles) {
     // quarters of 16 k-columns (a 32 KB staging area): four workgroups share a CU
-    __shared__ double S0[2 * B * KT], S1[2 * B * KT];
+    __shared__ __attribute__((aligned(16))) double S0[2 * B * KT], S1[2 * B * KT];
     const Stage S{S0, S1};
     int mi;
     int64_t local;
@@ -849,7 +870,7 @@ __global__ __launch_bounds__(NT, 4) void inv_lauum_kernel(InvLaunch L, int64_t t
     constexpr int KL = 16;
     constexpr int FD = B * (B + 1) / 2;   // a 64 x 65 float32 block, in doubles
     static_assert(FD >= 2 * B * KL, "the first array also holds the A and B quarters of buffer 0");
-    __shared__ double S0[FD], S1[2 * B * KL];
+    __shared__ __attribute__((aligned(16))) double S0[FD], S1[2 * B * KL];
     const Stage S{S0, S1};
     float* F = reinterpret_cast<float*>(S0);
     int mi;
