@@ -133,6 +133,44 @@ __device__ __forceinline__ void store_tile(const GemmProb& P, const GemmLaunch& 
             for (int r = 0; r < 16; ++r) elem_store(P, m0 + row_of(a, r), n0 + col_of(b), res[a][b][r]);
 }
 
+// Tiles are numbered in bands of kBand tile rows, column by column within a
+// band, so that kBand^2 consecutive tiles form about a kBand x kBand block.
+// Large launches hand the XCDs runs of kGemmRun = kBand^2 consecutive items,
+// so the tiles of a run read 2 kBand operand panels between them, which the
+// XCD's L2 serves to all of them (in row order, a run of tiles in one tile
+// row reads one panel of A and a different panel of B per tile).  Factor
+// problems number only the upper triangle (i <= j); there the first kBand
+// columns of a band form a triangle.
+constexpr int kBand = 4;
+static_assert(kBand * kBand == kGemmRun, "an XCD run is one block of tiles");
+__device__ __forceinline__ void tile_decode(const GemmProb& P, int64_t t, int& ti, int& tj) {
+    if (P.mode == kModeFactor) {
+        const int64_t T = P.tiles_m;
+        int ir, jr;
+        upper_decode(t, T, ir, jr);   // the row-major position gives the band
+        const int64_t i0 = (int64_t)(ir / kBand) * kBand;
+        const int64_t r = min<int64_t>(kBand, T - i0);
+        const int64_t u = t - (i0 * T - i0 * (i0 - 1) / 2);
+        const int64_t tri = r * (r + 1) / 2;
+        if (u < tri) {
+            int a, c;
+            column_decode(u, a, c);
+            ti = (int)(i0 + a);
+            tj = (int)(i0 + c);
+        } else {
+            const int64_t v = u - tri;
+            ti = (int)(i0 + v % r);
+            tj = (int)(i0 + r + v / r);
+        }
+    } else {
+        const int64_t i0 = t / ((int64_t)kBand * P.tiles_n) * kBand;
+        const int64_t r = min<int64_t>(kBand, P.tiles_m - i0);
+        const int64_t u = t - i0 * P.tiles_n;
+        ti = (int)(i0 + u % r);
+        tj = (int)(u / r);
+    }
+}
+
 // Tile and K-chunk of a work item.
 struct TileWork {
     GemmProb P;
@@ -148,12 +186,7 @@ __device__ __forceinline__ TileWork decode_item(const GemmLaunch& L, int64_t ite
     w.kc = (int)(q / P.ntiles);
     w.t = (int)(q % P.ntiles);
     int ti, tj;
-    if (P.mode == kModeFactor) {
-        upper_decode(w.t, P.tiles_m, ti, tj);
-    } else {
-        ti = w.t / P.tiles_n;
-        tj = w.t % P.tiles_n;
-    }
+    tile_decode(P, w.t, ti, tj);
     w.m0 = ti * BM;
     w.n0 = tj * BM;
     w.k_begin = w.kc * P.kchunk;
@@ -587,12 +620,7 @@ __device__ __forceinline__ void gemm_reduce(const GemmLaunch& L, int64_t slices)
     const GemmProb P = L.probs[find_prob(L.probs, L.nprob, tile, true)];
     const int t = (int)(tile - P.red_begin);
     int ti, tj;
-    if (P.mode == kModeFactor) {
-        upper_decode(t, P.tiles_m, ti, tj);
-    } else {
-        ti = t / P.tiles_n;
-        tj = t % P.tiles_n;
-    }
+    tile_decode(P, t, ti, tj);
     const int e0 = slice * (4 * NT) + threadIdx.x * 4;
     const int64_t stride4 = (int64_t)P.ntiles * T * T / 4;
     const float4* base = reinterpret_cast<const float4*>(P.part + (int64_t)t * T * T + e0);

@@ -220,6 +220,8 @@ struct InvLaunch {
     int64_t part_end;     // potrf step launch: [fin_end, part_end) partial sums of the next column
     int32_t vlow;         // V_ic is kept in block (c, i) below the diagonal (formed beside potrf), not in (i, c)
     int32_t plo;          // potrf step launch: row k and the trailing update apply panels [plo, k)
+    int32_t rowq;         // potrf step launch: blocks of row k per row workgroup (>= 1)
+    int32_t pad_;
 };
 // At most this many panels per trailing update (k - plo).
 constexpr int kMaxPassDepth = 3;
@@ -258,7 +260,7 @@ __host__ __device__ inline bool trtri_balanced(int64_t nb) {
     return nb > 2 && nb - p <= p / 8;
 }
 
-__host__ __device__ inline int64_t inv_tiles(int kind, int64_t nb, int64_t step) {
+__host__ __device__ inline int64_t inv_tiles(int kind, int64_t nb, int64_t step, int64_t rowq = 1) {
     switch (kind) {
         case kInvPrepare:
         case kInvLauum:
@@ -275,8 +277,10 @@ __host__ __device__ inline int64_t inv_tiles(int kind, int64_t nb, int64_t step)
             return nb;
         case kInvBorderRun:  // one workgroup per block row (or column) and run of blocks
             return nb * border_runs(nb);
-        case kInvPanel:  // one workgroup per block right of the diagonal, at least one
-            return nb > step ? (nb - step - 1 > 1 ? nb - step - 1 : 1) : 0;
+        case kInvPanel: {  // one workgroup per rowq blocks right of the diagonal, at least one
+            const int64_t right = nb - step - 1;
+            return nb > step ? (right > rowq ? (right + rowq - 1) / rowq : 1) : 0;
+        }
         case kInvSyrk: {  // step k applies step k-1's update to blocks (i, j), k < i <= j
             const int64_t t = nb - step - 1;
             return step >= 1 && t > 0 ? t * (t + 1) / 2 : 0;

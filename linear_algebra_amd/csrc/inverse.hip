@@ -67,7 +67,7 @@ constexpr int kRun = 16;       // items per XCD run in launches of uneven items 
 __device__ __forceinline__ bool locate(const InvLaunch& L, int kind, int64_t tile, int& mat, int64_t& local) {
     for (int b = 0; b < L.nbuckets; ++b) {
         const InvBucket bk = L.buckets[b];
-        const int64_t per = inv_tiles(kind, bk.nb, L.step);
+        const int64_t per = inv_tiles(kind, bk.nb, L.step, kind == kInvPanel ? L.rowq : 1);
         const int64_t cnt = per * bk.count;
         if (tile < cnt) {
             mat = bk.first + (int)(tile / per);
@@ -230,6 +230,16 @@ __device__ __forceinline__ void mma_staged(doublex4 (&acc)[2][2], const double* 
     }
 }
 
+// A barrier that waits only for the workgroup's LDS accesses: unlike
+// __syncthreads() it lets global loads stay in flight (the block a caller
+// loaded into registers before a product, and the product's first copies,
+// then travel together).  The memory clobber keeps the compiler from moving
+// LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0); vmcnt and expcnt left at their maximum
+    asm volatile("s_barrier" ::: "memory");
+}
+
 // acc += (neg ? -1 : 1) sum_{t in [t0, t1)} A_t B_t^T, A_t and B_t the
 // 64 x 64 blocks srcA(t), srcB(t) (staged as [m][k]); `same` reuses A for B.
 // Each block is staged in 64 / K pieces of K k-columns; even pieces go
@@ -252,7 +262,7 @@ __device__ __forceinline__ void block_gemm(doublex4 (&acc)[2][2], const Stage& S
     double* const B0 = S.s0 + (same ? 0 : PD);
     double* const A1 = S.s1;
     double* const B1 = S.s1 + (same ? 0 : PD);
-    __syncthreads();   // earlier users of the staging area are done
+    lds_barrier();   // earlier users of the staging area are done
     stage_piece<K>(A0, srcA(t0), 0);
     if (!same) stage_piece<K>(B0, srcB(t0), 0);
     const int pieces = P * (t1 - t0);
@@ -557,18 +567,40 @@ __global__ __launch_bounds__(NT) void inv_prepare_kernel(InvLaunch L, int64_t ti
 // k-1's update to the diagonal block (k, k) and to its own block, then
 // factors the diagonal block and inverts its triangle (every row-k
 // workgroup of a matrix does so redundantly, so no launch boundary separates
-// the two), and solves U_kj = U_kk^-T W_kj.  The workgroup of the first such
-// block (or of the diagonal alone, in a matrix's last step) stores U_kk^-1
-// and the failure code.  Diagonal blocks of W are not written: later steps
-// read dinv.
+// the two), and solves U_kj = U_kk^-T W_kj.  With rowq > 1 a workgroup
+// owns rowq consecutive blocks of the row and solves each of them after one
+// factorisation.  The workgroup of the first such block (or of the diagonal
+// alone, in a matrix's last step) stores U_kk^-1 and the failure code.
+// Diagonal blocks of W are not written: later steps read dinv.
 __device__ __forceinline__ void potrf_row_block(const InvLaunch& L, const InvMat& M, int64_t local, double* As,
                                                 double* Bs, PanelScratch& R) {
     const int k = L.step;
     const int64_t D = (int64_t)M.nb * B;
     const bool has_right = k + 1 < M.nb;
-    const int J = k + 1 + (int)local;
+    // this workgroup's blocks of row k right of the diagonal: [J, Jend)
+    const int J = k + 1 + (int)local * L.rowq;
+    const int Jend = min(J + L.rowq, M.nb);
     double* Wkk = M.w + (int64_t)k * B * D + (int64_t)k * B;
     double* Wkj = M.w + (int64_t)k * B * D + (int64_t)J * B;
+    // Blocks after the first (rowq > 1): each takes the panels [plo, k) in
+    // turn and is written back; its solve, after the factorisation, reads it
+    // again (the same threads read the elements they wrote).
+    for (int Jx = J + 1; Jx < Jend && L.plo < k; ++Jx) {
+        double* Wkx = M.w + (int64_t)k * B * D + (int64_t)Jx * B;
+        doublex4 wx[2][2];
+        double xa[PER], xb[PER];
+        acc_load(wx, Wkx, D);
+        for (int p = L.plo; p < k; ++p) {
+            fetch(xa, Blk{M.w + (int64_t)p * B * D + (int64_t)k * B, D, true});
+            fetch(xb, Blk{M.w + (int64_t)p * B * D + (int64_t)Jx * B, D, true});
+            put(As, xa, true);
+            put(Bs, xb, true);
+            __syncthreads();
+            mma_block(wx, As, Bs, true);
+            __syncthreads();
+        }
+        acc_store(wx, Wkx, D);
+    }
     // Row k still lacks the updates of panels [plo, k) (one, or two where
     // the trailing update runs every other step).  Every block this
     // workgroup reads first is requested before the first wait, the first
@@ -627,6 +659,18 @@ __device__ __forceinline__ void potrf_row_block(const InvLaunch& L, const InvMat
     acc_zero(acc);
     mma_block(acc, As, Bs, false);
     acc_store(acc, Wkj, D);
+    // the same solve for the other blocks of this workgroup
+    for (int Jx = J + 1; Jx < Jend; ++Jx) {
+        double* Wkx = M.w + (int64_t)k * B * D + (int64_t)Jx * B;
+        doublex4 wx[2][2];
+        acc_load(wx, Wkx, D);
+        __syncthreads();   // the previous product is done with Bs
+        for_acc([&](int a, int b, int r, int row, int col) { Bs[col * LD + row] = wx[a][b][r]; });
+        __syncthreads();
+        acc_zero(acc);
+        mma_block(acc, As, Bs, false);
+        acc_store(acc, Wkx, D);
+    }
 }
 
 // Block V_im of V = U^-1 (m >= i) staged as [row][k]: the inverted diagonal

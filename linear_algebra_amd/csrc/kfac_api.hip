@@ -262,8 +262,11 @@ constexpr int64_t kFuseTilesPerStep = 2048;
 // panels deep, and of at least kPass3Tiles every third step.
 constexpr int64_t kPass2Tiles = 1024;
 constexpr int64_t kPass3Tiles = 8192;
+// Resident step-kernel workgroups (two per CU): the target count of row
+// workgroups in a step without a trailing update.
+constexpr int64_t kInvRowSlots = 512;
 
-int64_t bucket_tiles(const InvPlan& p, int kind, int step);
+int64_t bucket_tiles(const InvPlan& p, int kind, int step, int rowq = 1);
 
 bool fuse_v(const InvPlan& p) {
     int64_t tiles = 0;
@@ -286,9 +289,9 @@ size_t inverse_ws(int n, const int64_t* d) {
     return c.used;
 }
 
-int64_t bucket_tiles(const InvPlan& p, int kind, int step) {
+int64_t bucket_tiles(const InvPlan& p, int kind, int step, int rowq) {
     int64_t t = 0;
-    for (const InvBucket& b : p.buckets) t += inv_tiles(kind, b.nb, step) * b.count;
+    for (const InvBucket& b : p.buckets) t += inv_tiles(kind, b.nb, step, rowq) * b.count;
     return t;
 }
 
@@ -583,7 +586,7 @@ kfac_status_t kfac_damped_inverse(int n, const float* const* x, const int64_t* d
                                  stream);
     if (e != hipSuccess) return KFAC_ERR_HIP;
 
-    InvLaunch L{mats_dev, buckets_dev, (int32_t)p.buckets.size(), 0, (double)gamma, 0, 0, 0, 0, fused ? 1 : 0, 0};
+    InvLaunch L{mats_dev, buckets_dev, (int32_t)p.buckets.size(), 0, (double)gamma, 0, 0, 0, 0, fused ? 1 : 0, 0, 1, 0};
     int last_pass = 0;   // rows below the last trailing update hold the updates of panels [0, last_pass)
     e = launch_inv_prepare(L, bucket_tiles(p, kInvPrepare, 0), stream);
     // with V formed beside potrf, two more launches finish its last columns
@@ -594,9 +597,6 @@ kfac_status_t kfac_damped_inverse(int n, const float* const* x, const int64_t* d
         // from a multiple of 8
         L.step = k;
         L.plo = last_pass;
-        L.split = bucket_tiles(p, kInvPanel, k);
-        L.fin_end = L.split + (fused ? bucket_tiles(p, kInvVFin, k) : 0);
-        L.part_end = L.fin_end + (fused ? bucket_tiles(p, kInvVPart, k) : 0);
         // A heavy trailing update (it rewrites its blocks in full) runs only
         // every second or third step, two or three panels deep; the rows in
         // between take the skipped panels themselves.  A step with no
@@ -606,6 +606,16 @@ kfac_status_t kfac_damped_inverse(int n, const float* const* x, const int64_t* d
         static_assert(kMaxPassDepth >= 3, "three-panel updates");
         if (k - last_pass >= depth || trail == 0) last_pass = k;
         else trail = 0;
+        // Every row workgroup factors the diagonal block itself.  In a step
+        // without a trailing update, more row blocks than resident slots
+        // would take several rounds of that factorisation; there each
+        // workgroup takes rowq consecutive blocks of the row instead, so
+        // that one round holds them all.
+        const int64_t rows1 = bucket_tiles(p, kInvPanel, k);
+        L.rowq = trail == 0 && !fused ? (int32_t)std::max<int64_t>(1, ceil_div(rows1, kInvRowSlots)) : 1;
+        L.split = bucket_tiles(p, kInvPanel, k, L.rowq);
+        L.fin_end = L.split + (fused ? bucket_tiles(p, kInvVFin, k) : 0);
+        L.part_end = L.fin_end + (fused ? bucket_tiles(p, kInvVPart, k) : 0);
         L.tail_first = trail > 0 ? (L.part_end + 7) / 8 * 8 : L.part_end;
         if (L.tail_first + trail > 0) e = launch_inv_step(L, L.tail_first + trail, stream);
     }
