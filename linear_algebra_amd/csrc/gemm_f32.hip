@@ -472,16 +472,25 @@ __device__ __forceinline__ void gemm_bf16_reg_tile(const GemmLaunch& L, const Ti
 // lane; two transposing LDS reads (ds_read_b64_tr_b16) assemble them: in a
 // group of 16 lanes, lane p points at k-row k0 + p/4, columns mb + 4 (p % 4),
 // and lane i receives column mb + i of rows k0 .. k0 + 3.  The 16-byte chunks
-// of row k sit at position c xor 2 (k % 4), so the 8 chunks a group reads
-// fall on distinct banks.
+// of row k sit at position c xor swz(k % 4), swz = 0, 6, 12, 10: the two
+// groups of a half-wave read chunks c0 .. c0 + 3 (c0 a multiple of 4) of
+// four consecutive rows, which then fall on four disjoint quarters of a
+// 256-byte bank line (bits 2-3 of the position differ), and each group's
+// two chunks per row on four disjoint quarters of a 128-byte line (bits
+// 1-2 differ).  With c xor 2 (k % 4) the rows paired up on the same banks
+// (half of the LDS cycles were conflicts).
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef short short8v __attribute__((ext_vector_type(8)));
 constexpr int SLAB16 = BK16 * BM;                  // bf16 per staged slab (8 KB)
 constexpr int kSlab16Copies = SLAB16 / (8 * NT);   // copy instructions per wave and slab (2)
 static_assert(kSlab16Copies * 8 * NT == SLAB16, "a slab is a whole number of 16-byte copies per lane");
 
+__device__ __forceinline__ int tr_swz(int k) {
+    const int x = k & 3;
+    return (2 * x) ^ (4 * x);
+}
 __device__ __forceinline__ int tr_at(int k, int m) {
-    return k * BM + ((((m >> 3) ^ (2 * (k & 3))) << 3) | (m & 7));
+    return k * BM + ((((m >> 3) ^ tr_swz(k)) << 3) | (m & 7));
 }
 
 __device__ __forceinline__ void stage_slab16(uint16_t* S, __amdgpu_buffer_rsrc_t r,
@@ -523,28 +532,123 @@ __device__ __forceinline__ void mma_slab16(floatx16 (&acc)[2][2], const uint16_t
     }
 }
 
+// mma_slab16 with the LDS reads written out, for the ring below.  The
+// compiler, which cannot follow which ring buffer each copy in flight
+// targets across the loop, would otherwise wait for every copy before the
+// reads of one of the buffers.  It then also does not track these reads,
+// so the waits before the products that use them are explicit: the reads
+// of step 0 and the A fragments of step 1 are issued, then (12 in flight)
+// lgkmcnt(4) before step 0's products, the B fragments of step 1, and
+// lgkmcnt(0) before step 1's.  The wait takes the fragments as operands, so
+// no product moves above it.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)reinterpret_cast<uintptr_t>(p); }
+__device__ __forceinline__ short4v tr_read(uint32_t a) {
+    short4v v;
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(a));
+    return v;
+}
+__device__ __forceinline__ void mma_slab16_ring(floatx16 (&acc)[2][2], const uint16_t* A, const uint16_t* Bm, int wm,
+                                                int wn, int lane) {
+    const int g = lane >> 4, p = lane & 15;
+    // lane p of a group reads k-rows k0 + p/4 and k0 + 4 + p/4, columns mb + 4 (p % 4)
+    auto addr = [&](const uint16_t* S, int k0, int mb) { return lds_addr(S + tr_at(k0 + (p >> 2), mb + 4 * (p & 3))); };
+    auto addr_hi = [&](const uint16_t* S, int k0, int mb) {
+        return lds_addr(S + tr_at(k0 + 4 + (p >> 2), mb + 4 * (p & 3)));
+    };
+    short4v fa[2][2][2], fb[2][2][2];   // [step][block][lo/hi]
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+        const int k0 = 16 * st + 8 * (g >> 1);
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+            const int mb = wm * 64 + a * 32 + 16 * (g & 1);
+            fa[st][a][0] = tr_read(addr(A, k0, mb));
+            fa[st][a][1] = tr_read(addr_hi(A, k0, mb));
+        }
+        if (st == 0) {
+#pragma unroll
+            for (int a = 0; a < 2; ++a) {
+                const int nb = wn * 64 + a * 32 + 16 * (g & 1);
+                fb[0][a][0] = tr_read(addr(Bm, k0, nb));
+                fb[0][a][1] = tr_read(addr_hi(Bm, k0, nb));
+            }
+        }
+    }
+    asm volatile("s_waitcnt lgkmcnt(4)"
+                 : "+v"(fa[0][0][0]), "+v"(fa[0][0][1]), "+v"(fa[0][1][0]), "+v"(fa[0][1][1]), "+v"(fb[0][0][0]),
+                   "+v"(fb[0][0][1]), "+v"(fb[0][1][0]), "+v"(fb[0][1][1]));
+    {
+        const int k0 = 16 + 8 * (g >> 1);
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+            const int nb = wn * 64 + a * 32 + 16 * (g & 1);
+            fb[1][a][0] = tr_read(addr(Bm, k0, nb));
+            fb[1][a][1] = tr_read(addr_hi(Bm, k0, nb));
+        }
+    }
+    auto frag = [](const short4v& lo, const short4v& hi) {
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+        if (st == 1)
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(fa[1][0][0]), "+v"(fa[1][0][1]), "+v"(fa[1][1][0]), "+v"(fa[1][1][1]),
+                           "+v"(fb[1][0][0]), "+v"(fb[1][0][1]), "+v"(fb[1][1][0]), "+v"(fb[1][1][1]));
+        const bf16x8 a0 = frag(fa[st][0][0], fa[st][0][1]), a1 = frag(fa[st][1][0], fa[st][1][1]);
+        const bf16x8 b0 = frag(fb[st][0][0], fb[st][0][1]), b1 = frag(fb[st][1][0], fb[st][1][1]);
+        acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc[0][0], 0, 0, 0);
+        acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc[0][1], 0, 0, 0);
+        acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc[1][0], 0, 0, 0);
+        acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc[1][1], 0, 0, 0);
+    }
+}
+
+// Slabs in flight: at 128 x 128 bf16 tiles a slab feeds the matrix cores for
+// only a few hundred cycles, less than a copy takes to arrive, so the slabs
+// go through a ring of kRing16 buffers: while slab s is multiplied, the
+// copies of slabs s + 1 .. s + kRing16 - 1 are in flight.
+constexpr int kRing16 = 4;
+
+// vmcnt(n) alone (expcnt and lgkmcnt left at their maximum)
+__device__ __forceinline__ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// A barrier that waits only for the workgroup's LDS accesses, so that the
+// copies of later slabs stay in flight (__syncthreads() would wait for all
+// of them).  The memory clobber keeps LDS accesses on their side of it.
+__device__ __forceinline__ void lds_barrier16() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+}
+
+// The ring: one LDS array per buffer (A's slab, then B's), so that the
+// compiler can tell the copies into one buffer from the reads of another
+// and waits for no copy it need not.
+struct Ring16 {
+    uint16_t* s[kRing16];
+};
+
 template <bool SAME>
-__device__ __forceinline__ void gemm_bf16_lds_tile(const GemmLaunch& L, const TileWork& W, uint16_t* A0, uint16_t* A1,
-                                               uint16_t* B0, uint16_t* B1) {
+__device__ __forceinline__ void gemm_bf16_lds_tile(const GemmLaunch& L, const TileWork& W, const Ring16& R) {
     const GemmProb& P = W.P;
     const int k_begin = W.k_begin, k_end = W.k_end;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const bool active = W.active;
-    uint16_t* const Bb0 = SAME ? A0 : B0;
-    uint16_t* const Bb1 = SAME ? A1 : B1;
     uint32_t offa[kSlab16Copies], offb[kSlab16Copies];
 #pragma unroll
     for (int s = 0; s < kSlab16Copies; ++s) {
         const int q = (kSlab16Copies * wave + s) * 64 + lane;
-        const int k = q >> 4, c = (q & 15) ^ (2 * (k & 3)), m = 8 * c;   // this copy's row and columns
+        const int k = q >> 4, c = (q & 15) ^ tr_swz(k), m = 8 * c;   // this copy's row and columns
         offa[s] = (W.m0 + m < P.M) ? (uint32_t)((k * P.lda + W.m0 + m) * 2) : kOOB;
         offb[s] = (W.n0 + m < P.N) ? (uint32_t)((k * P.ldb + W.n0 + m) * 2) : kOOB;
     }
-    auto stage = [&](uint16_t* SA, uint16_t* SB, int k0) {
-        stage_slab16(SA, slab_rsrc(P.a, P.lda, k0, k_end, 2, P.M), offa);
-        if (!SAME) stage_slab16(SB, slab_rsrc(P.b, P.ldb, k0, k_end, 2, P.N), offb);
+    auto stage = [&](int buf, int k0) {
+        stage_slab16(R.s[buf], slab_rsrc(P.a, P.lda, k0, k_end, 2, P.M), offa);
+        if (!SAME) stage_slab16(R.s[buf] + SLAB16, slab_rsrc(P.b, P.ldb, k0, k_end, 2, P.N), offb);
     };
+    // copy instructions of one slab, per wave
+    constexpr int CPS = kSlab16Copies * (SAME ? 1 : 2);
     floatx16 acc[2][2], sum[2][2];
 #pragma unroll
     for (int a = 0; a < 2; ++a)
@@ -566,44 +670,69 @@ __device__ __forceinline__ void gemm_bf16_lds_tile(const GemmLaunch& L, const Ti
         }
     };
     const int nstages = (k_end - k_begin + BK16 - 1) / BK16;
-    if (nstages > 0) stage(A0, B0, k_begin);
-    for (int st = 0; st < nstages; st += 2) {
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (st + 1 < nstages) stage(A1, B1, k_begin + (st + 1) * BK16);
-        if (active) {
-            mma_slab16(acc, A0, Bb0, wm, wn, lane);
-            fold(st, nstages);
-        }
-        if (st + 1 >= nstages) break;
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (st + 2 < nstages) stage(A0, B0, k_begin + (st + 2) * BK16);
-        if (active) {
-            mma_slab16(acc, A1, Bb1, wm, wn, lane);
-            fold(st + 1, nstages);
+#pragma unroll
+    for (int s = 0; s < kRing16 - 1; ++s)
+        if (s < nstages) stage(s, k_begin + s * BK16);
+    for (int st = 0; st < nstages; st += kRing16) {
+#pragma unroll
+        for (int r = 0; r < kRing16; ++r) {
+            const int cur = st + r;
+            if (cur < nstages) {
+                // slab cur has arrived once no more than the copies of the
+                // slabs after it that are already issued are outstanding
+                const int after = min(kRing16 - 2, nstages - 1 - cur);
+                static_assert(kRing16 == 4, "the waits below cover up to two later slabs");
+                if (after >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * CPS));
+                else if (after == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(CPS));
+                else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+                // the slab is visible to every wave, and the buffer of the
+                // slab before it, which the next copies overwrite, is read
+                lds_barrier16();
+                if (cur + kRing16 - 1 < nstages) stage((r + kRing16 - 1) % kRing16, k_begin + (cur + kRing16 - 1) * BK16);
+                if (active) {
+                    mma_slab16_ring(acc, R.s[r], R.s[r] + (SAME ? 0 : SLAB16), wm, wn, lane);
+                    fold(cur, nstages);
+                }
+            }
         }
     }
     store_tile(P, L, sum, W.kc, W.t, W.m0, W.n0, wm, wn, lane);
 }
 
-// Rows whose starts are all 4-byte aligned (an even row pitch and an
-// aligned base) take the copy path; others are loaded element by element.
+// Inputs whose rows all start 4-byte aligned (an even row pitch and an
+// aligned base: after the repack, every input) take the copy path.  A launch
+// with any other input uses the second kernel, which also holds the register
+// path that loads elements one at a time (and, with its larger LDS, runs one
+// workgroup per CU).
 __global__ __launch_bounds__(NT, 2) void factor_bf16_kernel(GemmLaunch L, int64_t items) {
+    __shared__ __attribute__((aligned(16))) uint16_t S0[2 * SLAB16];
+    __shared__ __attribute__((aligned(16))) uint16_t S1[2 * SLAB16];
+    __shared__ __attribute__((aligned(16))) uint16_t S2[2 * SLAB16];
+    __shared__ __attribute__((aligned(16))) uint16_t S3[2 * SLAB16];
+    const int64_t item = L.runs ? xcd_runs<kGemmRun>(blockIdx.x) : xcd_remap(blockIdx.x, gridDim.x);
+    if (item >= items) return;
+    const TileWork W = decode_item(L, item);
+    const Ring16 R{{S0, S1, S2, S3}};
+    if (W.same) gemm_bf16_lds_tile<true>(L, W, R);
+    else gemm_bf16_lds_tile<false>(L, W, R);
+}
+
+__global__ __launch_bounds__(NT, 1) void factor_bf16_any_kernel(GemmLaunch L, int64_t items) {
     __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDK16];
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BM * LDK16];
-    __shared__ __attribute__((aligned(16))) uint16_t A0[SLAB16];
-    __shared__ __attribute__((aligned(16))) uint16_t A1[SLAB16];
-    __shared__ __attribute__((aligned(16))) uint16_t B0[SLAB16];
-    __shared__ __attribute__((aligned(16))) uint16_t B1[SLAB16];
+    __shared__ __attribute__((aligned(16))) uint16_t S0[2 * SLAB16];
+    __shared__ __attribute__((aligned(16))) uint16_t S1[2 * SLAB16];
+    __shared__ __attribute__((aligned(16))) uint16_t S2[2 * SLAB16];
+    __shared__ __attribute__((aligned(16))) uint16_t S3[2 * SLAB16];
     const int64_t item = L.runs ? xcd_runs<kGemmRun>(blockIdx.x) : xcd_remap(blockIdx.x, gridDim.x);
     if (item >= items) return;
     const TileWork W = decode_item(L, item);
     const GemmProb& P = W.P;
     const bool copy = ((P.lda | P.ldb) & 1) == 0 && (((uintptr_t)P.a | (uintptr_t)P.b) & 3) == 0;
+    const Ring16 R{{S0, S1, S2, S3}};
     if (!copy) gemm_bf16_reg_tile(L, W, As, Bs);
-    else if (W.same) gemm_bf16_lds_tile<true>(L, W, A0, A1, B0, B1);
-    else gemm_bf16_lds_tile<false>(L, W, A0, A1, B0, B1);
+    else if (W.same) gemm_bf16_lds_tile<true>(L, W, R);
+    else gemm_bf16_lds_tile<false>(L, W, R);
 }
 
 // Sums the split-K partial tiles in chunk order and applies the epilogue.
@@ -655,7 +784,8 @@ __global__ __launch_bounds__(NT) void precond_reduce_kernel(GemmLaunch L, int64_
 
 }  // namespace
 
-hipError_t launch_gemm(const GemmLaunch& L, int64_t items, hipStream_t stream, bool bf16, bool factor) {
+hipError_t launch_gemm(const GemmLaunch& L, int64_t items, hipStream_t stream, bool bf16, bool factor,
+                       bool bf16_aligned) {
     if (items <= 0) return hipSuccess;
     // Items of different problems differ in cost (K chunks of different
     // length, diagonal tiles with an idle wave).  Large launches hand items to
@@ -666,7 +796,10 @@ hipError_t launch_gemm(const GemmLaunch& L, int64_t items, hipStream_t stream, b
     R.runs = items >= kGemmRunsMin ? 1 : 0;
     const int64_t grid = R.runs ? (items + 8 * kGemmRun - 1) / (8 * kGemmRun) * (8 * kGemmRun) : items;
     if (bf16) {
-        hipLaunchKernelGGL(factor_bf16_kernel, dim3((unsigned)grid), dim3(NT), 0, stream, R, items);
+        if (bf16_aligned)
+            hipLaunchKernelGGL(factor_bf16_kernel, dim3((unsigned)grid), dim3(NT), 0, stream, R, items);
+        else
+            hipLaunchKernelGGL(factor_bf16_any_kernel, dim3((unsigned)grid), dim3(NT), 0, stream, R, items);
     } else if (factor) {
         hipLaunchKernelGGL(factor_f32_kernel, dim3((unsigned)grid), dim3(NT), 0, stream, R, items);
     } else {

@@ -66,8 +66,10 @@ struct GemmLaunch {
 // C = alpha Aop^T Bop on 128 x 128 tiles (float32 operands, or bfloat16
 // operands when `bf16`), then, for split K, the partials summed in chunk
 // order and the epilogue.  `factor` picks the kernel names of the factor
-// stage (else those of the preconditioning products).
-hipError_t launch_gemm(const GemmLaunch& L, int64_t items, hipStream_t stream, bool bf16, bool factor);
+// stage (else those of the preconditioning products); `bf16_aligned` says
+// that every bf16 operand row starts on a 4-byte boundary.
+hipError_t launch_gemm(const GemmLaunch& L, int64_t items, hipStream_t stream, bool bf16, bool factor,
+                       bool bf16_aligned = true);
 hipError_t launch_gemm_reduce(const GemmLaunch& L, int64_t tiles, hipStream_t stream, bool factor);
 
 // An odd-width bf16 input copied to a pitch that is a multiple of 8 elements
