@@ -66,6 +66,30 @@ __device__ __forceinline__ void column_decode(int64_t t, int& i, int& j) {
     i = (int)(t - r * (r + 1) / 2);
 }
 
+// Banded enumeration of the upper triangle (i <= j) of a T x T grid: bands
+// of `band` rows, column by column within a band (the band's first `band`
+// columns form a triangle), so that band^2 consecutive entries form about
+// a band x band block.  t in [0, T(T+1)/2); a band occupies the same range
+// of t as its rows do in row-major order.
+__device__ __forceinline__ void upper_band_decode(int64_t t, int64_t T, int band, int& i, int& j) {
+    int ir, jr;
+    upper_decode(t, T, ir, jr);   // the row-major position gives the band
+    const int64_t i0 = (int64_t)(ir / band) * band;
+    const int64_t r = min<int64_t>(band, T - i0);
+    const int64_t u = t - (i0 * T - i0 * (i0 - 1) / 2);
+    const int64_t tri = r * (r + 1) / 2;
+    if (u < tri) {
+        int a, c;
+        column_decode(u, a, c);
+        i = (int)(i0 + a);
+        j = (int)(i0 + c);
+    } else {
+        const int64_t v = u - tri;
+        i = (int)(i0 + v % r);
+        j = (int)(i0 + r + v / r);
+    }
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
 
 }  // namespace kfac

@@ -145,23 +145,7 @@ constexpr int kBand = 4;
 static_assert(kBand * kBand == kGemmRun, "an XCD run is one block of tiles");
 __device__ __forceinline__ void tile_decode(const GemmProb& P, int64_t t, int& ti, int& tj) {
     if (P.mode == kModeFactor) {
-        const int64_t T = P.tiles_m;
-        int ir, jr;
-        upper_decode(t, T, ir, jr);   // the row-major position gives the band
-        const int64_t i0 = (int64_t)(ir / kBand) * kBand;
-        const int64_t r = min<int64_t>(kBand, T - i0);
-        const int64_t u = t - (i0 * T - i0 * (i0 - 1) / 2);
-        const int64_t tri = r * (r + 1) / 2;
-        if (u < tri) {
-            int a, c;
-            column_decode(u, a, c);
-            ti = (int)(i0 + a);
-            tj = (int)(i0 + c);
-        } else {
-            const int64_t v = u - tri;
-            ti = (int)(i0 + v % r);
-            tj = (int)(i0 + r + v / r);
-        }
+        upper_band_decode(t, P.tiles_m, kBand, ti, tj);
     } else {
         const int64_t i0 = t / ((int64_t)kBand * P.tiles_n) * kBand;
         const int64_t r = min<int64_t>(kBand, P.tiles_m - i0);
