@@ -310,6 +310,7 @@ __host__ __device__ inline int64_t inv_tiles(int kind, int64_t nb, int64_t step,
 
 hipError_t launch_inv_prepare(const InvLaunch& L, int64_t tiles, hipStream_t s);
 hipError_t launch_inv_step(const InvLaunch& L, int64_t tiles, hipStream_t s);
+hipError_t launch_inv_trail(const InvLaunch& L, int64_t tiles, hipStream_t stream);
 hipError_t launch_inv_trtri_a(const InvLaunch& L, int64_t tiles, hipStream_t s);
 hipError_t launch_inv_trtri_b(const InvLaunch& L, int64_t tiles, hipStream_t s);
 hipError_t launch_inv_lauum(const InvLaunch& L, int64_t tiles, hipStream_t s);

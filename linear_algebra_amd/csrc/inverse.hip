@@ -856,6 +856,31 @@ __device__ __forceinline__ bool trtri_decode(int64_t local, int nb, int step, in
 
 constexpr int KT = 16;   // k-columns per staged piece in the triangular-inverse products
 
+// The trailing update of a step as a launch of its own: quarters of 16
+// k-columns (32 KB of staging) and few registers, so four workgroups share a
+// CU, against two for the step kernel.
+__global__ __launch_bounds__(NT, 4) void inv_trail_kernel(InvLaunch L, int64_t tiles) {
+    __shared__ __attribute__((aligned(16))) double S0[2 * B * KT], S1[2 * B * KT];
+    const Stage S{S0, S1};
+    int mi;
+    int64_t local;
+    const int64_t item = xcd_remap(blockIdx.x, gridDim.x);
+    if (!locate(L, kInvSyrk, item, mi, local)) return;
+    const InvMat M = L.mats[mi];
+    const int k = L.step;
+    const int T = M.nb - k - 1;
+    int a, c;
+    upper_decode(local, T, a, c);
+    const int I = k + 1 + a, J = k + 1 + c;
+    const int64_t D = (int64_t)M.nb * B;
+    double* Wij = M.w + (int64_t)I * B * D + (int64_t)J * B;
+    doublex4 acc[2][2];
+    acc_load(acc, Wij, D);
+    block_gemm<KT>(acc, S, L.plo, k, [&](int t) { return Blk{M.w + (int64_t)t * B * D + (int64_t)I * B, D, true}; },
+                   [&](int t) { return Blk{M.w + (int64_t)t * B * D + (int64_t)J * B, D, true}; }, true, I == J);
+    acc_store(acc, Wij, D);
+}
+
 // T_IJ = sum_{t in G2, t <= J} U_It V_tJ, parked in W's lower block (J, I).
 __global__ __launch_bounds__(NT, 4) void inv_trtri_a_kernel(InvLaunch L, int64_t tiles) {
     // quarters of 16 k-columns (a 32 KB staging area): four workgroups share a CU
@@ -1130,6 +1155,7 @@ hipError_t launch(K kernel, const InvLaunch& L, int64_t tiles, hipStream_t s, bo
 
 hipError_t launch_inv_prepare(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_prepare_kernel, L, t, s); }
 hipError_t launch_inv_step(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_step_kernel, L, t, s); }
+hipError_t launch_inv_trail(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_trail_kernel, L, t, s); }
 hipError_t launch_inv_trtri_a(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_trtri_a_kernel, L, t, s, true); }
 hipError_t launch_inv_trtri_b(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_trtri_b_kernel, L, t, s, true); }
 hipError_t launch_inv_lauum(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_lauum_kernel, L, t, s, true); }

@@ -265,6 +265,9 @@ constexpr int64_t kPass3Tiles = 8192;
 // Resident step-kernel workgroups (two per CU): the target count of row
 // workgroups in a step without a trailing update.
 constexpr int64_t kInvRowSlots = 512;
+// Trailing updates of at least this many blocks (over several panels) get a
+// launch of their own.
+constexpr int64_t kApartTiles = 8192;
 
 int64_t bucket_tiles(const InvPlan& p, int kind, int step, int rowq = 1);
 
@@ -624,8 +627,18 @@ kfac_status_t kfac_damped_inverse(int n, const float* const* x, const int64_t* d
         L.split = bucket_tiles(p, kInvPanel, k, L.rowq);
         L.fin_end = L.split + (fused ? bucket_tiles(p, kInvVFin, k) : 0);
         L.part_end = L.fin_end + (fused ? bucket_tiles(p, kInvVPart, k) : 0);
+        // Large multi-panel trailing updates run as a launch of their own, at
+        // four workgroups per CU (the step kernel holds two), before the
+        // step's launch; smaller ones stay in it, beside its row workgroups,
+        // whose chain would otherwise stand alone.  The two touch disjoint
+        // blocks: rows below k, against row k and the panels above it.
+        const bool apart = trail >= kApartTiles && k - L.plo > 1;
+        if (apart) {
+            e = launch_inv_trail(L, trail, stream);
+            trail = 0;
+        }
         L.tail_first = trail > 0 ? (L.part_end + 7) / 8 * 8 : L.part_end;
-        if (L.tail_first + trail > 0) e = launch_inv_step(L, L.tail_first + trail, stream);
+        if (e == hipSuccess && L.tail_first + trail > 0) e = launch_inv_step(L, L.tail_first + trail, stream);
     }
     for (int lvl = 0; !fused && e == hipSuccess && (1 << lvl) < p.nbmax; ++lvl) {   // bottom level first
         L.step = lvl;
