@@ -221,9 +221,10 @@ struct InvLaunch {
     int64_t fin_end;      // potrf step launch: [split, fin_end) finish a column of V
     int64_t part_end;     // potrf step launch: [fin_end, part_end) partial sums of the next column
     int32_t vlow;         // V_ic is kept in block (c, i) below the diagonal (formed beside potrf), not in (i, c)
-    int32_t plo;          // potrf step launch: row k and the trailing update apply panels [plo, k)
+    int32_t plo;          // potrf step launch: the trailing update (and the next row) apply panels [plo, k)
     int32_t rowq;         // potrf step launch: blocks of row k per row workgroup (>= 1)
-    int32_t pad_;
+    int32_t rplo;         // potrf step launch: row k applies panels [rplo, k)
+    int64_t next_end;     // potrf step launch: [part_end, next_end) update row k + 1 with panels [plo, k)
 };
 // At most this many panels per trailing update (k - plo).
 constexpr int kMaxPassDepth = 3;
@@ -233,7 +234,7 @@ constexpr int kMaxPassDepth = 3;
 // sizes the grids, and the kernels, which decode their tile index.
 enum InvKind : int32_t {
     kInvPrepare = 0, kInvPanel = 1, kInvSyrk = 2, kInvTrtri = 3, kInvLauum = 4,
-    kInvVPart = 6, kInvVFin = 7, kInvBorder = 8, kInvBorderRun = 9
+    kInvVPart = 6, kInvVFin = 7, kInvBorder = 8, kInvBorderRun = 9, kInvNextRow = 10
 };
 
 // V = U^-1 formed column by column beside the potrf steps (V U = I):
@@ -283,6 +284,8 @@ __host__ __device__ inline int64_t inv_tiles(int kind, int64_t nb, int64_t step,
             const int64_t right = nb - step - 1;
             return nb > step ? (right > rowq ? (right + rowq - 1) / rowq : 1) : 0;
         }
+        case kInvNextRow:  // the blocks (k + 1, j), j >= k + 1
+            return step + 1 < nb ? nb - step - 1 : 0;
         case kInvSyrk: {  // step k applies step k-1's update to blocks (i, j), k < i <= j
             const int64_t t = nb - step - 1;
             return step >= 1 && t > 0 ? t * (t + 1) / 2 : 0;

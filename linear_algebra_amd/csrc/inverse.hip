@@ -585,12 +585,12 @@ __device__ __forceinline__ void potrf_row_block(const InvLaunch& L, const InvMat
     // Blocks after the first (rowq > 1): each takes the panels [plo, k) in
     // turn and is written back; its solve, after the factorisation, reads it
     // again (the same threads read the elements they wrote).
-    for (int Jx = J + 1; Jx < Jend && L.plo < k; ++Jx) {
+    for (int Jx = J + 1; Jx < Jend && L.rplo < k; ++Jx) {
         double* Wkx = M.w + (int64_t)k * B * D + (int64_t)Jx * B;
         doublex4 wx[2][2];
         double xa[PER], xb[PER];
         acc_load(wx, Wkx, D);
-        for (int p = L.plo; p < k; ++p) {
+        for (int p = L.rplo; p < k; ++p) {
             fetch(xa, Blk{M.w + (int64_t)p * B * D + (int64_t)k * B, D, true});
             fetch(xb, Blk{M.w + (int64_t)p * B * D + (int64_t)Jx * B, D, true});
             put(As, xa, true);
@@ -601,15 +601,15 @@ __device__ __forceinline__ void potrf_row_block(const InvLaunch& L, const InvMat
         }
         acc_store(wx, Wkx, D);
     }
-    // Row k still lacks the updates of panels [plo, k) (one, or two where
-    // the trailing update runs every other step).  Every block this
+    // Row k still lacks the updates of panels [rplo, k) (at most
+    // kMaxPassDepth; one where the step before updated this row).  Every block this
     // workgroup reads first is requested before the first wait, the first
     // panel's blocks first.  The requests are unconditional (a branch around
     // them would end in a wait for all of them): without a block right of
     // the diagonal, or at step 0, they read blocks of the matrix that are
     // then not used.
     const int Jr = has_right ? J : k;
-    const int p0 = L.plo < k ? L.plo : 0;
+    const int p0 = L.rplo < k ? L.rplo : 0;
     double ra[PER], rb[PER];
     fetch(ra, Blk{M.w + (int64_t)p0 * B * D + (int64_t)k * B, D, true});
     fetch(rb, Blk{M.w + (int64_t)p0 * B * D + (int64_t)Jr * B, D, true});
@@ -626,7 +626,7 @@ __device__ __forceinline__ void potrf_row_block(const InvLaunch& L, const InvMat
     };
     if (p0 < k) update();
 #pragma unroll
-    for (int u = 1; u < kMaxPassDepth; ++u) {   // the host keeps k - plo <= kMaxPassDepth
+    for (int u = 1; u < kMaxPassDepth; ++u) {   // the host keeps k - rplo <= kMaxPassDepth
         if (p0 + u < k) {
             fetch(ra, Blk{M.w + (int64_t)(p0 + u) * B * D + (int64_t)k * B, D, true});
             fetch(rb, Blk{M.w + (int64_t)(p0 + u) * B * D + (int64_t)Jr * B, D, true});
@@ -767,6 +767,21 @@ __global__ __launch_bounds__(NT, 2) void inv_step_kernel(InvLaunch L, int64_t ti
     if (b < L.part_end) {
         if (!locate(L, kInvVPart, b - L.fin_end, mi, local)) return;
         v_partial(L, L.mats[mi], local, S);
+        return;
+    }
+    if (b < L.next_end) {
+        // block (k + 1, J) of the next row takes panels [plo, k) now, off the
+        // chain, so that its row workgroups at step k + 1 apply only panel k
+        if (!locate(L, kInvNextRow, b - L.part_end, mi, local)) return;
+        const InvMat M = L.mats[mi];
+        const int k = L.step, I = k + 1, J = k + 1 + (int)local;
+        const int64_t D = (int64_t)M.nb * B;
+        double* Wij = M.w + (int64_t)I * B * D + (int64_t)J * B;
+        doublex4 acc[2][2];
+        acc_load(acc, Wij, D);
+        block_gemm(acc, S, L.plo, k, [&](int t) { return Blk{M.w + (int64_t)t * B * D + (int64_t)I * B, D, true}; },
+                   [&](int t) { return Blk{M.w + (int64_t)t * B * D + (int64_t)J * B, D, true}; }, true, I == J);
+        acc_store(acc, Wij, D);
         return;
     }
     if (b < L.tail_first) return;

@@ -597,7 +597,8 @@ kfac_status_t kfac_damped_inverse(int n, const float* const* x, const int64_t* d
                                  stream);
     if (e != hipSuccess) return KFAC_ERR_HIP;
 
-    InvLaunch L{mats_dev, buckets_dev, (int32_t)p.buckets.size(), 0, (double)gamma, 0, 0, 0, 0, fused ? 1 : 0, 0, 1, 0};
+    InvLaunch L{mats_dev, buckets_dev, (int32_t)p.buckets.size(), 0, (double)gamma, 0, 0, 0, 0, fused ? 1 : 0, 0, 1, 0, 0};
+    bool next_done = false;   // the step before updated this step's row with its pending panels
     int last_pass = 0;   // rows below the last trailing update hold the updates of panels [0, last_pass)
     e = launch_inv_prepare(L, bucket_tiles(p, kInvPrepare, 0), stream);
     // with V formed beside potrf, two more launches finish its last columns
@@ -608,6 +609,7 @@ kfac_status_t kfac_damped_inverse(int n, const float* const* x, const int64_t* d
         // from a multiple of 8
         L.step = k;
         L.plo = last_pass;
+        L.rplo = next_done ? k - 1 : last_pass;
         // A heavy trailing update (it rewrites its blocks in full) runs only
         // every second or third step, two or three panels deep; the rows in
         // between take the skipped panels themselves.  A step with no
@@ -627,6 +629,13 @@ kfac_status_t kfac_damped_inverse(int n, const float* const* x, const int64_t* d
         L.split = bucket_tiles(p, kInvPanel, k, L.rowq);
         L.fin_end = L.split + (fused ? bucket_tiles(p, kInvVFin, k) : 0);
         L.part_end = L.fin_end + (fused ? bucket_tiles(p, kInvVPart, k) : 0);
+        // In a step without a trailing update, row k + 1 takes the panels
+        // [plo, k) that it lacks in this launch, beside (after) the row
+        // workgroups, instead of on the chain of the next step.  (Not where
+        // V is formed beside potrf: there the step launches are short and
+        // the extra workgroups cost more than they take off the chain.)
+        next_done = !fused && trail == 0 && k > L.plo && k + 1 < p.nbmax;
+        L.next_end = L.part_end + (next_done ? bucket_tiles(p, kInvNextRow, k) : 0);
         // Large multi-panel trailing updates run as a launch of their own, at
         // four workgroups per CU (the step kernel holds two), before the
         // step's launch; smaller ones stay in it, beside its row workgroups,
@@ -637,7 +646,7 @@ kfac_status_t kfac_damped_inverse(int n, const float* const* x, const int64_t* d
             e = launch_inv_trail(L, trail, stream);
             trail = 0;
         }
-        L.tail_first = trail > 0 ? (L.part_end + 7) / 8 * 8 : L.part_end;
+        L.tail_first = trail > 0 ? (L.next_end + 7) / 8 * 8 : L.next_end;
         if (e == hipSuccess && L.tail_first + trail > 0) e = launch_inv_step(L, L.tail_first + trail, stream);
     }
     for (int lvl = 0; !fused && e == hipSuccess && (1 << lvl) < p.nbmax; ++lvl) {   // bottom level first
