@@ -258,10 +258,13 @@ InvPlan plan_inverse(int n, const int64_t* d) {
 // are busy with the trailing update and V is formed afterwards by recursive
 // doubling, in launches of its own.
 constexpr int64_t kFuseTilesPerStep = 2048;
-// Trailing updates of at least this many blocks run every other step, two
-// panels deep, and of at least kPass3Tiles every third step.
+// Trailing updates of at least kPass2Tiles blocks run every second step
+// (two panels deep) where V is formed beside potrf, every kDeepPass2-th step
+// otherwise; of at least kPass3Tiles, every third or every kDeepPass3-th.
 constexpr int64_t kPass2Tiles = 1024;
 constexpr int64_t kPass3Tiles = 8192;
+constexpr int kDeepPass2 = 4;
+constexpr int kDeepPass3 = 8;
 // Resident step-kernel workgroups (two per CU): the target count of row
 // workgroups in a step without a trailing update.
 constexpr int64_t kInvRowSlots = 512;
@@ -611,12 +614,17 @@ kfac_status_t kfac_damped_inverse(int n, const float* const* x, const int64_t* d
         L.plo = last_pass;
         L.rplo = next_done ? k - 1 : last_pass;
         // A heavy trailing update (it rewrites its blocks in full) runs only
-        // every second or third step, two or three panels deep; the rows in
-        // between take the skipped panels themselves.  A step with no
-        // trailing blocks at all (no rows below it) counts as an update.
+        // every few steps, that many panels deep; the rows in between take the
+        // skipped panels from the next-row workgroups of the step before
+        // (below), and apply only the last panel themselves.  Where V is
+        // formed beside potrf there are no next-row workgroups, the rows
+        // apply every skipped panel, and the depth stays within
+        // kMaxPassDepth.  A step with no trailing blocks at all (no rows below
+        // it) counts as an update.
         int64_t trail = bucket_tiles(p, kInvSyrk, k);
-        const int depth = trail >= kPass3Tiles ? 3 : trail >= kPass2Tiles ? 2 : 1;
-        static_assert(kMaxPassDepth >= 3, "three-panel updates");
+        const int depth = fused ? (trail >= kPass3Tiles ? 3 : trail >= kPass2Tiles ? 2 : 1)
+                                : (trail >= kPass3Tiles ? kDeepPass3 : trail >= kPass2Tiles ? kDeepPass2 : 1);
+        static_assert(kMaxPassDepth >= 3, "three-panel updates where the rows apply every skipped panel");
         if (k - last_pass >= depth || trail == 0) last_pass = k;
         else trail = 0;
         // Every row workgroup factors the diagonal block itself.  In a step

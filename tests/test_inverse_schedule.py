@@ -7,8 +7,9 @@ only every second or third step where the trailing matrix is large, several
 panels at once), the row workgroups of step k applying the panels their row
 still lacks, and, in a step without a trailing update, workgroups that bring
 row k + 1 up to date.  This model follows the rules the host applies in
-`kfac_damped_inverse` (thresholds of 1024 and 8192 trailing blocks for two-
-and three-panel updates; V formed beside potrf or not) and checks the
+`kfac_damped_inverse` (thresholds of 1024 and 8192 trailing blocks: two- and
+three-panel updates where V is formed beside potrf, four and eight panels
+otherwise, where the next row is brought up to date each step) and checks the
 invariant the kernels rely on: when row k is factored it has received every
 panel p < k exactly once, and the row workgroups never apply more than three.
 """
@@ -17,6 +18,7 @@ import random
 import pytest
 
 PASS2_TILES, PASS3_TILES, MAX_DEPTH = 1024, 8192, 3
+DEEP_PASS2, DEEP_PASS3 = 4, 8   # update depths where the next row is brought up to date by the step before
 
 
 def syrk_tiles(nb, k):
@@ -39,7 +41,10 @@ def schedule_violation(nbs, fused):
                 if sorted(applied[m][k]) != list(range(k)):
                     return f"row {k} of matrix {m} (nb {nb}) holds panels {sorted(applied[m][k])}"
         trail = sum(syrk_tiles(nb, k) for nb in nbs)
-        depth = 3 if trail >= PASS3_TILES else 2 if trail >= PASS2_TILES else 1
+        if fused:
+            depth = 3 if trail >= PASS3_TILES else 2 if trail >= PASS2_TILES else 1
+        else:
+            depth = DEEP_PASS3 if trail >= PASS3_TILES else DEEP_PASS2 if trail >= PASS2_TILES else 1
         if k - last_pass >= depth or trail == 0:
             last_pass = k
         else:
