@@ -497,26 +497,7 @@ __device__ __forceinline__ bf16x8 tr_frag(const uint16_t* S, int k0, int mb, int
     return __builtin_bit_cast(bf16x8, v);
 }
 
-__device__ __forceinline__ void mma_slab16(floatx16 (&acc)[2][2], const uint16_t* A, const uint16_t* Bm, int wm,
-                                           int wn, int lane) {
-    const int g = lane >> 4, p = lane & 15;
-#pragma unroll
-    for (int s = 0; s < BK16 / 16; ++s) {
-        const int k0 = 16 * s + 8 * (g >> 1);
-        bf16x8 fa[2], fb[2];
-#pragma unroll
-        for (int a = 0; a < 2; ++a) {
-            fa[a] = tr_frag(A, k0, wm * 64 + a * 32 + 16 * (g & 1), p);
-            fb[a] = tr_frag(Bm, k0, wn * 64 + a * 32 + 16 * (g & 1), p);
-        }
-        acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0], fb[0], acc[0][0], 0, 0, 0);
-        acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0], fb[1], acc[0][1], 0, 0, 0);
-        acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1], fb[0], acc[1][0], 0, 0, 0);
-        acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1], fb[1], acc[1][1], 0, 0, 0);
-    }
-}
-
-// mma_slab16 with the LDS reads written out, for the ring below.  The
+// The products of a full wave, with the LDS reads written out, for the ring below.  The
 // compiler, which cannot follow which ring buffer each copy in flight
 // targets across the loop, would otherwise wait for every copy before the
 // reads of one of the buffers.  It then also does not track these reads,
@@ -588,6 +569,57 @@ __device__ __forceinline__ void mma_slab16_ring(floatx16 (&acc)[2][2], const uin
     }
 }
 
+// The products of a wave at the edge of a problem: NA x NB of its 32 x 32
+// blocks hold rows / columns of the problem (the others lie wholly past
+// them and are left at zero).  Reads written out as for a full wave, with
+// one wait per step (these waves are few).
+template <int NA, int NB>
+__device__ __forceinline__ void mma_slab16_edge(floatx16 (&acc)[2][2], const uint16_t* A, const uint16_t* Bm, int wm,
+                                                int wn, int lane) {
+    const int g = lane >> 4, p = lane & 15;
+    auto addr = [&](const uint16_t* S, int k0, int mb) { return lds_addr(S + tr_at(k0 + (p >> 2), mb + 4 * (p & 3))); };
+    auto addr_hi = [&](const uint16_t* S, int k0, int mb) {
+        return lds_addr(S + tr_at(k0 + 4 + (p >> 2), mb + 4 * (p & 3)));
+    };
+    auto frag = [](const short4v& lo, const short4v& hi) {
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+        const int k0 = 16 * st + 8 * (g >> 1);
+        short4v fa[2][2], fb[2][2];
+#pragma unroll
+        for (int a = 0; a < NA; ++a) {
+            const int mb = wm * 64 + a * 32 + 16 * (g & 1);
+            fa[a][0] = tr_read(addr(A, k0, mb));
+            fa[a][1] = tr_read(addr_hi(A, k0, mb));
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const int nb = wn * 64 + b * 32 + 16 * (g & 1);
+            fb[b][0] = tr_read(addr(Bm, k0, nb));
+            fb[b][1] = tr_read(addr_hi(Bm, k0, nb));
+        }
+        if constexpr (NA == 2 && NB == 2)
+            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fa[0][0]), "+v"(fa[0][1]), "+v"(fa[1][0]), "+v"(fa[1][1]),
+                         "+v"(fb[0][0]), "+v"(fb[0][1]), "+v"(fb[1][0]), "+v"(fb[1][1]));
+        else if constexpr (NA == 2)
+            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fa[0][0]), "+v"(fa[0][1]), "+v"(fa[1][0]), "+v"(fa[1][1]),
+                         "+v"(fb[0][0]), "+v"(fb[0][1]));
+        else if constexpr (NB == 2)
+            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fa[0][0]), "+v"(fa[0][1]), "+v"(fb[0][0]), "+v"(fb[0][1]),
+                         "+v"(fb[1][0]), "+v"(fb[1][1]));
+        else
+            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fa[0][0]), "+v"(fa[0][1]), "+v"(fb[0][0]), "+v"(fb[0][1]));
+#pragma unroll
+        for (int a = 0; a < NA; ++a)
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag(fa[a][0], fa[a][1]), frag(fb[b][0], fb[b][1]),
+                                                                    acc[a][b], 0, 0, 0);
+    }
+}
+
 // Slabs in flight: at 128 x 128 bf16 tiles a slab feeds the matrix cores for
 // only a few hundred cycles, less than a copy takes to arrive, so the slabs
 // go through a ring of kRing16 buffers: while slab s is multiplied, the
@@ -612,13 +644,19 @@ struct Ring16 {
     uint16_t* s[kRing16];
 };
 
-template <bool SAME>
+// EDGES: the launch has problems whose last tile row or column is partial
+// (their waves run only their valid blocks); without it every wave runs all four.
+template <bool SAME, bool EDGES>
 __device__ __forceinline__ void gemm_bf16_lds_tile(const GemmLaunch& L, const TileWork& W, const Ring16& R) {
     const GemmProb& P = W.P;
     const int k_begin = W.k_begin, k_end = W.k_end;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const bool active = W.active;
+    // a wave whose 64 rows or columns all lie past the problem's edge has
+    // nothing to compute; one whose second 32 do runs only its valid blocks
+    const int wr = W.m0 + 64 * wm, wc = W.n0 + 64 * wn;
+    const bool active = W.active && (!EDGES || (wr < P.M && wc < P.N));
+    const bool a2 = wr + 32 < P.M, b2 = wc + 32 < P.N, full = !EDGES || (a2 && b2);
     uint32_t offa[kSlab16Copies], offb[kSlab16Copies];
 #pragma unroll
     for (int s = 0; s < kSlab16Copies; ++s) {
@@ -674,7 +712,12 @@ __device__ __forceinline__ void gemm_bf16_lds_tile(const GemmLaunch& L, const Ti
                 lds_barrier16();
                 if (cur + kRing16 - 1 < nstages) stage((r + kRing16 - 1) % kRing16, k_begin + (cur + kRing16 - 1) * BK16);
                 if (active) {
-                    mma_slab16_ring(acc, R.s[r], R.s[r] + (SAME ? 0 : SLAB16), wm, wn, lane);
+                    const uint16_t* SA = R.s[r];
+                    const uint16_t* SB = R.s[r] + (SAME ? 0 : SLAB16);
+                    if (full) mma_slab16_ring(acc, SA, SB, wm, wn, lane);
+                    else if (a2) mma_slab16_edge<2, 1>(acc, SA, SB, wm, wn, lane);
+                    else if (b2) mma_slab16_edge<1, 2>(acc, SA, SB, wm, wn, lane);
+                    else mma_slab16_edge<1, 1>(acc, SA, SB, wm, wn, lane);
                     fold(cur, nstages);
                 }
             }
@@ -688,7 +731,8 @@ __device__ __forceinline__ void gemm_bf16_lds_tile(const GemmLaunch& L, const Ti
 // with any other input uses the second kernel, which also holds the register
 // path that loads elements one at a time (and, with its larger LDS, runs one
 // workgroup per CU).
-__global__ __launch_bounds__(NT, 2) void factor_bf16_kernel(GemmLaunch L, int64_t items) {
+template <bool EDGES>
+__device__ __forceinline__ void factor_bf16_item(const GemmLaunch& L, int64_t items) {
     __shared__ __attribute__((aligned(16))) uint16_t S0[2 * SLAB16];
     __shared__ __attribute__((aligned(16))) uint16_t S1[2 * SLAB16];
     __shared__ __attribute__((aligned(16))) uint16_t S2[2 * SLAB16];
@@ -697,9 +741,13 @@ __global__ __launch_bounds__(NT, 2) void factor_bf16_kernel(GemmLaunch L, int64_
     if (item >= items) return;
     const TileWork W = decode_item(L, item);
     const Ring16 R{{S0, S1, S2, S3}};
-    if (W.same) gemm_bf16_lds_tile<true>(L, W, R);
-    else gemm_bf16_lds_tile<false>(L, W, R);
+    if (W.same) gemm_bf16_lds_tile<true, EDGES>(L, W, R);
+    else gemm_bf16_lds_tile<false, EDGES>(L, W, R);
 }
+
+// Launches whose problems all have whole tiles skip the edge tests.
+__global__ __launch_bounds__(NT, 2) void factor_bf16_kernel(GemmLaunch L, int64_t items) { factor_bf16_item<false>(L, items); }
+__global__ __launch_bounds__(NT, 2) void factor_bf16_edge_kernel(GemmLaunch L, int64_t items) { factor_bf16_item<true>(L, items); }
 
 __global__ __launch_bounds__(NT, 1) void factor_bf16_any_kernel(GemmLaunch L, int64_t items) {
     __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDK16];
@@ -715,8 +763,8 @@ __global__ __launch_bounds__(NT, 1) void factor_bf16_any_kernel(GemmLaunch L, in
     const bool copy = ((P.lda | P.ldb) & 1) == 0 && (((uintptr_t)P.a | (uintptr_t)P.b) & 3) == 0;
     const Ring16 R{{S0, S1, S2, S3}};
     if (!copy) gemm_bf16_reg_tile(L, W, As, Bs);
-    else if (W.same) gemm_bf16_lds_tile<true>(L, W, R);
-    else gemm_bf16_lds_tile<false>(L, W, R);
+    else if (W.same) gemm_bf16_lds_tile<true, true>(L, W, R);
+    else gemm_bf16_lds_tile<false, true>(L, W, R);
 }
 
 // Sums the split-K partial tiles in chunk order and applies the epilogue.
@@ -769,7 +817,7 @@ __global__ __launch_bounds__(NT) void precond_reduce_kernel(GemmLaunch L, int64_
 }  // namespace
 
 hipError_t launch_gemm(const GemmLaunch& L, int64_t items, hipStream_t stream, bool bf16, bool factor,
-                       bool bf16_aligned) {
+                       bool bf16_aligned, bool bf16_edges) {
     if (items <= 0) return hipSuccess;
     // Items of different problems differ in cost (K chunks of different
     // length, diagonal tiles with an idle wave).  Large launches hand items to
@@ -780,8 +828,10 @@ hipError_t launch_gemm(const GemmLaunch& L, int64_t items, hipStream_t stream, b
     R.runs = items >= kGemmRunsMin ? 1 : 0;
     const int64_t grid = R.runs ? (items + 8 * kGemmRun - 1) / (8 * kGemmRun) * (8 * kGemmRun) : items;
     if (bf16) {
-        if (bf16_aligned)
+        if (bf16_aligned && !bf16_edges)
             hipLaunchKernelGGL(factor_bf16_kernel, dim3((unsigned)grid), dim3(NT), 0, stream, R, items);
+        else if (bf16_aligned)
+            hipLaunchKernelGGL(factor_bf16_edge_kernel, dim3((unsigned)grid), dim3(NT), 0, stream, R, items);
         else
             hipLaunchKernelGGL(factor_bf16_any_kernel, dim3((unsigned)grid), dim3(NT), 0, stream, R, items);
     } else if (factor) {

@@ -67,9 +67,10 @@ struct GemmLaunch {
 // operands when `bf16`), then, for split K, the partials summed in chunk
 // order and the epilogue.  `factor` picks the kernel names of the factor
 // stage (else those of the preconditioning products); `bf16_aligned` says
-// that every bf16 operand row starts on a 4-byte boundary.
+// that every bf16 operand row starts on a 4-byte boundary, `bf16_edges`
+// that some problem's order is not a multiple of the tile edge.
 hipError_t launch_gemm(const GemmLaunch& L, int64_t items, hipStream_t stream, bool bf16, bool factor,
-                       bool bf16_aligned = true);
+                       bool bf16_aligned = true, bool bf16_edges = true);
 hipError_t launch_gemm_reduce(const GemmLaunch& L, int64_t tiles, hipStream_t stream, bool factor);
 
 // An odd-width bf16 input copied to a pitch that is a multiple of 8 elements

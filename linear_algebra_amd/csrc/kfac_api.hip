@@ -496,13 +496,14 @@ kfac_status_t kfac_factors(int n, const void* const* x, const int64_t* rows, con
     // bf16 rows that all start 4-byte aligned (every input after the repack,
     // unless a base is one element off) take the kernel without the
     // element-wise path
-    bool aligned_rows = true;
+    bool aligned_rows = true, edges = false;
     for (int i = 0; i < n; ++i) {
         const GemmProb& g = p.probs[i];
         aligned_rows = aligned_rows && (g.lda & 1) == 0 && aligned(g.a, 4);
+        edges = edges || g.M % kGemmTile != 0;
     }
     GemmLaunch L{probs_dev, n, first_step ? 1 : 0, eps, 0, kGemmTile};
-    e = launch_gemm(L, p.items, stream, bf16, true, aligned_rows);
+    e = launch_gemm(L, p.items, stream, bf16, true, aligned_rows, edges);
     if (e != hipSuccess) return KFAC_ERR_HIP;
     return hip_status(launch_gemm_reduce(L, p.red_tiles, stream, true));
 }
