@@ -1,8 +1,10 @@
 // bfloat16 factor inputs of odd width: copied to a pitch that is a multiple
-// of 8 elements before the factor GEMM.  A row of odd width starts on a
+// of 64 elements before the factor GEMM.  A row of odd width starts on a
 // 2-byte boundary every other row, and the 16-byte copies that stage GEMM
 // slabs straight into LDS only read from 4-byte boundaries; after the copy
-// every row starts on a 16-byte boundary and the factor takes the copy path.
+// every row starts on a 128-byte cache line and the factor takes the copy
+// path, each 256-byte row segment of a slab then covering two whole lines
+// (from a 16-byte boundary it touches three).
 #include "device_common.h"
 #include "internal.h"
 
@@ -12,8 +14,8 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Repacks a bf16 input whose rows do not all start on 4-byte boundaries
-// (odd width) into a copy whose pitch is a multiple of 8 elements (16-byte
-// aligned rows), columns past the width zero.  Each thread writes one
+// (odd width) into a copy whose pitch is a multiple of 64 elements (rows on
+// 128-byte lines), columns past the width zero.  Each thread writes one
 // 16-byte group of 8 elements of one row, read as 20 bytes from the 4-byte
 // boundary at or below it and shifted into place.  Each layer has its own
 // range of workgroups, so a workgroup's rows all belong to one layer and

@@ -73,16 +73,17 @@ hipError_t launch_gemm(const GemmLaunch& L, int64_t items, hipStream_t stream, b
                        bool bf16_aligned = true, bool bf16_edges = true);
 hipError_t launch_gemm_reduce(const GemmLaunch& L, int64_t tiles, hipStream_t stream, bool factor);
 
-// An odd-width bf16 input copied to a pitch that is a multiple of 8 elements
-// (columns past d zero); 256 groups of 8 elements per workgroup.
+// An odd-width bf16 input copied to a pitch that is a multiple of 64 elements
+// (rows start on 128-byte lines; columns past d zero); 256 groups of 8
+// elements per workgroup.
 struct RepackLayer {
     const uint16_t* src;   // [rows][d]
-    uint16_t* dst;         // [rows][pitch], 16-byte aligned
+    uint16_t* dst;         // [rows][pitch], 256-byte aligned
     int64_t rows;
     int64_t block_begin;   // first workgroup of this layer
     int32_t d, pitch;
 };
-__host__ __device__ inline int64_t repack_pitch(int64_t d) { return (d + 7) / 8 * 8; }
+__host__ __device__ inline int64_t repack_pitch(int64_t d) { return (d + 63) / 64 * 64; }
 hipError_t launch_repack_bf16(const RepackLayer* layers, int n, int64_t blocks, hipStream_t stream);
 
 // ----------------------------------------------------------------- layers --
