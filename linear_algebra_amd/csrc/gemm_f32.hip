@@ -22,7 +22,9 @@
 // v_mfma_f32_32x32x16_bf16 takes 8 consecutive k-values per lane; rows of
 // odd width are first repacked to an aligned pitch (bf16_repack.hip), and
 // only an input of even width at a base one element off a 4-byte boundary
-// passes through registers, stored as [m][k].
+// passes through registers, stored as [m][k].  bf16 factor launches with K
+// unsplit, at most kWideMaxK rows and enough tiles take 256 x 128 tiles
+// (each wave 128 x 64), which read fewer LDS bytes per product.
 #include "device_common.h"
 #include "internal.h"
 
@@ -767,6 +769,281 @@ __global__ __launch_bounds__(NT, 1) void factor_bf16_any_kernel(GemmLaunch L, in
     else gemm_bf16_lds_tile<false, true>(L, W, R);
 }
 
+// Wide bfloat16 factor tiles: 256 rows x 128 columns, each wave 128 x 64
+// (4 x 2 blocks of 32 x 32).  The LDS serves about 128 bytes per clock per CU
+// (a probe of the transposing reads alone sustains 116); at 128 x 128 tiles
+// each product of a wave reads 1 KB of fragments and the slab copies write
+// another 0.5 KB into LDS per product, which caps the matrix cores near two
+// thirds of their rate.  A 128 x 64 wave reads 0.75 KB per product and the
+// copies write 0.375 KB.  Slabs are staged as for the 128 x 128 tiles
+// ([k][m] rows, 16-byte chunks swizzled by row): A's rows 256 columns long,
+// B's 128.  A tile that reaches the diagonal (J = 2 I or 2 I + 1) stages
+// only A and reads B's columns from it.  K is never split here and the sum
+// is not folded (at most kWideMaxK rows).  Three slabs in a ring: with 72 KB
+// of LDS and at most 256 registers per lane, two workgroups share a CU, so
+// that one's epilogue overlaps the other's products.
+constexpr int WM = kWideM, WN = kWideN;
+constexpr int SLAB_WA = BK16 * WM;                 // bf16 per A slab (16 KB)
+constexpr int SLAB_WB = BK16 * WN;                 // bf16 per B slab (8 KB)
+constexpr int kWideCopiesA = SLAB_WA / (8 * NT);   // copy instructions per wave and A slab (4)
+constexpr int kWideCopiesB = SLAB_WB / (8 * NT);   // and B slab (2)
+constexpr int kWideRing = 3;
+static_assert(kWideCopiesA * 8 * NT == SLAB_WA && kWideCopiesB * 8 * NT == SLAB_WB,
+              "a slab is a whole number of 16-byte copies per lane");
+static_assert(WM == 2 * WN, "a tile row spans two tile columns");
+
+struct RingW {
+    uint16_t* s[kWideRing];
+};
+
+// Position of element (k, m) in a staged slab whose rows hold LD columns.
+template <int LD>
+__device__ __forceinline__ int tr_at_ld(int k, int m) {
+    return k * LD + ((((m >> 3) ^ tr_swz(k)) << 3) | (m & 7));
+}
+
+// Both transposing reads of the fragment of the 32-wide block at column mb:
+// lane p of group g points at k-rows k0 + p/4 (lo) and k0 + 4 + p/4 (hi),
+// columns mb + 16 (g % 2) + 4 (p % 4).
+template <int LD>
+__device__ __forceinline__ void wide_frag_read(short4v (&f)[2], const uint16_t* S, int k0, int mb, int g, int p) {
+    const int m = mb + 16 * (g & 1) + 4 * (p & 3);
+    f[0] = tr_read(lds_addr(S + tr_at_ld<LD>(k0 + (p >> 2), m)));
+    f[1] = tr_read(lds_addr(S + tr_at_ld<LD>(k0 + 4 + (p >> 2), m)));
+}
+
+__device__ __forceinline__ bf16x8 wide_frag(const short4v (&f)[2]) {
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(f[0], f[1], 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// The products of one slab for a whole wave (A columns am .. am + 127 of
+// the A slab, B columns bn .. bn + 63 of the B slab).  At most 12 reads are
+// in flight: step 0's fragments of A blocks 0-1 and B, then of A blocks
+// 2-3; step 1's fragments follow as step 0's products free their turn.
+// Each wait names the fragments it covers, so that no product moves above
+// it.  With MASK, only the blocks whose bit (2 a + b) is set in `live` are
+// multiplied (the others lie wholly below the diagonal or past the
+// problem's edge; their fragments are read all the same).
+template <int LDA, int LDB, bool MASK>
+__device__ __forceinline__ void mma_wide(floatx16 (&acc)[4][2], const uint16_t* A, const uint16_t* B, int am, int bn,
+                                         int lane, uint32_t live) {
+    auto mfma = [&](int a, int b, const bf16x8& x, const bf16x8& y) {
+        if (!MASK || ((live >> (2 * a + b)) & 1u))
+            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, y, acc[a][b], 0, 0, 0);
+    };
+    const int g = lane >> 4, p = lane & 15;
+    const int k00 = 8 * (g >> 1), k01 = 16 + k00;
+    short4v fa0[4][2], fb0[2][2], fa1[4][2], fb1[2][2];
+    wide_frag_read<LDA>(fa0[0], A, k00, am, g, p);
+    wide_frag_read<LDA>(fa0[1], A, k00, am + 32, g, p);
+    wide_frag_read<LDB>(fb0[0], B, k00, bn, g, p);
+    wide_frag_read<LDB>(fb0[1], B, k00, bn + 32, g, p);
+    wide_frag_read<LDA>(fa0[2], A, k00, am + 64, g, p);
+    wide_frag_read<LDA>(fa0[3], A, k00, am + 96, g, p);
+    asm volatile("s_waitcnt lgkmcnt(4)"
+                 : "+v"(fa0[0][0]), "+v"(fa0[0][1]), "+v"(fa0[1][0]), "+v"(fa0[1][1]), "+v"(fb0[0][0]),
+                   "+v"(fb0[0][1]), "+v"(fb0[1][0]), "+v"(fb0[1][1]));
+    wide_frag_read<LDA>(fa1[0], A, k01, am, g, p);
+    wide_frag_read<LDA>(fa1[1], A, k01, am + 32, g, p);
+    wide_frag_read<LDB>(fb1[0], B, k01, bn, g, p);
+    wide_frag_read<LDB>(fb1[1], B, k01, bn + 32, g, p);
+    const bf16x8 b00 = wide_frag(fb0[0]), b01 = wide_frag(fb0[1]);
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+        const bf16x8 x = wide_frag(fa0[a]);
+        mfma(a, 0, x, b00);
+        mfma(a, 1, x, b01);
+    }
+    asm volatile("s_waitcnt lgkmcnt(8)" : "+v"(fa0[2][0]), "+v"(fa0[2][1]), "+v"(fa0[3][0]), "+v"(fa0[3][1]));
+    wide_frag_read<LDA>(fa1[2], A, k01, am + 64, g, p);
+    wide_frag_read<LDA>(fa1[3], A, k01, am + 96, g, p);
+#pragma unroll
+    for (int a = 2; a < 4; ++a) {
+        const bf16x8 x = wide_frag(fa0[a]);
+        mfma(a, 0, x, b00);
+        mfma(a, 1, x, b01);
+    }
+    asm volatile("s_waitcnt lgkmcnt(4)"
+                 : "+v"(fa1[0][0]), "+v"(fa1[0][1]), "+v"(fa1[1][0]), "+v"(fa1[1][1]), "+v"(fb1[0][0]),
+                   "+v"(fb1[0][1]), "+v"(fb1[1][0]), "+v"(fb1[1][1]));
+    const bf16x8 b10 = wide_frag(fb1[0]), b11 = wide_frag(fb1[1]);
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+        const bf16x8 x = wide_frag(fa1[a]);
+        mfma(a, 0, x, b10);
+        mfma(a, 1, x, b11);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fa1[2][0]), "+v"(fa1[2][1]), "+v"(fa1[3][0]), "+v"(fa1[3][1]));
+#pragma unroll
+    for (int a = 2; a < 4; ++a) {
+        const bf16x8 x = wide_frag(fa1[a]);
+        mfma(a, 0, x, b10);
+        mfma(a, 1, x, b11);
+    }
+}
+
+// Tile (I, J) of wide tile t of a problem (numbering of wide_tiles).
+__device__ __forceinline__ void wide_decode(int64_t t, int64_t ti, int64_t tj, int& I, int& J) {
+    int64_t b = 0;
+    while (2 * b + 2 < ti) {
+        const int64_t n = wide_band_tiles(b, ti, tj);
+        if (t < n) break;
+        t -= n;
+        ++b;
+    }
+    if (t < 2) {
+        I = (int)(2 * b);
+        J = (int)(4 * b + t);
+    } else if (2 * b + 1 < ti) {
+        I = (int)(2 * b + ((t - 2) & 1));
+        J = (int)(4 * b + 2 + (t - 2) / 2);
+    } else {
+        I = (int)(2 * b);
+        J = (int)(4 * b + t);
+    }
+}
+
+// SAME: the tile reaches the diagonal (B's columns lie inside A's).
+// EDGES: the launch has problems whose order is not a multiple of 256.
+template <bool SAME, bool EDGES>
+__device__ __forceinline__ void gemm_bf16_wide_tile(const GemmLaunch& L, const GemmProb& P, int m0, int n0,
+                                                    const RingW& R) {
+    const int K = P.K;
+    // the wave index is uniform: in a scalar register, so that the block
+    // mask below and the branches on it are scalar too
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int wr = m0 + 128 * wm, wc = n0 + 64 * wn;
+    // the wave's blocks (a, b) with an element on or above the diagonal and
+    // inside the problem; a wave with none has nothing to compute
+    uint32_t live = 0;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int r0 = wr + 32 * a, c0 = wc + 32 * b;
+            if ((!SAME || r0 <= c0 + 31) && (!EDGES || (r0 < P.M && c0 < P.N))) live |= 1u << (2 * a + b);
+        }
+    const bool active = live != 0;
+    uint32_t offa[kWideCopiesA], offb[kWideCopiesB];
+#pragma unroll
+    for (int s = 0; s < kWideCopiesA; ++s) {
+        const int q = (kWideCopiesA * wave + s) * 64 + lane;
+        const int k = q >> 5, c = (q & 31) ^ tr_swz(k), m = 8 * c;   // this copy's row and columns
+        offa[s] = (m0 + m < P.M) ? (uint32_t)((k * P.lda + m0 + m) * 2) : kOOB;
+    }
+#pragma unroll
+    for (int s = 0; s < kWideCopiesB; ++s) {
+        const int q = (kWideCopiesB * wave + s) * 64 + lane;
+        const int k = q >> 4, c = (q & 15) ^ tr_swz(k), m = 8 * c;
+        offb[s] = (n0 + m < P.N) ? (uint32_t)((k * P.ldb + n0 + m) * 2) : kOOB;
+    }
+    auto stage = [&](int buf, int k0) {
+        uint16_t* S = R.s[buf];
+        const __amdgpu_buffer_rsrc_t ra = slab_rsrc(P.a, P.lda, k0, K, 2, P.M);
+#pragma unroll
+        for (int s = 0; s < kWideCopiesA; ++s)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                ra, (__attribute__((address_space(3))) void*)(S + 512 * (kWideCopiesA * wave + s)), 16, offa[s], 0, 0,
+                0);
+        if (!SAME) {
+            const __amdgpu_buffer_rsrc_t rb = slab_rsrc(P.b, P.ldb, k0, K, 2, P.N);
+#pragma unroll
+            for (int s = 0; s < kWideCopiesB; ++s)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rb, (__attribute__((address_space(3))) void*)(S + SLAB_WA + 512 * (kWideCopiesB * wave + s)), 16,
+                    offb[s], 0, 0, 0);
+        }
+    };
+    constexpr int CPS = kWideCopiesA + (SAME ? 0 : kWideCopiesB);   // copy instructions of one slab, per wave
+    constexpr int LDB = SAME ? WM : WN;
+    const int am = 128 * wm, bn = (SAME ? n0 - m0 : 0) + 64 * wn;
+    floatx16 acc[4][2];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+    const int nstages = (K + BK16 - 1) / BK16;
+#pragma unroll
+    for (int s = 0; s < kWideRing - 1; ++s)
+        if (s < nstages) stage(s, s * BK16);
+    for (int st = 0; st < nstages; st += kWideRing) {
+#pragma unroll
+        for (int r = 0; r < kWideRing; ++r) {
+            const int cur = st + r;
+            if (cur < nstages) {
+                // slab cur has arrived once only the next slab's copies are outstanding
+                static_assert(kWideRing == 3, "one later slab in flight at the wait");
+                if (cur + 1 < nstages) __builtin_amdgcn_s_waitcnt(vmcnt_imm(CPS));
+                else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+                // the slab is visible to every wave, and the buffer of the
+                // slab before it, which the next copies overwrite, is read
+                lds_barrier16();
+                if (cur + kWideRing - 1 < nstages) stage((r + kWideRing - 1) % kWideRing, (cur + kWideRing - 1) * BK16);
+                if (active) {
+                    const uint16_t* SA = R.s[r];
+                    const uint16_t* SB = SAME ? SA : SA + SLAB_WA;
+                    mma_wide<WM, LDB, SAME || EDGES>(acc, SA, SB, am, bn, lane, live);
+                }
+            }
+        }
+    }
+    if (!active) return;   // every element of such a wave lies below the diagonal or past the edge
+    // the epilogue in two halves of the wave's rows (64 old values in flight)
+    const int khalf = lane >> 5;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        auto row_of = [&](int a, int r) { return m0 + am + (2 * h + a) * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3); };
+        auto col_of = [&](int b) { return n0 + 64 * wn + b * 32 + (lane & 31); };
+        floatx16 res[2][2];
+        if (!L.first_step) {
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) res[a][b][r] = elem_prev(P, row_of(a, r), col_of(b));
+        }
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    res[a][b][r] = elem_value(P, acc[2 * h + a][b][r], res[a][b][r], L.eps, L.first_step);
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) elem_store(P, row_of(a, r), col_of(b), res[a][b][r]);
+    }
+}
+
+template <bool EDGES>
+__device__ __forceinline__ void factor_bf16_wide_item(const GemmLaunch& L, int64_t items) {
+    __shared__ __attribute__((aligned(16))) uint16_t W0[SLAB_WA + SLAB_WB];
+    __shared__ __attribute__((aligned(16))) uint16_t W1[SLAB_WA + SLAB_WB];
+    __shared__ __attribute__((aligned(16))) uint16_t W2[SLAB_WA + SLAB_WB];
+    const int64_t item = L.runs ? xcd_runs<kGemmRun>(blockIdx.x) : xcd_remap(blockIdx.x, gridDim.x);
+    if (item >= items) return;
+    const GemmProb P = L.probs[find_prob(L.probs, L.nprob, item, false)];
+    int I, J;
+    wide_decode(item - P.item_begin, P.tiles_m, P.tiles_n, I, J);
+    const RingW R{{W0, W1, W2}};
+    if (J <= 2 * I + 1) gemm_bf16_wide_tile<true, EDGES>(L, P, I * WM, J * WN, R);
+    else gemm_bf16_wide_tile<false, EDGES>(L, P, I * WM, J * WN, R);
+}
+
+__global__ __launch_bounds__(NT, 2) void factor_bf16_wide_kernel(GemmLaunch L, int64_t items) {
+    factor_bf16_wide_item<false>(L, items);
+}
+__global__ __launch_bounds__(NT, 2) void factor_bf16_wide_edge_kernel(GemmLaunch L, int64_t items) {
+    factor_bf16_wide_item<true>(L, items);
+}
+
 // Sums the split-K partial tiles in chunk order and applies the epilogue.
 // Each partial tile (T x T, T the launch's tile edge) is spread over
 // T * T / 1024 workgroups; thread t sums four consecutive elements, with
@@ -839,6 +1116,18 @@ hipError_t launch_gemm(const GemmLaunch& L, int64_t items, hipStream_t stream, b
     } else {
         hipLaunchKernelGGL(precond_f32_kernel, dim3((unsigned)grid), dim3(NT), 0, stream, R, items);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_factor_wide(const GemmLaunch& L, int64_t items, hipStream_t stream, bool edges) {
+    if (items <= 0) return hipSuccess;
+    GemmLaunch R = L;
+    R.runs = items >= kGemmRunsMin ? 1 : 0;
+    const int64_t grid = R.runs ? (items + 8 * kGemmRun - 1) / (8 * kGemmRun) * (8 * kGemmRun) : items;
+    if (edges)
+        hipLaunchKernelGGL(factor_bf16_wide_edge_kernel, dim3((unsigned)grid), dim3(NT), 0, stream, R, items);
+    else
+        hipLaunchKernelGGL(factor_bf16_wide_kernel, dim3((unsigned)grid), dim3(NT), 0, stream, R, items);
     return hipGetLastError();
 }
 

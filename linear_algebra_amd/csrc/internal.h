@@ -33,6 +33,31 @@ constexpr int kGemmBK = 32;        // rows of each operand staged per LDS buffer
 constexpr int kGemmThreads = 256;  // 4 waves, 2 x 2 over the tile, 64 x 64 each
 constexpr int kGemmSubK = 512;     // rows accumulated before folding into the running sum
 
+// Wide bfloat16 factor tiles: 256 rows x 128 columns per workgroup, each wave
+// 128 x 64.  For factor launches with bf16 inputs whose rows all start on a
+// 4-byte boundary, no problem split along K, and at most kWideMaxK rows: the
+// products go into one float32 sum per element without the second-level
+// fold (at most kWideMaxK / 16 additions of exact 16-term products).
+constexpr int kWideM = 256;
+constexpr int kWideN = 128;
+constexpr int kWideMaxK = 16384;
+constexpr int64_t kWideMinTiles = 1024;   // fewer tiles than this leave CUs idle: 128 x 128 tiles instead
+
+// The wide tiles of a factor of order d: tile row I (rows 256 I ..) holds the
+// tile columns J >= 2 I (columns 128 J ..), the ones that reach the upper
+// triangle.  Tiles are numbered in bands of two tile rows, column by
+// column: band b has row 2 b from column 4 b and row 2 b + 1 from column
+// 4 b + 2 (each row holds at least one tile).
+__host__ __device__ inline int64_t wide_band_tiles(int64_t b, int64_t ti, int64_t tj) {
+    return (tj - 4 * b) + (2 * b + 1 < ti ? tj - 4 * b - 2 : 0);
+}
+__host__ __device__ inline int64_t wide_tiles(int64_t d) {
+    const int64_t ti = (d + kWideM - 1) / kWideM, tj = (d + kWideN - 1) / kWideN;
+    int64_t n = 0;
+    for (int64_t b = 0; 2 * b < ti; ++b) n += wide_band_tiles(b, ti, tj);
+    return n;
+}
+
 enum GemmMode : int32_t { kModePlain = 0, kModeFactor = 1 };
 
 struct GemmProb {
@@ -72,6 +97,9 @@ struct GemmLaunch {
 hipError_t launch_gemm(const GemmLaunch& L, int64_t items, hipStream_t stream, bool bf16, bool factor,
                        bool bf16_aligned = true, bool bf16_edges = true);
 hipError_t launch_gemm_reduce(const GemmLaunch& L, int64_t tiles, hipStream_t stream, bool factor);
+// bf16 factors on wide tiles (problems numbered by wide_tiles, K unsplit);
+// `edges`: some order is not a multiple of 256.
+hipError_t launch_factor_wide(const GemmLaunch& L, int64_t items, hipStream_t stream, bool edges);
 
 // An odd-width bf16 input copied to a pitch that is a multiple of 64 elements
 // (rows start on 128-byte lines; columns past d zero); 256 groups of 8

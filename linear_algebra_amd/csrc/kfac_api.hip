@@ -487,22 +487,40 @@ kfac_status_t kfac_factors(int n, const void* const* x, const int64_t* rows, con
             part_off += (int64_t)g.ntiles * g.ksplit * kGemmTile * kGemmTile;
         }
     }
+    // bf16 rows that all start 4-byte aligned (every input after the repack,
+    // unless a base is one element off) take the kernels without the
+    // element-wise path; with no split of K, at most kWideMaxK rows and
+    // enough tiles, the wide tiles
+    bool aligned_rows = true, edges = false, wide = bf16, wide_edges = false;
+    int64_t wide_items = 0;
+    for (int i = 0; i < n; ++i) {
+        const GemmProb& g = p.probs[i];
+        aligned_rows = aligned_rows && (g.lda & 1) == 0 && aligned(g.a, 4);
+        edges = edges || g.M % kGemmTile != 0;
+        wide = wide && g.ksplit == 1 && g.K <= kWideMaxK;
+        wide_edges = wide_edges || g.M % kWideM != 0;
+        wide_items += wide_tiles(g.M);
+    }
+    wide = wide && aligned_rows && wide_items >= kWideMinTiles;
+    if (wide) {
+        int64_t item = 0;
+        for (int i = 0; i < n; ++i) {
+            GemmProb& g = p.probs[i];
+            g.tiles_m = (int32_t)ceil_div((int64_t)g.M, (int64_t)kWideM);
+            g.tiles_n = (int32_t)ceil_div((int64_t)g.N, (int64_t)kWideN);
+            g.ntiles = (int32_t)wide_tiles(g.M);
+            g.item_begin = item;
+            item += g.ntiles;
+        }
+    }
     hipError_t e = rl.empty() ? upload_table(probs_dev, p.probs.data(), sizeof(GemmProb) * n, stream)
                               : upload_tables({{probs_dev, p.probs.data(), sizeof(GemmProb) * n},
                                                {repack_dev, rl.data(), sizeof(RepackLayer) * rl.size()}},
                                               stream);
     if (e == hipSuccess && !rl.empty()) e = launch_repack_bf16(repack_dev, (int)rl.size(), repack_blocks, stream);
     if (e != hipSuccess) return KFAC_ERR_HIP;
-    // bf16 rows that all start 4-byte aligned (every input after the repack,
-    // unless a base is one element off) take the kernel without the
-    // element-wise path
-    bool aligned_rows = true, edges = false;
-    for (int i = 0; i < n; ++i) {
-        const GemmProb& g = p.probs[i];
-        aligned_rows = aligned_rows && (g.lda & 1) == 0 && aligned(g.a, 4);
-        edges = edges || g.M % kGemmTile != 0;
-    }
     GemmLaunch L{probs_dev, n, first_step ? 1 : 0, eps, 0, kGemmTile};
+    if (wide) return hip_status(launch_factor_wide(L, wide_items, stream, wide_edges));
     e = launch_gemm(L, p.items, stream, bf16, true, aligned_rows, edges);
     if (e != hipSuccess) return KFAC_ERR_HIP;
     return hip_status(launch_gemm_reduce(L, p.red_tiles, stream, true));

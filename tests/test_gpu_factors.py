@@ -146,6 +146,41 @@ def test_factors_slab_and_matrix_ends(dtype, rows, d):
     assert upper_rel_fro(got, ref) <= 1e-6
 
 
+def test_factors_bf16_wide_tiles():
+    """bf16 launches with enough tiles, no split of K and at most 16384 rows
+    take 256 x 128 tiles.  One call over orders with every kind of edge
+    (multiples of 256, of 128 only, 64m + 1, others; 1223 wide tiles in
+    all), rows not a multiple of the 32-row slab, two running-average steps.
+    The last layer carries the slab-end pattern: only its last two columns
+    are nonzero, in the last row of every slab and in the last row."""
+    from workloads import f32_to_bf16_bits
+    say("factors bf16 wide tiles")
+    rng = np.random.default_rng(8)
+    rows = 1000
+    dims = [4097, 4096, 3000, 2049, 2000, 1025, 1000, 513, 384, 257, 130, 4097]
+    ms = [nan_f32(d, d) for d in dims]
+    ref = [None] * len(dims)
+    ends = sorted(set(list(range(31, rows, 32)) + [rows - 1]))
+    for step in range(2):
+        fs = [0.05 * rng.standard_normal((rows, d)).astype(np.float32) for d in dims]
+        last = np.zeros((rows, dims[-1]), dtype=np.float32)
+        last[ends, -1] = 1.0
+        last[ends, -2] = 2.0
+        fs[-1] = last
+        hs = [f32_to_bf16_bits(f) for f in fs]
+        gpu_factors(hs, ms, EPS, step == 0)
+        for k, h in enumerate(hs):
+            ref[k] = oracle.running_average(ref[k], oracle.factor(oracle.upcast(h, "bf16")), np.float32(EPS), step == 0)
+            got = to_host(ms[k])
+            err = upper_rel_fro(got, ref[k])
+            say("  wide err", dims[k], step, err)
+            assert err <= TOL_BF16, (dims[k], step, err)
+            assert np.all(np.isnan(got[np.tril_indices(dims[k], -1)]))
+        got = to_host(ms[-1]).astype(np.float64)
+        assert upper_rel_fro(got, ref[-1]) <= 1e-6
+        assert got[-1, -1] == pytest.approx(ref[-1][-1, -1], rel=1e-6)
+
+
 def run_config_factors(cid, steps=None):
     """A factors then G factors of every layer, as one call each, for the
     given steps of the workload's schedule; full comparison with the oracle."""
