@@ -1,4 +1,4 @@
-// fp32 MFMA GEMM for the factor (syrk, upper tiles, running average) and
+// MFMA GEMMs for the factor (syrk, upper tiles, running average) and
 // precondition (two plain products) stages.
 //
 // C = alpha * Aop^T Bop, Aop [K][lda], Bop [K][ldb], both with the reduction
@@ -6,25 +6,28 @@
 // contiguous row segments and the global loads coalesce.
 //
 // Tile 128 x 128 per workgroup of 4 waves (2 x 2, 64 x 64 each, four
-// accumulators per wave).  K is staged through two LDS buffers of kGemmBK
-// rows per operand: the copies of the next slab are in flight while the
-// current one feeds the matrix cores.  Products are summed in float32 over
-// sub-chunks of kGemmSubK rows and then folded into a second float32 sum,
-// which keeps the rounding error of long reductions (hundreds of thousands
-// of rows) near that of a 512-term sum.
+// accumulators per wave).  Products are summed in float32 over sub-chunks
+// of kGemmSubK rows and then folded into a second float32 sum, which keeps
+// the rounding error of long reductions (hundreds of thousands of rows)
+// near that of a 512-term sum.  Operands are read with buffer loads whose
+// descriptor covers one K-slab: rows past the end of the input read as
+// zero without a branch, and the per-thread offsets inside a slab are
+// computed once.
 //
-// Operands are read with buffer loads whose descriptor covers one K-slab:
-// rows past the end of the input read as zero without a branch, and the
-// per-thread offsets inside a slab are computed once.  float32 slabs go
-// from memory straight into LDS as [k][m] rows (v_mfma_f32_32x32x2f32 takes
-// one k-value per lane).  bfloat16 slabs of 4-byte aligned rows do the same
-// and are read back with transposing LDS reads, since
+// float32 operands run on the bf16 matrix cores (v_mfma_f32_32x32x16_bf16,
+// 16 times the rate of v_mfma_f32_32x32x2f32 on gfx950): every value is
+// split exactly into three bf16 values and each block product becomes six
+// bf16 products, which carry the rounding of a float32 product (see the
+// split kernel below).  bfloat16 inputs go from memory straight into LDS as
+// [k][m] rows and are read back with transposing LDS reads, since
 // v_mfma_f32_32x32x16_bf16 takes 8 consecutive k-values per lane; rows of
 // odd width are first repacked to an aligned pitch (bf16_repack.hip), and
 // only an input of even width at a base one element off a 4-byte boundary
 // passes through registers, stored as [m][k].  bf16 factor launches with K
 // unsplit, at most kWideMaxK rows and enough tiles take 256 x 128 tiles
 // (each wave 128 x 64), which read fewer LDS bytes per product.
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -36,8 +39,6 @@ constexpr int BK = kGemmBK;
 constexpr int NT = kGemmThreads;
 constexpr int kGemmRun = 16;        // items per XCD run in large launches
 constexpr int64_t kGemmRunsMin = 2048;
-constexpr int KPL = BK / 2;          // slab rows each lane feeds to the matrix cores
-constexpr int SUB_STAGES = kGemmSubK / BK;
 
 __device__ __forceinline__ int find_prob(const GemmProb* probs, int nprob, int64_t item, bool reduce) {
     int lo = 0, hi = nprob - 1;
@@ -185,153 +186,6 @@ __device__ __forceinline__ TileWork decode_item(const GemmLaunch& L, int64_t ite
     return w;
 }
 
-// float32 slabs are copied by the load units straight into LDS
-// (buffer_load_dwordx4 ... lds, 16 bytes per lane), as [k][m] rows of the
-// tile, the way they lie in memory: no registers, no transposing stores.
-// A lane copies 4 consecutive columns of one slab row; a chunk wholly past
-// the last column gets an offset beyond the descriptor and reads as zero
-// (one that straddles it reads a few values of the next row, which only
-// reach outputs that are not stored, or, in the slab's last row, stops at
-// the descriptor's end), and rows past the end of the slab read as zero
-// through the descriptor.  The two buffers of each operand
-// are separate LDS arrays, so that the compiler can tell the copies into
-// one from the reads of the other.
-constexpr int SLAB = BK * BM;                 // floats per staged slab
-constexpr int kSlabCopies = SLAB / (4 * NT);  // copy instructions per wave and slab (4)
-static_assert(kSlabCopies * 4 * NT == SLAB && BM % 4 == 0, "a slab is a whole number of 16-byte copies per lane");
-
-__device__ __forceinline__ void stage_slab(float* S, __amdgpu_buffer_rsrc_t r, const uint32_t (&off)[kSlabCopies]) {
-    const int w = threadIdx.x >> 6;
-#pragma unroll
-    for (int s = 0; s < kSlabCopies; ++s)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            r, (__attribute__((address_space(3))) void*)(S + 256 * (kSlabCopies * w + s)), 16, off[s], 0, 0, 0);
-}
-
-// acc += one staged slab: lane l supplies row/column (l % 32) of its
-// 32-wide blocks and, at step s, the slab row 16 (l / 32) + s (the sum over
-// the slab does not depend on how its rows are paired).
-// NA x NB of the wave's 32 x 32 blocks (the others lie wholly past the
-// last row or column of the problem and are left at zero)
-template <int NA, int NB>
-__device__ __forceinline__ void mma_slab(floatx16 (&acc)[2][2], const float* A, const float* Bm, int wm, int wn,
-                                         int lane) {
-    const int fr = lane & 31, fk = (lane >> 5) * KPL;
-    const float* pa = A + fk * BM + wm * 64 + fr;
-    const float* pb = Bm + fk * BM + wn * 64 + fr;
-#pragma unroll
-    for (int s = 0; s < KPL; ++s) {
-        const float a0 = pa[s * BM], a1 = NA > 1 ? pa[s * BM + 32] : 0.0f;
-        const float b0 = pb[s * BM], b1 = NB > 1 ? pb[s * BM + 32] : 0.0f;
-        acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
-        if (NB > 1) acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
-        if (NA > 1) acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
-        if (NA > 1 && NB > 1) acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
-    }
-}
-
-// full == both blocks in each direction hold rows / columns of the problem
-__device__ __forceinline__ void mma_slab_edge(floatx16 (&acc)[2][2], const float* A, const float* Bm, int wm,
-                                              int wn, int lane, bool full, bool a2, bool b2) {
-    if (full) mma_slab<2, 2>(acc, A, Bm, wm, wn, lane);
-    else if (a2) mma_slab<2, 1>(acc, A, Bm, wm, wn, lane);
-    else if (b2) mma_slab<1, 2>(acc, A, Bm, wm, wn, lane);
-    else mma_slab<1, 1>(acc, A, Bm, wm, wn, lane);
-}
-
-// One tile; SAME (a factor tile on the diagonal) stages only A and reads
-// both operands from it.
-template <bool SAME>
-__device__ __forceinline__ void gemm_f32_tile(const GemmLaunch& L, const TileWork& W, float* A0, float* A1, float* B0,
-                                              float* B1) {
-    const GemmProb& P = W.P;
-    const int k_begin = W.k_begin, k_end = W.k_end;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    // a wave whose 64 rows or columns all lie past the problem's edge has
-    // nothing to compute; one whose second 32 do skips those blocks
-    const int wr = W.m0 + 64 * wm, wc = W.n0 + 64 * wn;
-    const bool active = W.active && wr < P.M && wc < P.N;
-    const bool a2 = wr + 32 < P.M, b2 = wc + 32 < P.N, full = a2 && b2;
-    float* const Bb0 = SAME ? A0 : B0;
-    float* const Bb1 = SAME ? A1 : B1;
-
-    // copy s of this lane: slab row k, columns 4c .. 4c + 3 of the tile
-    uint32_t offa[kSlabCopies], offb[kSlabCopies];
-#pragma unroll
-    for (int s = 0; s < kSlabCopies; ++s) {
-        const int chunk = (kSlabCopies * wave + s) * 64 + lane;
-        const int k = chunk >> 5, m = 4 * (chunk & 31);
-        offa[s] = (W.m0 + m < P.M) ? (uint32_t)((k * P.lda + W.m0 + m) * 4) : kOOB;
-        offb[s] = (W.n0 + m < P.N) ? (uint32_t)((k * P.ldb + W.n0 + m) * 4) : kOOB;
-    }
-    auto stage = [&](float* SA, float* SB, int k0) {
-        stage_slab(SA, slab_rsrc(P.a, P.lda, k0, k_end, 4, P.M), offa);
-        if (!SAME) stage_slab(SB, slab_rsrc(P.b, P.ldb, k0, k_end, 4, P.N), offb);
-    };
-
-    floatx16 acc[2][2], sum[2][2];
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) { acc[a][b][r] = 0.0f; sum[a][b][r] = 0.0f; }
-    auto fold = [&](int st, int nstages) {
-        if ((st + 1) % SUB_STAGES == 0 || st + 1 == nstages) {
-#pragma unroll
-            for (int a = 0; a < 2; ++a)
-#pragma unroll
-                for (int b = 0; b < 2; ++b) {
-                    sum[a][b] += acc[a][b];
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
-                }
-        }
-    };
-
-    const int nstages = (k_end - k_begin + BK - 1) / BK;
-    if (nstages > 0) stage(A0, B0, k_begin);
-    // slab st in buffer st % 2; the copies of slab st + 1 are issued right
-    // after the barrier that frees their buffer
-    for (int st = 0; st < nstages; st += 2) {
-        __builtin_amdgcn_s_waitcnt(0);   // this slab's copies (the only loads in flight)
-        __syncthreads();
-        if (st + 1 < nstages) stage(A1, B1, k_begin + (st + 1) * BK);
-        if (active) {
-            mma_slab_edge(acc, A0, Bb0, wm, wn, lane, full, a2, b2);
-            fold(st, nstages);
-        }
-        if (st + 1 >= nstages) break;
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (st + 2 < nstages) stage(A0, B0, k_begin + (st + 2) * BK);
-        if (active) {
-            mma_slab_edge(acc, A1, Bb1, wm, wn, lane, full, a2, b2);
-            fold(st + 1, nstages);
-        }
-    }
-    store_tile(P, L, sum, W.kc, W.t, W.m0, W.n0, wm, wn, lane);
-}
-
-__device__ __forceinline__ void gemm_f32_item(const GemmLaunch& L, int64_t items) {
-    __shared__ __attribute__((aligned(16))) float A0[SLAB];
-    __shared__ __attribute__((aligned(16))) float A1[SLAB];
-    __shared__ __attribute__((aligned(16))) float B0[SLAB];
-    __shared__ __attribute__((aligned(16))) float B1[SLAB];
-    const int64_t item = L.runs ? xcd_runs<kGemmRun>(blockIdx.x) : xcd_remap(blockIdx.x, gridDim.x);
-    if (item >= items) return;
-    const TileWork W = decode_item(L, item);
-    if (W.same) gemm_f32_tile<true>(L, W, A0, A1, B0, B1);
-    else gemm_f32_tile<false>(L, W, A0, A1, B0, B1);
-}
-
-// The same kernel under the name of each stage, so that kernel traces give
-// the factors and the preconditioning products their own figures.
-__global__ __launch_bounds__(NT, 2) void factor_f32_kernel(GemmLaunch L, int64_t items) { gemm_f32_item(L, items); }
-__global__ __launch_bounds__(NT, 2) void precond_f32_kernel(GemmLaunch L, int64_t items) { gemm_f32_item(L, items); }
-
-
 // bfloat16 inputs on v_mfma_f32_32x32x16_bf16 (products exact in float32,
 // float32 accumulation).  Slabs of 32 rows are staged as [m][k] bf16 with k
 // contiguous; a lane's eight k-values of a block are one 16-byte LDS read,
@@ -466,6 +320,8 @@ __device__ __forceinline__ void gemm_bf16_reg_tile(const GemmLaunch& L, const Ti
 // 1-2 differ).  With c xor 2 (k % 4) the rows paired up on the same banks
 // (half of the LDS cycles were conflicts).
 typedef short short4v __attribute__((ext_vector_type(4)));
+typedef float float2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 typedef short short8v __attribute__((ext_vector_type(8)));
 constexpr int SLAB16 = BK16 * BM;                  // bf16 per staged slab (8 KB)
 constexpr int kSlab16Copies = SLAB16 / (8 * NT);   // copy instructions per wave and slab (2)
@@ -486,17 +342,6 @@ __device__ __forceinline__ void stage_slab16(uint16_t* S, __amdgpu_buffer_rsrc_t
     for (int s = 0; s < kSlab16Copies; ++s)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             r, (__attribute__((address_space(3))) void*)(S + 512 * (kSlab16Copies * w + s)), 16, off[s], 0, 0, 0);
-}
-
-// 8 consecutive k-values (k0 .. k0 + 7 of the lane's group) of column mb + (lane % 16)
-__device__ __forceinline__ bf16x8 tr_frag(const uint16_t* S, int k0, int mb, int p) {
-    const int m = mb + 4 * (p & 3);
-    const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) short4v*)(S + tr_at(k0 + (p >> 2), m)));
-    const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) short4v*)(S + tr_at(k0 + 4 + (p >> 2), m)));
-    const short8v v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    return __builtin_bit_cast(bf16x8, v);
 }
 
 // The products of a full wave, with the LDS reads written out, for the ring below.  The
@@ -1044,6 +889,273 @@ __global__ __launch_bounds__(NT, 2) void factor_bf16_wide_edge_kernel(GemmLaunch
     factor_bf16_wide_item<true>(L, items);
 }
 
+// float32 products on the bf16 matrix cores.  The float32 matrix cores of
+// gfx950 run at 1/16 the rate of the bf16 ones.  A float32 value splits
+// exactly into three bf16 values, x = x0 + x1 + x2: x0 = bf16(x) rounded to
+// nearest, x1 = bf16(x - x0), x2 = x - x0 - x1 (each difference is exact in
+// float32, and the last has at most 8 significant bits).  |x1| <= 2^-8 |x|
+// and |x2| <= 2^-16 |x|, so x y is x0 y0 + x0 y1 + x1 y0 + x0 y2 + x1 y1 +
+// x2 y0 up to the three dropped cross terms, below 2^-23 |x y| together and
+// of either sign; each of the six products is exact in float32.  The sum
+// therefore carries the rounding of a float32 product, and the six products
+// take 6 x 32 cycles of the bf16 matrix cores against 8 x 64 of the
+// float32 ones for the same 32 x 32 x 16 block.
+//
+// Tiles, waves, the split-K partials, the epilogue and the running sums are
+// those of the float32 kernel (128 x 128 tiles, four 64 x 64 waves, a fold
+// every kGemmSubK rows).  K advances in steps of XK = 16 rows: each thread
+// loads two 16-byte chunks of each operand's step (rows t / 32 and t / 32 +
+// 8, columns 4 (t % 32) ..) two steps ahead into registers, splits them
+// and writes the three bf16 planes of the step into LDS ([k][m] rows, the
+// 16-byte chunks swizzled as for the bf16 slabs); the waves then read
+// their fragments with transposing reads.  Each value is split once per
+// workgroup.  Planes are double buffered: the split of step s + 1 goes to
+// the other buffer while the products of step s run, and one barrier per
+// step separates them.
+constexpr int XK = 16;                         // rows of K per step
+constexpr int XPLANE = XK * BM;                // bf16 per plane of one operand (4 KB)
+constexpr int XSUB = kGemmSubK / XK;           // steps per fold
+typedef float xf4 __attribute__((ext_vector_type(4)));
+typedef uint32_t xu2 __attribute__((ext_vector_type(2)));
+
+// Buffer resource over rows [k0, min(k0 + XK, k_end)) of a float32 operand;
+// rows past them read as zero, and the range ends at the operand's last
+// element of the step's last row.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t step_rsrc(const void* base, int64_t ld, int k0, int k_end,
+                                                            int cols) {
+    const char* p = static_cast<const char*>(base) + (int64_t)k0 * ld * 4;
+    const int rows = max(0, min(XK, k_end - k0));
+    const int bytes = __builtin_amdgcn_readfirstlane(rows > 0 ? ((rows - 1) * (int)ld + cols) * 4 : 0);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p), (short)0, bytes, 0x00020000);
+}
+
+// Splits four float32 values into three planes of four bf16 values (the
+// low element of each pair in the low half).
+__device__ __forceinline__ void split4(const xf4 v, xu2& p0, xu2& p1, xu2& p2) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const float2v x = {v[2 * i], v[2 * i + 1]};
+        const uint32_t u0 = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2v));
+        const float2v x0 = {__builtin_bit_cast(float, u0 << 16), __builtin_bit_cast(float, u0 & 0xffff0000u)};
+        const float2v r = {x[0] - x0[0], x[1] - x0[1]};
+        const uint32_t u1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2v));
+        const float2v r1 = {__builtin_bit_cast(float, u1 << 16), __builtin_bit_cast(float, u1 & 0xffff0000u)};
+        const float2v r2 = {r[0] - r1[0], r[1] - r1[1]};
+        p0[i] = u0;
+        p1[i] = u1;
+        p2[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r2, bf16x2v));
+    }
+}
+
+// Transposing read at an immediate byte offset from `a`.
+template <int OFF>
+__device__ __forceinline__ short4v tr_read_at(uint32_t a) {
+    short4v v;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(a), "i"(OFF));
+    return v;
+}
+
+// The block products of one step for a wave: NA x NB of its 32 x 32 blocks
+// (the others lie wholly past the problem's edge).  The step's planes lie
+// at byte offset BASE of the plane buffers: A's plane q at BASE + q 4 KB,
+// B's at BASE + BOFF + q 4 KB.  ra[a] / rb[b] hold this lane's address of
+// its first read in A block a / B block b of plane 0; the other reads
+// differ from it by immediates (the rows k0 + 4 + p / 4 lie 1 KB further).
+// B's three planes are read first and stay; A's planes follow one at a
+// time (plane 0 meets B's planes 0-2, plane 1 B's 0-1, plane 2 B's 0), each
+// read while the products of the one before run.  At most 12 reads are in
+// flight, and the products go round the blocks so that none waits for the
+// one before it on the same accumulator.
+template <int NA, int NB, int BASE, int BOFF>
+__device__ __forceinline__ void mma_x6(floatx16 (&acc)[2][2], const uint32_t (&ra)[2], const uint32_t (&rb)[2]) {
+    constexpr int PL = XPLANE * 2;   // bytes per plane
+    auto fr = [](const short4v& lo, const short4v& hi) {
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    short4v bp[3][2][2], ap[2][2][2];   // B planes; A planes, two at a time
+#define X6_RD(F, R, OFF) F[0] = tr_read_at<(OFF)>(R); F[1] = tr_read_at<(OFF) + 1024>(R)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) { X6_RD(bp[0][b], rb[b], BASE + BOFF); }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) { X6_RD(bp[1][b], rb[b], BASE + BOFF + PL); }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) { X6_RD(bp[2][b], rb[b], BASE + BOFF + 2 * PL); }
+    // B planes 0-1 in (B plane 2's reads may be outstanding); the waits
+    // name the fragments they cover (those of an edge wave's missing blocks
+    // are undefined and unread)
+    if constexpr (NB == 2)
+        asm volatile("s_waitcnt lgkmcnt(4)"
+                     : "+v"(bp[0][0][0]), "+v"(bp[0][0][1]), "+v"(bp[0][1][0]), "+v"(bp[0][1][1]), "+v"(bp[1][0][0]),
+                       "+v"(bp[1][0][1]), "+v"(bp[1][1][0]), "+v"(bp[1][1][1]));
+    else
+        asm volatile("s_waitcnt lgkmcnt(2)"
+                     : "+v"(bp[0][0][0]), "+v"(bp[0][0][1]), "+v"(bp[1][0][0]), "+v"(bp[1][0][1]));
+#pragma unroll
+    for (int a = 0; a < NA; ++a) { X6_RD(ap[0][a], ra[a], BASE); }
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(bp[2][0][0]), "+v"(bp[2][0][1]), "+v"(bp[2][1][0]), "+v"(bp[2][1][1]), "+v"(ap[0][0][0]),
+                   "+v"(ap[0][0][1]), "+v"(ap[0][1][0]), "+v"(ap[0][1][1]));
+#pragma unroll
+    for (int a = 0; a < NA; ++a) { X6_RD(ap[1][a], ra[a], BASE + PL); }
+    auto prod = [&](const short4v (&x)[2][2], const short4v (&y)[2][2]) {
+#pragma unroll
+        for (int a = 0; a < NA; ++a)
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr(x[a][0], x[a][1]), fr(y[b][0], y[b][1]),
+                                                                    acc[a][b], 0, 0, 0);
+    };
+    prod(ap[0], bp[2]);
+    prod(ap[0], bp[1]);
+    prod(ap[0], bp[0]);
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(ap[1][0][0]), "+v"(ap[1][0][1]), "+v"(ap[1][1][0]), "+v"(ap[1][1][1]));
+#pragma unroll
+    for (int a = 0; a < NA; ++a) { X6_RD(ap[0][a], ra[a], BASE + 2 * PL); }
+#undef X6_RD
+    prod(ap[1], bp[1]);
+    prod(ap[1], bp[0]);
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(ap[0][0][0]), "+v"(ap[0][0][1]), "+v"(ap[0][1][0]), "+v"(ap[0][1][1]));
+    prod(ap[0], bp[0]);
+}
+
+template <bool SAME>
+__device__ __forceinline__ void gemm_x6_tile(const GemmLaunch& L, const TileWork& W, uint16_t* XS) {
+    const GemmProb& P = W.P;
+    const int k_begin = W.k_begin, k_end = W.k_end;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int wr = W.m0 + 64 * wm, wc = W.n0 + 64 * wn;
+    const bool active = W.active && wr < P.M && wc < P.N;
+    const bool a2 = wr + 32 < P.M, b2 = wc + 32 < P.N;
+    // this thread's chunks: rows kt and kt + 8 of a step, columns mt .. mt + 3
+    const int kt = tid >> 5, mt = 4 * (tid & 31);
+    uint32_t offa[2], offb[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        offa[j] = (W.m0 + mt < P.M) ? (uint32_t)(((kt + 8 * j) * P.lda + W.m0 + mt) * 4) : kOOB;
+        offb[j] = (W.n0 + mt < P.N) ? (uint32_t)(((kt + 8 * j) * P.ldb + W.n0 + mt) * 4) : kOOB;
+    }
+    // this lane's first fragment read in each block (plane 0 of buffer 0)
+    uint32_t ra[2], rb[2];
+    {
+        const int g = lane >> 4, p = lane & 15, k = 8 * (g >> 1) + (p >> 2);
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+            ra[a] = lds_addr(XS + tr_at(k, wm * 64 + a * 32 + 16 * (g & 1) + 4 * (p & 3)));
+            rb[a] = lds_addr(XS + tr_at(k, wn * 64 + a * 32 + 16 * (g & 1) + 4 * (p & 3)));
+        }
+    }
+    // two steps of chunks in registers
+    xf4 ra4[2][2], rb4[2][2];
+    auto load = [&](int set, int k0) {
+        const __amdgpu_buffer_rsrc_t rs = step_rsrc(P.a, P.lda, k0, k_end, P.M);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            ra4[set][j] = __builtin_bit_cast(xf4, __builtin_amdgcn_raw_buffer_load_b128(rs, offa[j], 0, 0));
+        if (!SAME) {
+            const __amdgpu_buffer_rsrc_t rt = step_rsrc(P.b, P.ldb, k0, k_end, P.N);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                rb4[set][j] = __builtin_bit_cast(xf4, __builtin_amdgcn_raw_buffer_load_b128(rt, offb[j], 0, 0));
+        }
+    };
+    // splits register set `set` into the planes of buffer `buf`
+    auto split = [&](int set, int buf) {
+        uint16_t* const X = XS + buf * 6 * XPLANE;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int at = tr_at(kt + 8 * j, mt);
+            xu2 p0, p1, p2;
+            split4(ra4[set][j], p0, p1, p2);
+            *reinterpret_cast<xu2*>(X + at) = p0;
+            *reinterpret_cast<xu2*>(X + XPLANE + at) = p1;
+            *reinterpret_cast<xu2*>(X + 2 * XPLANE + at) = p2;
+            if (!SAME) {
+                split4(rb4[set][j], p0, p1, p2);
+                *reinterpret_cast<xu2*>(X + 3 * XPLANE + at) = p0;
+                *reinterpret_cast<xu2*>(X + 4 * XPLANE + at) = p1;
+                *reinterpret_cast<xu2*>(X + 5 * XPLANE + at) = p2;
+            }
+        }
+    };
+    constexpr int LPS = SAME ? 2 : 4;   // loads per step, per thread
+    constexpr int BOFF = SAME ? 0 : 3 * XPLANE * 2;
+
+    floatx16 acc[2][2], sum[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) { acc[a][b][r] = 0.0f; sum[a][b][r] = 0.0f; }
+    const int nsteps = (k_end - k_begin + 2 * XK - 1) / (2 * XK) * 2;
+    auto mma = [&](auto buf) {
+        constexpr int BASE = decltype(buf)::value * 6 * XPLANE * 2;
+        if (a2 && b2) mma_x6<2, 2, BASE, BOFF>(acc, ra, rb);
+        else if (a2) mma_x6<2, 1, BASE, BOFF>(acc, ra, rb);
+        else if (b2) mma_x6<1, 2, BASE, BOFF>(acc, ra, rb);
+        else mma_x6<1, 1, BASE, BOFF>(acc, ra, rb);
+    };
+    auto fold = [&](int st) {
+        if ((st + 1) % XSUB == 0 || st + 1 == nsteps) {
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    sum[a][b] += acc[a][b];
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+                }
+        }
+    };
+    // step s: planes in buffer s % 2, its chunks in register set s % 2.
+    // Loads run two steps ahead and are issued for every step, also past
+    // the end (their range is then empty and they read zeros without
+    // touching memory): with no load left out on any path, the wait for
+    // one register set leaves the other set's loads in flight.
+    if (nsteps <= 0) {
+        store_tile(P, L, sum, W.kc, W.t, W.m0, W.n0, wm, wn, lane);
+        return;
+    }
+    load(0, k_begin);
+    load(1, k_begin + XK);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPS));
+    split(0, 0);
+    load(0, k_begin + 2 * XK);
+    lds_barrier16();
+    auto step = [&](int cur, auto h) {
+        constexpr int H = decltype(h)::value;
+        if (active) mma(std::integral_constant<int, H>());
+        // step cur + 1's chunks (set 1 - H) have arrived once only step
+        // cur + 2's (set H) are outstanding
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPS));
+        split(1 - H, 1 - H);
+        load(1 - H, k_begin + (cur + 3) * XK);
+        if (active) fold(cur);
+        // the next step's planes are written and this step's are read
+        lds_barrier16();
+    };
+    // an even number of steps (a last step past the end reads zeros), so
+    // that every pass of the loop takes both halves
+    for (int st = 0; st < nsteps; st += 2) {
+        step(st, std::integral_constant<int, 0>());
+        step(st + 1, std::integral_constant<int, 1>());
+    }
+    store_tile(P, L, sum, W.kc, W.t, W.m0, W.n0, wm, wn, lane);
+}
+
+__device__ __forceinline__ void gemm_x6_item(const GemmLaunch& L, int64_t items) {
+    __shared__ __attribute__((aligned(16))) uint16_t XS[2 * 6 * XPLANE];
+    const int64_t item = L.runs ? xcd_runs<kGemmRun>(blockIdx.x) : xcd_remap(blockIdx.x, gridDim.x);
+    if (item >= items) return;
+    const TileWork W = decode_item(L, item);
+    if (W.same) gemm_x6_tile<true>(L, W, XS);
+    else gemm_x6_tile<false>(L, W, XS);
+}
+
+__global__ __launch_bounds__(NT, 2) void factor_x6_kernel(GemmLaunch L, int64_t items) { gemm_x6_item(L, items); }
+__global__ __launch_bounds__(NT, 2) void precond_x6_kernel(GemmLaunch L, int64_t items) { gemm_x6_item(L, items); }
+
 // Sums the split-K partial tiles in chunk order and applies the epilogue.
 // Each partial tile (T x T, T the launch's tile edge) is spread over
 // T * T / 1024 workgroups; thread t sums four consecutive elements, with
@@ -1112,9 +1224,9 @@ hipError_t launch_gemm(const GemmLaunch& L, int64_t items, hipStream_t stream, b
         else
             hipLaunchKernelGGL(factor_bf16_any_kernel, dim3((unsigned)grid), dim3(NT), 0, stream, R, items);
     } else if (factor) {
-        hipLaunchKernelGGL(factor_f32_kernel, dim3((unsigned)grid), dim3(NT), 0, stream, R, items);
+        hipLaunchKernelGGL(factor_x6_kernel, dim3((unsigned)grid), dim3(NT), 0, stream, R, items);
     } else {
-        hipLaunchKernelGGL(precond_f32_kernel, dim3((unsigned)grid), dim3(NT), 0, stream, R, items);
+        hipLaunchKernelGGL(precond_x6_kernel, dim3((unsigned)grid), dim3(NT), 0, stream, R, items);
     }
     return hipGetLastError();
 }

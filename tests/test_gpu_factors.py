@@ -71,6 +71,23 @@ def test_factors_deterministic():
                                   to_host(m2).view(np.uint32)[np.triu_indices(300)])
 
 
+def test_factors_f32_float32_rounding():
+    """float32 inputs run on the bf16 matrix cores as six products of exact
+    three-way splits.  With values that use all 24 significand bits (and a
+    2^40 spread of magnitudes) the factor stays within float32 rounding:
+    1e-6, a tenth of the gate (a two-way split leaves about 1e-5)."""
+    say("factors f32 rounding")
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((6000, 300)).astype(np.float32)
+    y = (rng.standard_normal((3000, 257)) * np.exp2(rng.integers(-20, 20, size=(1, 257)))).astype(np.float32)
+    ms = [nan_f32(300, 300), nan_f32(257, 257)]
+    gpu_factors([x, y], ms, EPS, True)
+    for h, m in zip((x, y), ms):
+        err = upper_rel_fro(to_host(m), oracle.factor(oracle.upcast(h)))
+        say("  f32 rounding err", h.shape, err)
+        assert err <= 1e-6, (h.shape, err)
+
+
 def test_factors_bf16_small():
     from workloads import f32_to_bf16_bits
     rng = np.random.default_rng(5)

@@ -55,6 +55,19 @@ def test_precondition_identity_closed_form():
     np.testing.assert_allclose(out, g.astype(np.float64) * float(c) ** 2, rtol=1e-6, atol=1e-30)
 
 
+def test_precondition_float32_rounding():
+    """The products run on the bf16 matrix cores as six products of exact
+    three-way splits: the result stays within float32 rounding (2e-6; a
+    two-way split leaves about 1e-5)."""
+    rng = np.random.default_rng(13)
+    zg, za = sym_f32(rng, 640), sym_f32(rng, 1153)
+    g = rng.standard_normal((640, 1153)).astype(np.float32)
+    out = run([zg], [g], [za])[0]
+    err = rel_fro(out, oracle.precondition(zg, g, za))
+    say("precondition f32 rounding err", err)
+    assert err <= 2e-6, err
+
+
 @pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
 def test_precondition_config_full(cid):
     """Every layer of a workload in one call, compared in full."""
