@@ -1089,24 +1089,15 @@ __device__ __forceinline__ void gemm_x6_tile(const GemmLaunch& L, const TileWork
 #pragma unroll
             for (int r = 0; r < 16; ++r) { acc[a][b][r] = 0.0f; sum[a][b][r] = 0.0f; }
     const int nsteps = (k_end - k_begin + 2 * XK - 1) / (2 * XK) * 2;
-    auto mma = [&](auto buf) {
-        constexpr int BASE = decltype(buf)::value * 6 * XPLANE * 2;
-        if (a2 && b2) mma_x6<2, 2, BASE, BOFF>(acc, ra, rb);
-        else if (a2) mma_x6<2, 1, BASE, BOFF>(acc, ra, rb);
-        else if (b2) mma_x6<1, 2, BASE, BOFF>(acc, ra, rb);
-        else mma_x6<1, 1, BASE, BOFF>(acc, ra, rb);
-    };
-    auto fold = [&](int st) {
-        if ((st + 1) % XSUB == 0 || st + 1 == nsteps) {
+    auto fold = [&]() {
 #pragma unroll
-            for (int a = 0; a < 2; ++a)
+        for (int a = 0; a < 2; ++a)
 #pragma unroll
-                for (int b = 0; b < 2; ++b) {
-                    sum[a][b] += acc[a][b];
+            for (int b = 0; b < 2; ++b) {
+                sum[a][b] += acc[a][b];
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
-                }
-        }
+                for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+            }
     };
     // step s: planes in buffer s % 2, its chunks in register set s % 2.
     // Loads run two steps ahead and are issued for every step, also past
@@ -1123,24 +1114,40 @@ __device__ __forceinline__ void gemm_x6_tile(const GemmLaunch& L, const TileWork
     split(0, 0);
     load(0, k_begin + 2 * XK);
     lds_barrier16();
-    auto step = [&](int cur, auto h) {
-        constexpr int H = decltype(h)::value;
-        if (active) mma(std::integral_constant<int, H>());
-        // step cur + 1's chunks (set 1 - H) have arrived once only step
-        // cur + 2's (set H) are outstanding
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPS));
-        split(1 - H, 1 - H);
-        load(1 - H, k_begin + (cur + 3) * XK);
-        if (active) fold(cur);
-        // the next step's planes are written and this step's are read
-        lds_barrier16();
+    // The loop, compiled once per shape of the wave's work (NA x NB blocks;
+    // none for a wave with nothing to compute), so that a step holds no
+    // branch and the split of the next step can be scheduled among the
+    // products of this one.  The step count is even (a last step past the
+    // end reads zeros), and a fold every XSUB steps falls between pairs.
+    auto run = [&](auto na, auto nb) {
+        constexpr int NA = decltype(na)::value, NB = decltype(nb)::value;
+        auto step = [&](int cur, auto h) {
+            constexpr int H = decltype(h)::value;
+            if constexpr (NA > 0) mma_x6<NA, NB, H * 6 * XPLANE * 2, BOFF>(acc, ra, rb);
+            // step cur + 1's chunks (set 1 - H) have arrived once only step
+            // cur + 2's (set H) are outstanding
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPS));
+            split(1 - H, 1 - H);
+            load(1 - H, k_begin + (cur + 3) * XK);
+            // the next step's planes are written and this step's are read
+            lds_barrier16();
+        };
+        for (int st = 0; st < nsteps; st += 2) {
+            step(st, std::integral_constant<int, 0>());
+            step(st + 1, std::integral_constant<int, 1>());
+            if constexpr (NA > 0)
+                if ((st + 2) % XSUB == 0 || st + 2 == nsteps) fold();
+        }
     };
-    // an even number of steps (a last step past the end reads zeros), so
-    // that every pass of the loop takes both halves
-    for (int st = 0; st < nsteps; st += 2) {
-        step(st, std::integral_constant<int, 0>());
-        step(st + 1, std::integral_constant<int, 1>());
-    }
+    static_assert(XSUB % 2 == 0, "folds fall between pairs of steps");
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    if (!active) run(I0(), I0());
+    else if (a2 && b2) run(I2(), I2());
+    else if (a2) run(I2(), I1());
+    else if (b2) run(I1(), I2());
+    else run(I1(), I1());
     store_tile(P, L, sum, W.kc, W.t, W.m0, W.n0, wm, wn, lane);
 }
 
