@@ -68,7 +68,10 @@ __device__ __forceinline__ float elem_prev(const GemmProb& P, int i, int j) {
     return as_global(P.c)[off];
 }
 __device__ __forceinline__ void elem_store(const GemmProb& P, int i, int j, float r) {
-    if (elem_kept(P, i, j)) as_global(P.c)[(int64_t)i * P.ldc + j] = r;
+    if (elem_kept(P, i, j)) {
+        as_global(P.c)[(int64_t)i * P.ldc + j] = r;
+        if ((P.flags & kGemmMirror) && j != i) as_global(P.c)[(int64_t)j * P.ldc + i] = r;
+    }
 }
 
 constexpr uint32_t kOOB = 0x80000000u;  // buffer offset past any slab: loads return 0
@@ -178,6 +181,8 @@ __device__ __forceinline__ TileWork decode_item(const GemmLaunch& L, int64_t ite
     w.n0 = tj * BM;
     w.k_begin = w.kc * P.kchunk;
     w.k_end = min(P.K, w.k_begin + P.kchunk);
+    // an operand zero above its diagonal contributes from row max(m0, n0) on
+    if (P.flags & kGemmTriK) w.k_begin = max(w.k_begin, max(w.m0, w.n0));
     // factor tiles on the diagonal read the same columns for both operands
     w.same = (P.a == P.b) && (w.m0 == w.n0);
     const int wave = threadIdx.x >> 6;

@@ -59,6 +59,10 @@ __host__ __device__ inline int64_t wide_tiles(int64_t d) {
 }
 
 enum GemmMode : int32_t { kModePlain = 0, kModeFactor = 1 };
+// GemmProb flags: the K range of an output tile starts at max(first row,
+// first column) (an operand that is zero above its diagonal, Aop[k][i] = 0
+// for k < i), and every element kept is also written to its mirror position.
+enum GemmFlag : int32_t { kGemmTriK = 1, kGemmMirror = 2 };
 
 struct GemmProb {
     const void* a;        // Aop
@@ -76,7 +80,7 @@ struct GemmProb {
     int32_t mode;         // GemmMode
     int32_t bf16;         // operands are bfloat16 bit patterns
     float alpha;
-    float pad_;
+    int32_t flags;        // GemmFlag bits
 };
 
 struct GemmLaunch {
@@ -205,6 +209,8 @@ struct InvMat {
     int32_t* info;        // &info[original index]
     double* part;         // workspace: partial blocks of V, 2 x vpart_slots(nb - 1) blocks (by column parity)
     double* bvec;         // bordered matrices (n < d): border_doubles(nb), see there
+    float* vt;            // workspace [n + 1][64 nb] float32: V^T, and for a bordered matrix the
+                          // border column of V as row n; the operand of the last product Z = V V^T
     int32_t d;            // order of the matrix and row stride of x and z
     int32_t n;            // order of the part factored in blocks: d, or d - 1 when the last row and
                           // column are attached afterwards as a border
@@ -263,7 +269,7 @@ constexpr int kMaxPassDepth = 3;
 // given potrf step (trsm, syrk) or trtri level.  Shared by the host, which
 // sizes the grids, and the kernels, which decode their tile index.
 enum InvKind : int32_t {
-    kInvPrepare = 0, kInvPanel = 1, kInvSyrk = 2, kInvTrtri = 3, kInvLauum = 4,
+    kInvPrepare = 0, kInvPanel = 1, kInvSyrk = 2, kInvTrtri = 3, kInvUpper = 4,
     kInvVPart = 6, kInvVFin = 7, kInvBorder = 8, kInvBorderRun = 9, kInvNextRow = 10
 };
 
@@ -296,7 +302,7 @@ __host__ __device__ inline bool trtri_balanced(int64_t nb) {
 __host__ __device__ inline int64_t inv_tiles(int kind, int64_t nb, int64_t step, int64_t rowq = 1) {
     switch (kind) {
         case kInvPrepare:
-        case kInvLauum:
+        case kInvUpper:
             return nb * (nb + 1) / 2;
         case kInvVPart: {  // partial sums of column step - 1
             const int64_t c = step - 1;
@@ -346,7 +352,7 @@ hipError_t launch_inv_step(const InvLaunch& L, int64_t tiles, hipStream_t s);
 hipError_t launch_inv_trail(const InvLaunch& L, int64_t tiles, hipStream_t stream);
 hipError_t launch_inv_trtri_a(const InvLaunch& L, int64_t tiles, hipStream_t s);
 hipError_t launch_inv_trtri_b(const InvLaunch& L, int64_t tiles, hipStream_t s);
-hipError_t launch_inv_lauum(const InvLaunch& L, int64_t tiles, hipStream_t s);
+hipError_t launch_inv_vt32(const InvLaunch& L, int64_t tiles, hipStream_t s);
 hipError_t launch_inv_border_w(const InvLaunch& L, int64_t tiles, hipStream_t s);
 hipError_t launch_inv_border_u(const InvLaunch& L, int64_t tiles, hipStream_t s);
 hipError_t launch_inv_border_v(const InvLaunch& L, int64_t tiles, hipStream_t s);

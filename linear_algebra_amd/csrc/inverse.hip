@@ -37,8 +37,13 @@
 //   border    for an order d = 64m + 1 (d > 64), only the leading 64m x 64m
 //             part goes through the steps above; its last row and column are
 //             attached afterwards as one more (bordered) Cholesky step, by two
-//             matrix-vector launches, and lauum adds the border column of V;
-//   lauum     Z = V V^T (upper blocks), written as float32 to both triangles.
+//             matrix-vector launches, and the last product adds v v^T for
+//             the border column v of V;
+//   V V^T     Z = V V^T: V^T rounded to float32 (vt32), then the float32
+//             GEMM of the factor stage (products as six bf16 products of
+//             exact splits), upper tiles with K from max(row, column), both
+//             triangles written (see inv_vt32_kernel for why float32
+//             suffices here).
 //
 // Diagonal blocks of V are the inverses of the diagonal blocks of U, kept in
 // a separate array (dinv).  Matrices are grouped in buckets of equal nb,
@@ -61,7 +66,7 @@ constexpr int LD = B + 1;      // LDS row stride in doubles (conflict-free colum
 constexpr int NT = kInvThreads;
 constexpr int BB = B * B;
 constexpr int PER = BB / NT;   // block elements per thread (16)
-constexpr int kRun = 16;       // items per XCD run in launches of uneven items (trtri, lauum)
+constexpr int kRun = 16;       // items per XCD run in launches of uneven items (trtri)
 
 // Which matrix and which of its tiles a workgroup owns.
 __device__ __forceinline__ bool locate(const InvLaunch& L, int kind, int64_t tile, int& mat, int64_t& local) {
@@ -946,65 +951,58 @@ __global__ __launch_bounds__(NT, 4) void inv_trtri_b_kernel(InvLaunch L, int64_t
     acc_store(acc, M.w + (int64_t)I * B * D + (int64_t)J * B, D);
 }
 
-// Z_IJ = sum_{t >= J} V_It V_Jt^T for I <= J; float32 out, both triangles.
-// For a bordered matrix V has one more column, v, and Z_IJ gains v_I v_J^T.
-__global__ __launch_bounds__(NT, 4) void inv_lauum_kernel(InvLaunch L, int64_t tiles) {
-    // quarters of 16 k-columns, and the output transposed through LDS as
-    // float32: the staging area is 33 KB and four workgroups share a CU
-    constexpr int KL = 16;
-    constexpr int FD = B * (B + 1) / 2;   // a 64 x 65 float32 block, in doubles
-    static_assert(FD >= 2 * B * KL, "the first array also holds the A and B quarters of buffer 0");
-    __shared__ __attribute__((aligned(16))) double S0[FD], S1[2 * B * KL];
-    const Stage S{S0, S1};
-    float* F = reinterpret_cast<float*>(S0);
+// V^T in float32 for the last product Z = V V^T, which runs on the GEMM of
+// the factor stage (float32 products, K range of a tile from max(row,
+// column), both triangles written).  Its error against ||Z||_F does not grow
+// with the condition number: | |V| |V|^T | <= ||V||_F^2 = trace(Z) <=
+// sqrt(n) ||Z||_F, so products with float32 rounding keep Z within
+// float32-level error of the float64 result; the factorisation and V stay
+// in float64, where errors are amplified.  One workgroup per upper block
+// (I, t) of V (t >= I): the block is read row by row, rounded, transposed
+// through LDS and written as rows t 64 .. of vt (columns I 64 ..); a
+// diagonal block keeps only its upper triangle (rows k < i of vt are
+// zero).  For odd I the block (I - 1, I) of vt, which a 128-row tile of the
+// product reads, is written as zeros; for a bordered matrix the border
+// column of V becomes row n.
+__global__ __launch_bounds__(NT) void inv_vt32_kernel(InvLaunch L, int64_t tiles) {
+    __shared__ float T[B][B + 1];
     int mi;
     int64_t local;
-    const int64_t item = xcd_runs<kRun>(blockIdx.x);
-    if (item >= tiles || !locate(L, kInvLauum, item, mi, local)) return;
+    if ((int64_t)blockIdx.x >= tiles || !locate(L, kInvUpper, blockIdx.x, mi, local)) return;
     const InvMat M = L.mats[mi];
-    // column by column over the upper blocks (J ascending, I = 0..J): the
-    // longest products (small J) start first, and tiles that run side by side
-    // share the blocks of V row J
-    int I, J;
-    column_decode(local, I, J);
-    const int64_t D = (int64_t)M.nb * B, d = M.d, n = M.n;
-    const bool bord = n < d;
-    // the border column of V at rows I (vb[0, 64)) and J (vb[64, 128)),
-    // visible after the first barrier of the block product
-    __shared__ double vb[2 * B];
-    if (bord && threadIdx.x < 2 * B)
-        vb[threadIdx.x] = as_global(M.bvec)[(int64_t)(threadIdx.x < B ? I : J) * B + (threadIdx.x & 63)];
-    doublex4 acc[2][2];
-    acc_zero(acc);
-    auto V = [&](int row, int t) {
-        if (L.vlow) return v_low(M, D, row, t);
-        return t == row ? Blk{M.dinv + (int64_t)row * BB, B, false}
-                        : Blk{M.w + (int64_t)row * B * D + (int64_t)t * B, D, false};
-    };
-    block_gemm<KL>(acc, S, J, M.nb, [&](int t) { return V(I, t); }, [&](int t) { return V(J, t); }, false,
-               I == J);
-    // each element with its border term, rounded to float32, into F; both
-    // triangles are written from F, so the output is exactly symmetric
-    for_acc([&](int a, int b, int r, int row, int col) {
-        double v = acc[a][b][r];
-        if (bord) v += vb[row] * vb[B + col];
-        F[row * (B + 1) + col] = (float)v;
-    });
-    __syncthreads();
-    const int64_t r0 = (int64_t)I * B, c0 = (int64_t)J * B;
-    const int q0 = threadIdx.x >> 6, l = threadIdx.x & 63;
+    int I, t;
+    column_decode(local, I, t);
+    const int64_t D = (int64_t)M.nb * B, n = M.n;
+    const Blk src = t == I ? Blk{M.dinv + (int64_t)I * BB, B, false}
+                           : (L.vlow ? Blk{M.w + (int64_t)t * B * D + (int64_t)I * B, D, false}
+                                     : Blk{M.w + (int64_t)I * B * D + (int64_t)t * B, D, false});
+    double v[PER];
+    fetch(v, src);
+    const int r0 = threadIdx.x >> 6, c = threadIdx.x & 63;
 #pragma unroll
     for (int s = 0; s < PER; ++s) {
-        const int r = q0 + 4 * s, c = l;
-        const int64_t i = r0 + r, j = c0 + c;
-        if (i < n && j < n) as_global(M.z)[i * d + j] = (I != J || c >= r) ? F[r * (B + 1) + c] : F[c * (B + 1) + r];
+        const int r = r0 + 4 * s;   // row i = I 64 + r of V, column k = t 64 + c
+        T[c][r] = (t == I && c < r) ? 0.0f : (float)v[s];
     }
-    if (I != J) {
+    __syncthreads();
+    float* const vt = M.vt;
 #pragma unroll
-        for (int s = 0; s < PER; ++s) {
-            const int c = q0 + 4 * s, r = l;      // destination row c0+c, column r0+r
-            const int64_t i = c0 + c, j = r0 + r;
-            if (i < n && j < n) as_global(M.z)[i * d + j] = F[r * (B + 1) + c];
+    for (int s = 0; s < PER; ++s) {
+        const int kk = r0 + 4 * s;   // row k = t 64 + kk of vt, column i = I 64 + c
+        const int64_t k = (int64_t)t * B + kk, i = (int64_t)I * B + c;
+        if (k < n && i < n) as_global(vt)[k * D + i] = T[kk][c];
+    }
+    if (t == I) {
+        if (I & 1) {
+#pragma unroll
+            for (int s = 0; s < PER; ++s) {
+                const int64_t k = (int64_t)(I - 1) * B + r0 + 4 * s, i = (int64_t)I * B + c;
+                if (i < n) as_global(vt)[k * D + i] = 0.0f;
+            }
+        }
+        if (n < M.d && threadIdx.x < B) {
+            const int64_t i = (int64_t)I * B + threadIdx.x;
+            if (i < n) as_global(vt)[n * D + i] = (float)as_global(M.bvec)[i];
         }
     }
 }
@@ -1173,7 +1171,7 @@ hipError_t launch_inv_step(const InvLaunch& L, int64_t t, hipStream_t s) { retur
 hipError_t launch_inv_trail(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_trail_kernel, L, t, s); }
 hipError_t launch_inv_trtri_a(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_trtri_a_kernel, L, t, s, true); }
 hipError_t launch_inv_trtri_b(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_trtri_b_kernel, L, t, s, true); }
-hipError_t launch_inv_lauum(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_lauum_kernel, L, t, s, true); }
+hipError_t launch_inv_vt32(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_vt32_kernel, L, t, s); }
 hipError_t launch_inv_border_w(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_border_w_kernel, L, t, s); }
 hipError_t launch_inv_border_u(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_border_u_kernel, L, t, s); }
 hipError_t launch_inv_border_v(const InvLaunch& L, int64_t t, hipStream_t s) { return launch(inv_border_v_kernel, L, t, s); }

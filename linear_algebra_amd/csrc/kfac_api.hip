@@ -285,12 +285,14 @@ size_t inverse_ws(int n, const int64_t* d) {
     Carver c(nullptr);
     c.take(sizeof(InvMat) * n);
     c.take(sizeof(InvBucket) * n);
+    c.take(sizeof(GemmProb) * n);
     for (int i = 0; i < n; ++i) {
         const int64_t m = inv_extent(d[i]), nb = ceil_div(m, kInvNB), D = nb * kInvNB;
         c.take(sizeof(double) * (size_t)(D * D));
         c.take(sizeof(double) * (size_t)(D * kInvNB));
         if (fused) c.take(sizeof(double) * (size_t)(2 * vpart_slots(nb - 1) * kInvNB * kInvNB));
         if (m < d[i]) c.take(sizeof(double) * (size_t)border_doubles(nb));
+        c.take(sizeof(float) * (size_t)((m + 1) * D));
     }
     return c.used;
 }
@@ -595,8 +597,10 @@ kfac_status_t kfac_damped_inverse(int n, const float* const* x, const int64_t* d
     Carver c(workspace);
     InvMat* mats_dev = static_cast<InvMat*>(c.take(sizeof(InvMat) * n));
     InvBucket* buckets_dev = static_cast<InvBucket*>(c.take(sizeof(InvBucket) * n));
+    GemmProb* gprobs_dev = static_cast<GemmProb*>(c.take(sizeof(GemmProb) * n));
     // per-matrix scratch in original order
     std::vector<double*> w(n), dinv(n), part(n), bvec(n);
+    std::vector<float*> vt(n);
     bool bordered = false;
     for (int i = 0; i < n; ++i) {
         const int64_t m = inv_extent(d[i]), nb = ceil_div(m, kInvNB), D = nb * kInvNB;
@@ -605,17 +609,46 @@ kfac_status_t kfac_damped_inverse(int n, const float* const* x, const int64_t* d
         part[i] = fused ? static_cast<double*>(c.take(sizeof(double) * (size_t)(2 * vpart_slots(nb - 1) * kInvNB * kInvNB)))
                           : nullptr;
         bvec[i] = m < d[i] ? static_cast<double*>(c.take(sizeof(double) * (size_t)border_doubles(nb))) : nullptr;
+        vt[i] = static_cast<float*>(c.take(sizeof(float) * (size_t)((m + 1) * D)));
         bordered = bordered || m < d[i];
     }
     std::vector<InvMat> mats(n);
     for (int s = 0; s < n; ++s) {
         const int i = p.order[s];
         const int64_t m = inv_extent(d[i]);
-        mats[s] = InvMat{x[i], xinv[i], w[i], dinv[i], info + i, part[i], bvec[i], (int32_t)d[i], (int32_t)m,
+        mats[s] = InvMat{x[i], xinv[i], w[i], dinv[i], info + i, part[i], bvec[i], vt[i], (int32_t)d[i], (int32_t)m,
                          (int32_t)ceil_div(m, kInvNB), 0};
     }
+    // The last product Z = V V^T (plus v v^T for a bordered matrix) on the
+    // GEMM of the factor stage: Aop = Bop = V^T in float32 (row k holds
+    // V_ik, zero for k < i), upper tiles with K from max(row, column), both
+    // triangles written.  Matrices in the bucket order (largest first).
+    std::vector<GemmProb> gp(n);
+    int64_t gitems = 0;
+    for (int s = 0; s < n; ++s) {
+        const int i = p.order[s];
+        const int64_t m = inv_extent(d[i]), D = ceil_div(m, kInvNB) * kInvNB, t = ceil_div(m, kGemmTile);
+        GemmProb& g = gp[s];
+        std::memset(&g, 0, sizeof(g));
+        g.a = g.b = vt[i];
+        g.c = xinv[i];
+        g.lda = g.ldb = D;
+        g.ldc = d[i];
+        g.M = g.N = (int32_t)m;
+        g.K = (int32_t)(m + (m < d[i] ? 1 : 0));
+        g.tiles_m = g.tiles_n = (int32_t)t;
+        g.ntiles = (int32_t)(t * (t + 1) / 2);
+        g.ksplit = 1;
+        g.kchunk = (int32_t)align_up(g.K, kGemmBK);
+        g.mode = kModeFactor;
+        g.alpha = 1.0f;
+        g.flags = kGemmTriK | kGemmMirror;
+        g.item_begin = gitems;
+        gitems += g.ntiles;
+    }
     hipError_t e = upload_tables({{mats_dev, mats.data(), sizeof(InvMat) * n},
-                                  {buckets_dev, p.buckets.data(), sizeof(InvBucket) * p.buckets.size()}},
+                                  {buckets_dev, p.buckets.data(), sizeof(InvBucket) * p.buckets.size()},
+                                  {gprobs_dev, gp.data(), sizeof(GemmProb) * n}},
                                  stream);
     if (e != hipSuccess) return KFAC_ERR_HIP;
 
@@ -693,7 +726,11 @@ kfac_status_t kfac_damped_inverse(int n, const float* const* x, const int64_t* d
     }
     if (e == hipSuccess) {
         L.step = 0;
-        e = launch_inv_lauum(L, bucket_tiles(p, kInvLauum, 0), stream);
+        e = launch_inv_vt32(L, bucket_tiles(p, kInvUpper, 0), stream);
+    }
+    if (e == hipSuccess) {
+        const GemmLaunch G{gprobs_dev, n, 1, 1.0f, 0, kGemmTile};
+        e = launch_gemm(G, gitems, stream, false, true);
     }
     return hip_status(e);
 }
