@@ -150,7 +150,10 @@ __device__ __forceinline__ void store_tile(const GemmProb& P, const GemmLaunch& 
 constexpr int kBand = 4;
 static_assert(kBand * kBand == kGemmRun, "an XCD run is one block of tiles");
 __device__ __forceinline__ void tile_decode(const GemmProb& P, int64_t t, int& ti, int& tj) {
-    if (P.mode == kModeFactor) {
+    if (P.flags & kGemmTriK) {
+        // K runs from the tile's column on: column by column, the longest first
+        column_decode(t, ti, tj);
+    } else if (P.mode == kModeFactor) {
         upper_band_decode(t, P.tiles_m, kBand, ti, tj);
     } else {
         const int64_t i0 = t / ((int64_t)kBand * P.tiles_n) * kBand;
