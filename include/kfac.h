@@ -77,7 +77,9 @@ const char* kfac_status_string(kfac_status_t status);
  *     M_i <- eps * M_i + (1 - eps) * F_i         otherwise
  *
  * x[i]   : [rows[i], d[i]] row-major, float32 (in_dtype KFAC_F32) or bfloat16
- *          (KFAC_BF16, accumulated in float32).  A layer with a bias carries
+ *          (KFAC_BF16, accumulated in float32).  float32 products are formed
+ *          on the bf16 matrix cores as six bf16 products of exact three-way
+ *          splits of each value and carry float32 rounding.  A layer with a bias carries
  *          a trailing column of ones.
  * m[i]   : [d[i], d[i]] float32.  Only the upper triangle is read (when
  *          first_step == 0) and written; the strict lower triangle is left
@@ -147,8 +149,11 @@ kfac_status_t kfac_stream_copy(const void* src, void* dst, size_t bytes, hipStre
  *     Y_i = X_i + gamma I   (X_i read from the upper triangle of x[i])
  *     Y_i = U^T U  (Cholesky),  V = U^-1,  xinv[i] = V V^T = Y_i^-1
  *
- * computed in float64 on the GPU and written as float32, both triangles,
- * exactly symmetric.  info[i] (device int32 array of n entries) receives 0 on
+ * The factorisation and V are computed in float64 on the GPU, where errors
+ * grow with the condition number; the last product V V^T, whose error
+ * relative to ||xinv||_F does not, with float32-accurate products (each
+ * float32 product as six bf16 products of exact splits).  xinv[i] is written
+ * as float32, both triangles, exactly symmetric.  info[i] (device int32 array of n entries) receives 0 on
  * success, or k > 0 when the leading minor of order k of Y_i is not positive
  * definite or not finite (LAPACK xPOTRF convention); xinv[i] is then
  * unspecified.  gamma must be finite and >= 0.  x[i] and xinv[j] must not
