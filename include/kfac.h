@@ -176,7 +176,9 @@ kfac_status_t kfac_damped_inverse(int n, const float* const* x, const int64_t* d
  * ainv[l] : [d_a[l], d_a[l]] float32, (A + gamma I)^-1, symmetric;
  * out[l]  : [d_g[l], d_a[l]] float32.
  * ginv and ainv must be exactly symmetric (as kfac_damped_inverse writes
- * them): the kernels read them in whichever orientation coalesces.  out[l]
+ * them): the kernels read them in whichever orientation coalesces.  The two
+ * products run on the bf16 matrix cores as six bf16 products of exact
+ * splits per float32 product, with float32 rounding.  out[l]
  * must not overlap any input.
  */
 size_t kfac_precondition_workspace_size(int n, const int64_t* d_g, const int64_t* d_a);
