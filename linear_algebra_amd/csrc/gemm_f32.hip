@@ -963,48 +963,41 @@ __device__ __forceinline__ short4v tr_read_at(uint32_t a) {
     return v;
 }
 
+// Waits until at most N LDS reads are outstanding; the fragments of the
+// reads it covers are named, so that no product that uses them moves above
+// it (those of an edge wave's missing block are undefined and unread).
+template <int N>
+__device__ __forceinline__ void wait_frags(short4v (&f)[2][2]) {
+    asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(f[0][0]), "+v"(f[0][1]), "+v"(f[1][0]), "+v"(f[1][1]) : "i"(N));
+}
+
 // The block products of one step for a wave: NA x NB of its 32 x 32 blocks
 // (the others lie wholly past the problem's edge).  The step's planes lie
 // at byte offset BASE of the plane buffers: A's plane q at BASE + q 4 KB,
 // B's at BASE + BOFF + q 4 KB.  ra[a] / rb[b] hold this lane's address of
 // its first read in A block a / B block b of plane 0; the other reads
 // differ from it by immediates (the rows k0 + 4 + p / 4 lie 1 KB further).
-// B's three planes are read first and stay; A's planes follow one at a
-// time (plane 0 meets B's planes 0-2, plane 1 B's 0-1, plane 2 B's 0), each
-// read while the products of the one before run.  At most 12 reads are in
-// flight, and the products go round the blocks so that none waits for the
-// one before it on the same accumulator.
+// The reads run one plane ahead of the products: A0 meets B0, B1, B2 as
+// they arrive, then A1 meets B0 and B1, and A2 (read into A0's registers)
+// meets B0.  At most 12 reads are in flight, and the products go round the
+// blocks so that none waits for the one before it on the same accumulator.
 template <int NA, int NB, int BASE, int BOFF>
 __device__ __forceinline__ void mma_x6(floatx16 (&acc)[2][2], const uint32_t (&ra)[2], const uint32_t (&rb)[2]) {
     constexpr int PL = XPLANE * 2;   // bytes per plane
+    constexpr int RA = 2 * NA, RB = 2 * NB;   // reads per plane of A / B
     auto fr = [](const short4v& lo, const short4v& hi) {
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
-    short4v bp[3][2][2], ap[2][2][2];   // B planes; A planes, two at a time
-#define X6_RD(F, R, OFF) F[0] = tr_read_at<(OFF)>(R); F[1] = tr_read_at<(OFF) + 1024>(R)
+    short4v b0[2][2], b1[2][2], b2[2][2], a0[2][2], a1[2][2];
+    auto rd = [&](short4v (&f)[2][2], const uint32_t (&r)[2], int n, auto off) {
+        constexpr int OFF = decltype(off)::value;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) { X6_RD(bp[0][b], rb[b], BASE + BOFF); }
-#pragma unroll
-    for (int b = 0; b < NB; ++b) { X6_RD(bp[1][b], rb[b], BASE + BOFF + PL); }
-#pragma unroll
-    for (int b = 0; b < NB; ++b) { X6_RD(bp[2][b], rb[b], BASE + BOFF + 2 * PL); }
-    // B planes 0-1 in (B plane 2's reads may be outstanding); the waits
-    // name the fragments they cover (those of an edge wave's missing blocks
-    // are undefined and unread)
-    if constexpr (NB == 2)
-        asm volatile("s_waitcnt lgkmcnt(4)"
-                     : "+v"(bp[0][0][0]), "+v"(bp[0][0][1]), "+v"(bp[0][1][0]), "+v"(bp[0][1][1]), "+v"(bp[1][0][0]),
-                       "+v"(bp[1][0][1]), "+v"(bp[1][1][0]), "+v"(bp[1][1][1]));
-    else
-        asm volatile("s_waitcnt lgkmcnt(2)"
-                     : "+v"(bp[0][0][0]), "+v"(bp[0][0][1]), "+v"(bp[1][0][0]), "+v"(bp[1][0][1]));
-#pragma unroll
-    for (int a = 0; a < NA; ++a) { X6_RD(ap[0][a], ra[a], BASE); }
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(bp[2][0][0]), "+v"(bp[2][0][1]), "+v"(bp[2][1][0]), "+v"(bp[2][1][1]), "+v"(ap[0][0][0]),
-                   "+v"(ap[0][0][1]), "+v"(ap[0][1][0]), "+v"(ap[0][1][1]));
-#pragma unroll
-    for (int a = 0; a < NA; ++a) { X6_RD(ap[1][a], ra[a], BASE + PL); }
+        for (int q = 0; q < 2; ++q)
+            if (q < n) {
+                f[q][0] = tr_read_at<OFF>(r[q]);
+                f[q][1] = tr_read_at<OFF + 1024>(r[q]);
+            }
+    };
     auto prod = [&](const short4v (&x)[2][2], const short4v (&y)[2][2]) {
 #pragma unroll
         for (int a = 0; a < NA; ++a)
@@ -1013,17 +1006,25 @@ __device__ __forceinline__ void mma_x6(floatx16 (&acc)[2][2], const uint32_t (&r
                 acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr(x[a][0], x[a][1]), fr(y[b][0], y[b][1]),
                                                                     acc[a][b], 0, 0, 0);
     };
-    prod(ap[0], bp[2]);
-    prod(ap[0], bp[1]);
-    prod(ap[0], bp[0]);
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(ap[1][0][0]), "+v"(ap[1][0][1]), "+v"(ap[1][1][0]), "+v"(ap[1][1][1]));
-#pragma unroll
-    for (int a = 0; a < NA; ++a) { X6_RD(ap[0][a], ra[a], BASE + 2 * PL); }
-#undef X6_RD
-    prod(ap[1], bp[1]);
-    prod(ap[1], bp[0]);
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(ap[0][0][0]), "+v"(ap[0][0][1]), "+v"(ap[0][1][0]), "+v"(ap[0][1][1]));
-    prod(ap[0], bp[0]);
+    using std::integral_constant;
+    rd(b0, rb, NB, integral_constant<int, BASE + BOFF>());
+    rd(a0, ra, NA, integral_constant<int, BASE>());
+    rd(b1, rb, NB, integral_constant<int, BASE + BOFF + PL>());
+    wait_frags<RB>(b0);
+    wait_frags<RB>(a0);
+    prod(a0, b0);
+    rd(b2, rb, NB, integral_constant<int, BASE + BOFF + 2 * PL>());
+    wait_frags<RB>(b1);
+    prod(a0, b1);
+    rd(a1, ra, NA, integral_constant<int, BASE + PL>());
+    wait_frags<RA>(b2);
+    prod(a0, b2);
+    rd(a0, ra, NA, integral_constant<int, BASE + 2 * PL>());   // A2
+    wait_frags<RA>(a1);
+    prod(a1, b0);
+    prod(a1, b1);
+    wait_frags<0>(a0);
+    prod(a0, b0);
 }
 
 template <bool SAME>
