@@ -28,6 +28,7 @@ if ROOT not in sys.path:
 
 # MI355X published peaks
 PEAK_FP64_MFMA = 78.6e12
+PEAK_FP32_MFMA = 157.3e12   # the float32 matrix cores, for comparison with the split products
 PEAK_BF16_MFMA = 2.5e15
 # float32 operands run on the bf16 matrix cores as six bf16 products per
 # float32 product (exact three-way splits of each value), so their products'
@@ -456,6 +457,8 @@ def main(argv=None):
                          "traffic": measured_traffic(cfg.name, k)}
         if bound == "hbm":
             stages_out[k]["frac_of_copy"] = round(rate / copy_rate, 4)
+        if basis[k] == split_basis:
+            stages_out[k]["rate_over_fp32_mfma_peak"] = round(rate / PEAK_FP32_MFMA, 4)
     dom = max(stages, key=lambda k: stage_ms[k])
     bound, rate, peak, unit = stage_rate[dom]
     roofline = {"bound": bound, "stage": dom, "achieved": round(rate / scale[unit], 3),
