@@ -56,6 +56,41 @@ def algorithmic_work(cfg):
                 pack_bytes=b_pack, unpack_bytes=b_unpack, packed=packed)
 
 
+def matrix_core_rates(dev, runs=3):
+    """FLOP/s that kfac_matrix_rate's register-only product loops sustain on
+    this part (bf16 32x32x16, fp64 16x16x4, fp32 32x32x2; about 25 ms per
+    run, mean of `runs` after one warm-up): the measured counterpart of the
+    published peaks, taken under the part's own clock and power limits."""
+    import torch
+    import linear_algebra_amd as la
+    blocks = 2 * torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.zeros(4 * blocks, device=dev)
+    out = {}
+    for name, kind, iters in (("bf16", la.KFAC_RATE_BF16, 200000), ("fp64", la.KFAC_RATE_F64, 100000),
+                              ("fp32", la.KFAC_RATE_F32, 100000)):
+        la.kfac_matrix_rate(kind, iters // 10, sink)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        flops = 0.0
+        e0.record()
+        for _ in range(runs):
+            flops += la.kfac_matrix_rate(kind, iters, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = flops / (e0.elapsed_time(e1) * 1e-3)
+    return out
+
+
+def measured_ceiling(stage, cfg, rates):
+    """A stage's ceiling from the measured matrix-core rates, in the same
+    composition as its published ceiling."""
+    split = rates["bf16"] / SPLIT_PRODUCTS
+    if stage in ("factors_A", "factors_G"):
+        return rates["bf16"] if cfg.in_dtype == "bf16" else split
+    if stage == "inverse":
+        return 1.0 / ((2.0 / 3.0) / rates["fp64"] + (1.0 / 3.0) / split)
+    return split
+
+
 def kernel_source_sha256():
     """Hash of the library's kernel sources, the key of stored counter data.
     Comments and blank lines are left out, so that the key changes only
@@ -65,7 +100,8 @@ def kernel_source_sha256():
     import re
     h = hashlib.sha256()
     for p in sorted(glob.glob(os.path.join(ROOT, "linear_algebra_amd", "csrc", "*"))):
-        if p.endswith((".hip", ".h", ".cpp")):
+        # rates.hip holds the matrix-core reference loops, no stage's kernel
+        if p.endswith((".hip", ".h", ".cpp")) and os.path.basename(p) != "rates.hip":
             h.update(os.path.basename(p).encode())
             with open(p, encoding="utf-8") as f:
                 text = f.read()
@@ -405,6 +441,11 @@ def main(argv=None):
             stage_ms[name] += ev[i].elapsed_time(ev[i + 1])
     stage_ms = {k: v / args.steps for k, v in stage_ms.items()}
     ms = wall * 1e3 / args.steps
+    # spread of the step over the timed steps (HIP events around each step)
+    per_step = np.array([ev[0].elapsed_time(ev[-1]) for ev in events])
+    step_stats = {"median": round(float(np.median(per_step)), 4), "mean": round(float(per_step.mean()), 4),
+                  "std": round(float(per_step.std()), 4), "min": round(float(per_step.min()), 4),
+                  "max": round(float(per_step.max()), 4)}
 
     # streaming reference for the HBM-bound stages: the library's plain copy
     # of a buffer as large as the fused one (same bytes as pack moves)
@@ -421,6 +462,10 @@ def main(argv=None):
     torch.cuda.synchronize()
     copy_rate = 2 * n4 * 4 / (c0.elapsed_time(c1) / 20 * 1e-3)
     del copy_src, copy_dst
+
+    # measured reference for the matrix-core-bound stages: register-only
+    # product loops of the library on every CU (two workgroups per CU)
+    rates = matrix_core_rates(dev)
 
     bad = [i for i, v in enumerate(info.cpu().tolist()) if v != 0]
     finite = all(bool(torch.isfinite(o).all()) for o in out)
@@ -459,6 +504,8 @@ def main(argv=None):
             stages_out[k]["frac_of_copy"] = round(rate / copy_rate, 4)
         if basis[k] == split_basis:
             stages_out[k]["rate_over_fp32_mfma_peak"] = round(rate / PEAK_FP32_MFMA, 4)
+        if bound == "mfma":
+            stages_out[k]["frac_of_measured_rate"] = round(rate / measured_ceiling(k, cfg, rates), 4)
     dom = max(stages, key=lambda k: stage_ms[k])
     bound, rate, peak, unit = stage_rate[dom]
     roofline = {"bound": bound, "stage": dom, "achieved": round(rate / scale[unit], 3),
@@ -473,6 +520,7 @@ def main(argv=None):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "step_ms_events": step_stats,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -483,6 +531,8 @@ def main(argv=None):
                    "gamma": gamma, "eps": eps, "flops_per_step": flops, "parallelism": "single GPU"},
         "roofline": roofline,
         "stages": stages_out,
+        "matrix_core_rate": {k: {"TFLOPs": round(v / 1e12, 1), "frac_of_peak": round(v / p, 4)}
+                             for (k, v), p in zip(rates.items(), (PEAK_BF16_MFMA, PEAK_FP64_MFMA, PEAK_FP32_MFMA))},
         "stream_copy": {"GBps": round(copy_rate / 1e9, 1), "bytes": 2 * n4 * 4,
                         "frac_of_peak": round(copy_rate / PEAK_HBM, 4),
                         "note": "kfac_stream_copy of a buffer the size of the fused one: the achievable "

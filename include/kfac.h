@@ -140,6 +140,24 @@ kfac_status_t kfac_pack_sym_static(int n, float* const* m, const int64_t* d, flo
  */
 kfac_status_t kfac_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
 
+/* Matrix-core rate reference.  `blocks` workgroups of four waves each run
+ * `iters` rounds of four independent matrix-core products on register
+ * operands, with no memory traffic besides one float per wave written to
+ * `sink` (device, 4 * blocks floats, 4-byte aligned), which keeps the products
+ * from being removed.  The products are v_mfma_f32_32x32x16_bf16
+ * (KFAC_RATE_BF16, 32768 flops each), v_mfma_f64_16x16x4f64 (KFAC_RATE_F64,
+ * 2048) or v_mfma_f32_32x32x2f32 (KFAC_RATE_F32, 4096).  It computes nothing
+ * of the method: timed by the caller, it is the rate the matrix cores
+ * sustain on this part under its own clock and power limits, the measured
+ * reference for the matrix-core-bound stages beside the published peaks.
+ * *flops (host, may be NULL) receives the flops of the call.
+ * KFAC_ERR_INVALID_VALUE for an unknown kind, iters outside [1, 2^24],
+ * blocks outside [1, 65536] or a null sink.
+ */
+typedef enum { KFAC_RATE_BF16 = 0, KFAC_RATE_F64 = 1, KFAC_RATE_F32 = 2 } kfac_rate_kind_t;
+kfac_status_t kfac_matrix_rate(kfac_rate_kind_t kind, int64_t iters, int blocks, float* sink, double* flops,
+                               hipStream_t stream);
+
 /* ---------------------------------------------------------------- inverse --
  * Tikhonov-damped inverse of each factor (paragraph on damping before
  * inverting; the inverses of different layers are independent, paragraph on

@@ -26,6 +26,7 @@ EXPORTS = (
     "kfac_abi_version", "kfac_status_string",
     "kfac_factors_workspace_size", "kfac_factors",
     "kfac_packed_size", "kfac_pack_workspace_size", "kfac_pack_sym", "kfac_pack_sym_static", "kfac_stream_copy",
+    "kfac_matrix_rate",
     "kfac_inverse_workspace_size", "kfac_damped_inverse",
     "kfac_precondition_workspace_size", "kfac_precondition",
     "kfac_im2col_workspace_size", "kfac_im2col",
@@ -75,6 +76,7 @@ def load_library(path: str = LIB_PATH):
         "kfac_pack_sym": (i32, [i32, vp, vp, vp, i32, vp, sz, vp]),
         "kfac_pack_sym_static": (i32, [i32, vp, vp, vp, i32, vp]),
         "kfac_stream_copy": (i32, [vp, vp, sz, vp]),
+        "kfac_matrix_rate": (i32, [i32, i64, i32, vp, vp, vp]),
         "kfac_inverse_workspace_size": (sz, [i32, vp]),
         "kfac_damped_inverse": (i32, [i32, vp, vp, f32, vp, vp, vp, sz, vp]),
         "kfac_precondition_workspace_size": (sz, [i32, vp, vp]),
@@ -245,6 +247,24 @@ def kfac_stream_copy(src, dst, stream=None) -> None:
                                _stream(dev, stream)), "kfac_stream_copy")
 
 
+KFAC_RATE_BF16, KFAC_RATE_F64, KFAC_RATE_F32 = 0, 1, 2
+
+
+def kfac_matrix_rate(kind: int, iters: int, sink, stream=None) -> float:
+    """Register-only matrix-core product loops (the measured reference of the
+    matrix-core-bound stages); sink float32 with 4 entries per workgroup.
+    Returns the flops the call runs."""
+    import torch
+    lib = load_library()
+    dev = _check([sink], torch.float32, "kfac_matrix_rate")
+    if sink.numel() % 4 != 0 or sink.numel() == 0:
+        raise ValueError("kfac_matrix_rate: sink needs 4 floats per workgroup")
+    flops = ctypes.c_double(0.0)
+    _call(lib.kfac_matrix_rate(int(kind), int(iters), sink.numel() // 4, ctypes.c_void_p(sink.data_ptr()),
+                               ctypes.byref(flops), _stream(dev, stream)), "kfac_matrix_rate")
+    return flops.value
+
+
 def kfac_damped_inverse(xs: Sequence, gamma: float, xinvs: Sequence, info, stream=None) -> None:
     """xinv_i <- (X_i + gamma I)^-1 (X_i read from the upper triangle), info int32 [n]."""
     import torch
@@ -295,6 +315,7 @@ def kfac_precondition(ginvs: Sequence, grads: Sequence, ainvs: Sequence, outs: S
 __all__ = [
     "load_library", "status_string", "KfacError", "KfacLibraryError",
     "kfac_factors", "kfac_packed_size", "kfac_pack_sym", "kfac_pack_sym_static", "kfac_stream_copy",
+    "kfac_matrix_rate", "KFAC_RATE_BF16", "KFAC_RATE_F64", "KFAC_RATE_F32",
     "kfac_damped_inverse",
     "kfac_precondition",
     "KFAC_F32", "KFAC_BF16", "KFAC_PACK", "KFAC_UNPACK", "EXPORTS",

@@ -154,6 +154,20 @@ def test_stream_copy_rejects_bad_arguments(lib):
     assert lib.kfac_stream_copy(ctypes.c_void_p(0), dst, 16, None) == la.KFAC_ERR_INVALID_VALUE
 
 
+def test_matrix_rate_rejects_bad_arguments(lib):
+    sink = ctypes.c_void_p(FAKE)
+    flops = ctypes.c_double(-1.0)
+    rate = lib.kfac_matrix_rate
+    assert rate(3, 10, 1, sink, ctypes.byref(flops), None) == la.KFAC_ERR_INVALID_VALUE          # unknown kind
+    assert rate(0, 0, 1, sink, None, None) == la.KFAC_ERR_INVALID_VALUE                           # no rounds
+    assert rate(0, (1 << 24) + 1, 1, sink, None, None) == la.KFAC_ERR_INVALID_VALUE               # too many rounds
+    assert rate(1, 10, 0, sink, None, None) == la.KFAC_ERR_INVALID_VALUE                          # no workgroups
+    assert rate(1, 10, 65537, sink, None, None) == la.KFAC_ERR_INVALID_VALUE
+    assert rate(2, 10, 1, ctypes.c_void_p(0), None, None) == la.KFAC_ERR_INVALID_VALUE            # no sink
+    assert rate(2, 10, 1, ctypes.c_void_p(FAKE + 2), None, None) == la.KFAC_ERR_INVALID_VALUE     # misaligned sink
+    assert flops.value == -1.0                                                                     # untouched on error
+
+
 def test_python_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros(4, 3)
