@@ -447,6 +447,19 @@ def main(argv=None):
                   "std": round(float(per_step.std()), 4), "min": round(float(per_step.min()), 4),
                   "max": round(float(per_step.max()), 4)}
 
+    # the factor stages in their first-step form (M <- F: the running
+    # average is not read), after the timed region
+    fs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(5)]
+    for ev in fs:
+        ev[0].record()
+        la.kfac_factors(a_d, ma, eps, True)
+        ev[1].record()
+        la.kfac_factors(g_d, mg, eps, True)
+        ev[2].record()
+    torch.cuda.synchronize()
+    first_step = {"factors_A": round(sum(ev[0].elapsed_time(ev[1]) for ev in fs) / len(fs), 4),
+                  "factors_G": round(sum(ev[1].elapsed_time(ev[2]) for ev in fs) / len(fs), 4)}
+
     # streaming reference for the HBM-bound stages: the library's plain copy
     # of a buffer as large as the fused one (same bytes as pack moves)
     # (whole 16-byte units of it)
@@ -531,6 +544,7 @@ def main(argv=None):
                    "gamma": gamma, "eps": eps, "flops_per_step": flops, "parallelism": "single GPU"},
         "roofline": roofline,
         "stages": stages_out,
+        "first_step_factors_ms": first_step,
         "matrix_core_rate": {k: {"TFLOPs": round(v / 1e12, 1), "frac_of_peak": round(v / p, 4)}
                              for (k, v), p in zip(rates.items(), (PEAK_BF16_MFMA, PEAK_FP64_MFMA, PEAK_FP32_MFMA))},
         "stream_copy": {"GBps": round(copy_rate / 1e9, 1), "bytes": 2 * n4 * 4,
