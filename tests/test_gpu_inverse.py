@@ -219,6 +219,24 @@ def check_sampled(xs, zs, gamma, pick, ncols=6, seed=0):
     return worst
 
 
+def check_full_per_order(xs, zs, gamma):
+    """The whole inverse of the first matrix of every order against the
+    oracle's (Cholesky, then every column by substitution)."""
+    worst, seen = 0.0, set()
+    for k, x in enumerate(xs):
+        d = x.shape[0]
+        if d in seen:
+            continue
+        seen.add(d)
+        ref, info = oracle.damped_inverse(x, gamma)
+        assert info == 0
+        err = rel_fro(zs[k], ref)
+        worst = max(worst, err)
+        say(f"  matrix {k} (order {d}): whole inverse, rel err {err:.3e}")
+        assert err <= TOL, (k, d, err)
+    return worst
+
+
 def test_inverse_config1_full():
     xs = config_factor_inputs(1)
     gamma = np.float32(0.01)
@@ -287,7 +305,8 @@ def test_inverse_config4_full_batch():
     """The encoder's 96 factors (orders 1024, 1025, 3072, 4096, 4097; the
     bf16 inputs upcast exactly) in one call, the configuration the benchmark
     runs: the first and last matrix of every order against oracle columns,
-    every output checked for symmetry."""
+    the first matrix of every order in whole, every output checked for
+    symmetry."""
     xs = config_factor_inputs(4)
     gamma = np.float32(1e-3)
     say("config 4 inverse:", len(xs), "matrices, orders", sorted({x.shape[0] for x in xs}))
@@ -296,7 +315,8 @@ def test_inverse_config4_full_batch():
     for z in zs:
         np.testing.assert_array_equal(z, z.T)
     worst = check_sampled(xs, zs, gamma, size_representatives(xs), ncols=6, seed=4)
-    say(f"config 4 inverse: worst sampled rel err {worst:.3e}")
+    worst = max(worst, check_full_per_order(xs, zs, gamma))
+    say(f"config 4 inverse: worst rel err (sampled and whole) {worst:.3e}")
 
 
 @pytest.mark.timeout(900)
@@ -305,8 +325,8 @@ def test_inverse_config5_full_batch(gamma):
     """The large-factor workload's 32 factors at its full 25,088 rows, in one
     call as the benchmark makes it (the bordered 2305 and 4609 with the
     plain 512, 2048 and 4096 in one launch sequence): every matrix against
-    oracle columns, every output checked for symmetry.  gamma = 1e-4 is
-    held to the same bound."""
+    oracle columns, the first matrix of every order in whole, every output
+    checked for symmetry.  gamma = 1e-4 is held to the same bound."""
     xs = config_factor_inputs(5)
     gamma = np.float32(gamma)
     say("config 5 inverse, full batch, gamma", float(gamma), [x.shape[0] for x in xs])
@@ -315,7 +335,8 @@ def test_inverse_config5_full_batch(gamma):
     for z in zs:
         np.testing.assert_array_equal(z, z.T)
     worst = check_sampled(xs, zs, gamma, range(len(xs)), ncols=3, seed=int(1 / gamma))
-    say(f"config 5 inverse gamma={float(gamma)}: worst sampled rel err {worst:.3e}")
+    worst = max(worst, check_full_per_order(xs, zs, gamma))
+    say(f"config 5 inverse gamma={float(gamma)}: worst rel err (sampled and whole) {worst:.3e}")
 
 
 @pytest.mark.parametrize("gamma", [1e-2, 1e-4])
