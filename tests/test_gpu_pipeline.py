@@ -68,3 +68,15 @@ def test_pipeline_config2_first_steps():
     err = run_pipeline(2, 2, inverse_at={0})
     say(f"config 2 end-to-end rel err {err:.3e}")
     assert err <= 1e-2
+
+
+@pytest.mark.timeout(600)
+def test_pipeline_config2_full_schedule():
+    """The MLP workload's whole schedule: 20 steps of factors with their
+    running average, pack and unpack, inverses at steps 0 and 10 (of the
+    running averages at those steps), every step preconditioned with the
+    latest inverses, against the oracle pipeline from the same raw inputs."""
+    cfg = CONFIGS[2]
+    err = run_pipeline(2, cfg.steps, inverse_at=set(cfg.inverse_steps))
+    say(f"config 2 full schedule ({cfg.steps} steps, inverses at {cfg.inverse_steps}): end-to-end rel err {err:.3e}")
+    assert err <= 1e-2
