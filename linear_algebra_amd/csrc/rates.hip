@@ -19,6 +19,8 @@ constexpr int kRateBf16 = 0, kRateF64 = 1, kRateF32 = 2;
 
 typedef __bf16 bf16x8r __attribute__((ext_vector_type(8)));
 
+// An integer hash with good avalanche (the published "lowbias32" finaliser
+// of C. Wellons' hash-prospector), for the operands only.
 __device__ __forceinline__ uint32_t mix(uint32_t x) {
     x ^= x >> 16;
     x *= 0x7feb352du;
@@ -34,6 +36,10 @@ __device__ __forceinline__ float operand(uint32_t h) {
     return (h & 1u) ? -m : m;
 }
 
+// Two workgroups per CU (two waves per SIMD).  The occupancy hint also
+// keeps the accumulators in VGPRs: without it the compiler put the float64
+// products' accumulators in AGPRs and copied them to VGPRs and back on
+// every round of the loop.
 template <int KIND>
 __global__ __launch_bounds__(256, 2) void matrix_rate_kernel(int64_t iters, float* __restrict__ sink) {
     const uint32_t g = blockIdx.x * 256u + threadIdx.x;
