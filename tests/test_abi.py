@@ -95,6 +95,7 @@ def test_factors_rejects_bad_arguments(lib):
         lib.kfac_factors(n, x, rows, d, dt, m, ctypes.c_float(eps), 0, w, wsb, None)
     assert call(n=0) == la.KFAC_ERR_INVALID_VALUE
     assert call(d=i64([0])) == la.KFAC_ERR_INVALID_VALUE
+    assert call(d=i64([16385])) == la.KFAC_ERR_INVALID_VALUE           # past the largest order
     assert call(rows=i64([0])) == la.KFAC_ERR_INVALID_VALUE
     assert call(eps=1.5) == la.KFAC_ERR_INVALID_VALUE
     assert call(eps=float("nan")) == la.KFAC_ERR_INVALID_VALUE
@@ -116,6 +117,9 @@ def test_inverse_rejects_bad_arguments(lib):
     assert call(g=float("inf")) == la.KFAC_ERR_INVALID_VALUE
     assert call(info=ctypes.c_void_p(0)) == la.KFAC_ERR_INVALID_VALUE
     assert call(n=4097, d=i64([4] * 4097)) == la.KFAC_ERR_INVALID_VALUE
+    assert call(n=0) == la.KFAC_ERR_INVALID_VALUE
+    assert call(d=i64([0])) == la.KFAC_ERR_INVALID_VALUE
+    assert call(d=i64([16385])) == la.KFAC_ERR_INVALID_VALUE
     assert call(wsb=100) == la.KFAC_ERR_WORKSPACE
 
 
