@@ -84,7 +84,7 @@ const char* kfac_status_string(kfac_status_t status);
  * m[i]   : [d[i], d[i]] float32.  Only the upper triangle is read (when
  *          first_step == 0) and written; the strict lower triangle is left
  *          as it was.
- * eps    : in [0, 1].  rows[i] >= 1, 1 <= d[i] <= KFAC_MAX_DIM.
+ * eps    : in [0, 1].  1 <= rows[i] <= 2^31 - 1, 1 <= d[i] <= KFAC_MAX_DIM.
  * The x[i] must not overlap any m[j].  Results are deterministic: the same
  * inputs give the same bits on every run.
  */

@@ -97,6 +97,7 @@ def test_factors_rejects_bad_arguments(lib):
     assert call(d=i64([0])) == la.KFAC_ERR_INVALID_VALUE
     assert call(d=i64([16385])) == la.KFAC_ERR_INVALID_VALUE           # past the largest order
     assert call(rows=i64([0])) == la.KFAC_ERR_INVALID_VALUE
+    assert call(rows=i64([1 << 31])) == la.KFAC_ERR_INVALID_VALUE       # rows past 2^31 - 1
     assert call(eps=1.5) == la.KFAC_ERR_INVALID_VALUE
     assert call(eps=float("nan")) == la.KFAC_ERR_INVALID_VALUE
     assert call(dt=3) == la.KFAC_ERR_INVALID_VALUE
