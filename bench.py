@@ -92,16 +92,18 @@ def measured_ceiling(stage, cfg, rates):
 
 
 def kernel_source_sha256():
-    """Hash of the library's kernel sources, the key of stored counter data.
-    Comments and blank lines are left out, so that the key changes only
-    with the code."""
+    """Hash of the sources of the step's stage kernels, the key of stored
+    counter data.  Comments and blank lines are left out, so that the key
+    changes only with the code."""
     import glob
     import hashlib
     import re
     h = hashlib.sha256()
+    # the files that hold no kernel of the step's stages: the matrix-core
+    # reference loops and the layer row (im2col, gradient rows)
+    skip = {"rates.hip", "layers.hip"}
     for p in sorted(glob.glob(os.path.join(ROOT, "linear_algebra_amd", "csrc", "*"))):
-        # rates.hip holds the matrix-core reference loops, no stage's kernel
-        if p.endswith((".hip", ".h", ".cpp")) and os.path.basename(p) != "rates.hip":
+        if p.endswith((".hip", ".h", ".cpp")) and os.path.basename(p) not in skip:
             h.update(os.path.basename(p).encode())
             with open(p, encoding="utf-8") as f:
                 text = f.read()
